@@ -1,0 +1,191 @@
+/*
+ * libkvq2 — OSCAR-style INT2 KV-cache quantize-append and fused split-K
+ * decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Method (web pages, cited by title and section):
+ *   "Technical summary: OSCAR - Offline Spectral Covariance-Aware Rotation
+ *    for 2-bit KV cache quantization" (gist.science 2605.17757):
+ *      sec. 2.2-A items 1-4  offline calibration: C_Q, C_S, eigenbasis,
+ *                            R = U . H_Had . P_br, per-layer clip thresholds;
+ *      sec. 2.2-B            online serving: bf16 sink + recent tokens, INT2
+ *                            history after the fixed rotation and clipping, a
+ *                            fused kernel that unpacks, dequantizes, undoes the
+ *                            rotation and attends, over a paged cache.
+ *   tilnote.io note on OSCAR (Together AI), "why it matters for serving":
+ *      INT2 history with bf16 sink and recent tokens in a paged KV cache.
+ *
+ * Conventions (readings where the pages are silent):
+ *   - head_dim = 128; query head g uses KV head g / (n_q_heads / n_kv_heads).
+ *   - R is stored row-major fp32 [128][128] per KV head and applied as
+ *     x' = R^T x (x'_i = sum_j R[j][i] x_j).  Keys are rotated by R_K, values
+ *     by R_V; the query is rotated once by R_K^T and the output mapped back
+ *     once with o = R_V o'.
+ *   - Rotation of a new vector: fp64 accumulation over j = 0..127 in order,
+ *     rounded to fp32 then to bf16 (round-to-nearest-even).
+ *   - INT2 quantizer per (token, KV head, K|V) group of 128 channels:
+ *     x = clamp(r, -clip, clip) + 0; s = fp16((max x - min x) / 3);
+ *     z = fp16(min x); code = clamp(rint((x - z) * (1 / s)), 0, 3) with each
+ *     fp32 step rounded separately; s == 0 gives all-zero codes.
+ *     Dequantized value: z + code * s.
+ *   - Segments of a sequence of length L (positions 0..L-1):
+ *       sink   [0, min(L, n_sink))                 bf16, rotated
+ *       INT2   [n_sink, max(n_sink, L - n_recent))  paged INT2
+ *       recent [max(n_sink, L - n_recent), L)      bf16 ring, rotated
+ *
+ * Memory layout (all device buffers are owned by the caller):
+ *   pool         uint8 [num_pages][n_kv_heads][page_size/16][1152]
+ *                One 1152-byte chunk holds 16 consecutive positions
+ *                16c..16c+15 of one sequence and one KV head.  Position pos
+ *                lives in physical page block_table[b][pos / page_size],
+ *                chunk (pos % page_size) / 16, slot t = pos % 16.
+ *                Chunk bytes (four channels 4g..4g+3 of one token share a
+ *                byte; channel 4g+k occupies bits 2k..2k+1):
+ *                  [   0,  512) K codes: byte 32*t + g
+ *                  [ 512, 1024) V codes: byte 512 + 32*(g % 16) + 8*(t / 4)
+ *                                              + 4*(g / 16) + (t % 4)
+ *                  [1024, 1088) K params: slot t at 1024 + 4t: fp16 s, fp16 z
+ *                  [1088, 1152) V params: slot t at 1088 + 4t: fp16 s, fp16 z
+ *                (fp16 little-endian; g = channel / 4 in 0..31.)
+ *                Slots of sink positions and of positions still in the recent
+ *                window are never written or read.
+ *   sink         bf16 [batch][n_kv_heads][n_sink][2][128]   (K' then V')
+ *   recent       bf16 [batch][n_kv_heads][n_recent][2][128] ring: position
+ *                pos lives in slot (pos - n_sink) % n_recent
+ *   block_table  int32 [batch][bt_stride]; entries for every page that holds
+ *                an INT2 position of the sequence must be valid page numbers
+ *                in [0, num_pages).  Several sequences may share pages (a
+ *                shared read-only prefix).
+ *
+ * Error behaviour: every entry point validates its arguments on the host
+ * before any HIP call and returns a negative kvq_status without side effects
+ * on failure.  Device faults surface at the caller's next synchronisation.
+ * Non-finite q/K/V values give unspecified (but memory-safe) results.
+ * All pointers must be 16-byte aligned.  Calls are asynchronous on `stream`
+ * (a hipStream_t; NULL means the default stream) except kvq_calibrate.
+ */
+#ifndef KVQ2_H
+#define KVQ2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,          /* null/misaligned pointer, bad size or count */
+  KVQ_ERR_UNSUPPORTED = -2,  /* head_dim != 128, page size, group size > 16 */
+  KVQ_ERR_WORKSPACE = -3,    /* decode workspace smaller than required */
+  KVQ_ERR_NUMERIC = -4,      /* calibrate: non-finite input, no convergence,
+                                clip threshold outside (0, 16384] */
+  KVQ_ERR_HIP = -5           /* a HIP launch or runtime call failed */
+};
+
+typedef struct kvq_dims {
+  int32_t n_q_heads;   /* Hq  >= 1, a multiple of n_kv_heads               */
+  int32_t n_kv_heads;  /* Hkv >= 1; Hq / Hkv <= 16                          */
+  int32_t head_dim;    /* must be 128                                       */
+  int32_t page_size;   /* tokens per page: 16, 32 or 64                     */
+  int32_t n_sink;      /* >= 0 bf16 sink tokens                             */
+  int32_t n_recent;    /* >= 1 bf16 recent-window tokens (ring size)        */
+  float sm_scale;      /* softmax scale; <= 0 selects 1/sqrt(head_dim)      */
+} kvq_dims;
+
+/* Per-layer calibration products (device pointers for the online calls). */
+typedef struct kvq_layer {
+  const float* R_K;    /* fp32 [Hkv][128][128], orthogonal, applied as R^T x */
+  const float* R_V;    /* fp32 [Hkv][128][128]                              */
+  float clip_K;        /* 0 < clip <= 16384                                 */
+  float clip_V;
+} kvq_layer;
+
+typedef struct kvq_cache {
+  uint8_t* pool;              /* see layout above                           */
+  int64_t num_pages;          /* physical pages in `pool`                   */
+  uint16_t* sink;             /* bf16; may be NULL when n_sink == 0         */
+  uint16_t* recent;           /* bf16 ring                                  */
+  const int32_t* block_table; /* int32 [batch][bt_stride]                   */
+  int32_t bt_stride;          /* >= ceil(max length / page_size)            */
+} kvq_cache;
+
+/*
+ * Offline calibration of one layer on the host (synchronous, host memory).
+ * OSCAR summary sec. 2.2-A: C_Q = (1/N) sum q q^T pooled over the query heads
+ * of each KV head; C_S = (1/N) V^T S^T S V = (1/N) O^T O with S the causal
+ * softmax scores of the calibration tokens; eigenbases U_Q, U_S (descending
+ * eigenvalues; each column's largest-magnitude entry positive); R = U H P
+ * with H the 128x128 Sylvester Hadamard / sqrt(128) and P the 7-bit
+ * bit-reversal permutation; clip = nearest-rank `clip_quantile` quantile of
+ * |rotated calibration values| over all tokens, KV heads and channels.
+ *   q   bf16 [n_tokens][Hq][128];  k, v  bf16 [n_tokens][Hkv][128]
+ *   R_K, R_V  out fp32 [Hkv][128][128];  clip_K, clip_V  out (one float each)
+ * 0 < clip_quantile <= 1.  n_tokens >= 1.  Uses up to 16 host threads.
+ */
+int kvq_calibrate(const kvq_dims* dims, int32_t n_tokens,
+                  const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  double clip_quantile,
+                  float* R_K, float* R_V, float* clip_K, float* clip_V);
+
+/*
+ * Quantize-append (OSCAR summary sec. 2.2-B).  For every sequence b, the
+ * tokens cu_new[b] .. cu_new[b+1]-1 of k_new/v_new are appended at positions
+ * start_pos[b], start_pos[b]+1, ...  Each new K/V head-vector is rotated;
+ * positions < n_sink go to the sink; positions older than the recent window
+ * at the end of this append go straight to INT2 pages; the rest go to the
+ * ring.  Ring tokens pushed out of the window are first quantized from their
+ * stored bf16 values into INT2.  Byte-identical to appending one token at a
+ * time.
+ *   start_pos  device int32 [batch]      length of each sequence before the call
+ *   cu_new     device int32 [batch + 1]  token offsets (cu_new[0] = 0)
+ *   total_new  host: cu_new[batch];  max_new host: max per-sequence count
+ *   k_new, v_new  device bf16 [total_new][Hkv][128]
+ * Page entries of every INT2 position written must exist in block_table.
+ */
+int kvq_quantize_append(const kvq_dims* dims, const kvq_layer* layer,
+                        const kvq_cache* cache, int32_t batch,
+                        const int32_t* start_pos, const int32_t* cu_new,
+                        int32_t total_new, int32_t max_new,
+                        const uint16_t* k_new, const uint16_t* v_new,
+                        void* stream);
+
+/*
+ * Bytes of device workspace kvq_decode_attention needs for this batch and
+ * longest sequence: split-K partial results and one arrival counter per
+ * (sequence, KV head).  The caller allocates it, zero-fills it once, and may
+ * reuse it for every later call with the same or smaller sizes: each call
+ * leaves the counters at zero again.  Concurrent calls must not share it.
+ */
+size_t kvq_decode_workspace_bytes(const kvq_dims* dims, int32_t batch,
+                                  int32_t max_seq_len);
+
+/*
+ * Decode attention of one new query per sequence over its whole cache
+ * (OSCAR summary sec. 2.2-B, fused INT2 attention).  q' = R_K^T q once per
+ * query head; logits sm_scale * q' . k' over the sink, INT2 (dequantized in
+ * registers) and recent segments; one softmax; o' = sum p v' in rotated
+ * space; out = R_V o' once.
+ *   seq_len      device int32 [batch]  length L of every sequence (>= 0)
+ *   max_seq_len  host, >= every seq_len (sizes the split-K grid)
+ *   q            device bf16 [batch][Hq][128]
+ *   out          device fp32 [batch][Hq][128]  (an empty sequence gives 0)
+ */
+int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer,
+                         const kvq_cache* cache, int32_t batch,
+                         const int32_t* seq_len, int32_t max_seq_len,
+                         const uint16_t* q, float* out,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Human-readable name of a kvq_status value (static storage). */
+const char* kvq_status_string(int status);
+
+/* Last HIP error text recorded by this thread after KVQ_ERR_HIP ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ2_H */

@@ -1,0 +1,203 @@
+// Quantize-append kernel (OSCAR technical summary, sec. 2.2-B: history is
+// stored as INT2 after the fixed rotation and clipping; sink and recent
+// tokens stay bf16).
+//
+// One wave (64 lanes) handles one new (token, KV head, K|V) head-vector;
+// lane l owns channels l and l + 64.  A work-group of four waves shares one
+// (KV head, K|V) pair and stages that 64 KiB rotation matrix in LDS once for
+// the 16 tokens it handles.
+//
+// Per vector:
+//   1. If the token is written to the recent ring and the slot's previous
+//      occupant (an older token of this sequence) leaves the window, that
+//      occupant is quantized from its stored bf16 values into its INT2 page
+//      first.  The same lanes read the slot before they overwrite it.
+//   2. r = bf16(fp32(R^T x)) with fp64 accumulation in channel order.
+//   3. Sink slot, INT2 page (quantize + pack), or ring slot, by position.
+#include "kvq2_device.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kTokensPerBlock = 16;
+constexpr int kWaves = 4;
+
+struct AppendArgs {
+  const float* R[2];
+  float clip[2];
+  uint8_t* pool;
+  int64_t num_pages;
+  uint16_t* sink;
+  uint16_t* recent;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int n_kv_heads, page_size, n_sink, n_recent;
+  int batch;
+  const int32_t* start_pos;
+  const int32_t* cu_new;
+  int total_new;
+  const uint16_t* x_new[2];
+};
+
+// Quantize one rotated vector (channels lane and lane + 64) and store its
+// packed codes and fp16 (scale, zero) in slot t of the chunk at `chunk`.
+// Pinned fp32 steps, each rounded separately (no contraction).
+__device__ void quantize_store(uint8_t* chunk, int t, int kind, float r0, float r1, float clip,
+                               int lane) {
+  const float x0 = fminf(fmaxf(r0, -clip), clip) + 0.0f;   // + 0 turns -0 into +0
+  const float x1 = fminf(fmaxf(r1, -clip), clip) + 0.0f;
+  const float mn = wave_min(fminf(x0, x1));
+  const float mx = wave_max(fmaxf(x0, x1));
+  const float s = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
+  const uint32_t s_bits = float_to_f16_bits(s);
+  const uint32_t z_bits = float_to_f16_bits(mn);
+  const float sf = f16_bits_to_float(s_bits);
+  const float zf = f16_bits_to_float(z_bits);
+  uint32_t c0 = 0, c1 = 0;
+  if (sf != 0.0f) {
+    const float inv = __fdiv_rn(1.0f, sf);
+    const float t0 = __fmul_rn(__fsub_rn(x0, zf), inv);
+    const float t1 = __fmul_rn(__fsub_rn(x1, zf), inv);
+    c0 = static_cast<uint32_t>(fminf(fmaxf(rintf(t0), 0.0f), 3.0f));
+    c1 = static_cast<uint32_t>(fminf(fmaxf(rintf(t1), 0.0f), 3.0f));
+  }
+  // Four consecutive channels form a byte: channel 4g + k at bits 2k.
+  uint32_t b0 = c0 << (2 * (lane & 3));
+  uint32_t b1 = c1 << (2 * (lane & 3));
+  b0 |= __shfl_xor(b0, 1);
+  b0 |= __shfl_xor(b0, 2);
+  b1 |= __shfl_xor(b1, 1);
+  b1 |= __shfl_xor(b1, 2);
+  if ((lane & 3) == 0) {
+    const int g = lane >> 2;   // channel group of channel `lane`; group g + 16 holds lane + 64
+    if (kind == 0) {
+      chunk[kKCodesOff + 32 * t + g] = static_cast<uint8_t>(b0);
+      chunk[kKCodesOff + 32 * t + g + 16] = static_cast<uint8_t>(b1);
+    } else {
+      const int base = kVCodesOff + 32 * g + 8 * (t >> 2) + (t & 3);
+      chunk[base] = static_cast<uint8_t>(b0);
+      chunk[base + 4] = static_cast<uint8_t>(b1);
+    }
+  }
+  if (lane == 0) {
+    const int off = (kind == 0 ? kKParamsOff : kVParamsOff) + 4 * t;
+    *reinterpret_cast<uint32_t*>(chunk + off) = s_bits | (z_bits << 16);
+  }
+}
+
+__global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
+  __shared__ float Rs[kHeadDim * kHeadDim];
+  __shared__ double xs[kWaves][kHeadDim];
+  const int h = blockIdx.y;
+  const int kind = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  {
+    const float4* src = reinterpret_cast<const float4*>(a.R[kind] + int64_t(h) * kHeadDim * kHeadDim);
+    float4* dst = reinterpret_cast<float4*>(Rs);
+    for (int i = threadIdx.x; i < kHeadDim * kHeadDim / 4; i += blockDim.x) dst[i] = src[i];
+  }
+  __syncthreads();
+  const float clip = a.clip[kind];
+  const int W = a.n_recent;
+  const int ns = a.n_sink;
+  for (int it = 0; it < kTokensPerBlock / kWaves; ++it) {
+    const int n = blockIdx.x * kTokensPerBlock + wave * (kTokensPerBlock / kWaves) + it;
+    if (n >= a.total_new) break;
+    // Sequence of token n: the largest b with cu_new[b] <= n.
+    int lo = 0, hi = a.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_new[mid] <= n) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int start = a.start_pos[b];
+    if (start < 0) continue;   // invalid length: nothing is written
+    const int pos = start + (n - a.cu_new[b]);
+    const int end = start + (a.cu_new[b + 1] - a.cu_new[b]);
+    const int64_t seq_head = int64_t(b) * a.n_kv_heads + h;
+    const bool to_ring = pos >= ns && pos >= end - W;
+
+    if (to_ring) {
+      // The ring slot's occupant from before this append, if it leaves the window.
+      const int pold = pos - ((pos - start) / W + 1) * W;
+      if (pold >= ns) {
+        const uint16_t* src = a.recent + (seq_head * W + (pold - ns) % W) * 2 * kHeadDim + kind * kHeadDim;
+        const float r0 = bf16_bits_to_float(src[lane]);
+        const float r1 = bf16_bits_to_float(src[lane + 64]);
+        const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
+                                         a.page_size, b, h, pold);
+        if (off >= 0) quantize_store(a.pool + off, pold % kChunkTokens, kind, r0, r1, clip, lane);
+      }
+    }
+
+    // Pinned rotation of the new vector.
+    const uint16_t* x = a.x_new[kind] + (int64_t(n) * a.n_kv_heads + h) * kHeadDim;
+    xs[wave][lane] = double(bf16_bits_to_float(x[lane]));
+    xs[wave][lane + 64] = double(bf16_bits_to_float(x[lane + 64]));
+    __builtin_amdgcn_wave_barrier();
+    double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll 8
+    for (int j = 0; j < kHeadDim; ++j) {
+      const double xj = xs[wave][j];
+      acc0 = __fma_rn(xj, double(Rs[j * kHeadDim + lane]), acc0);
+      acc1 = __fma_rn(xj, double(Rs[j * kHeadDim + lane + 64]), acc1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t rb0 = float_to_bf16_bits(__double2float_rn(acc0));
+    const uint32_t rb1 = float_to_bf16_bits(__double2float_rn(acc1));
+
+    if (pos < ns) {
+      uint16_t* dst = a.sink + (seq_head * ns + pos) * 2 * kHeadDim + kind * kHeadDim;
+      dst[lane] = static_cast<uint16_t>(rb0);
+      dst[lane + 64] = static_cast<uint16_t>(rb1);
+    } else if (!to_ring) {
+      const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
+                                       a.page_size, b, h, pos);
+      if (off >= 0)
+        quantize_store(a.pool + off, pos % kChunkTokens, kind, bf16_bits_to_float(rb0),
+                       bf16_bits_to_float(rb1), clip, lane);
+    } else {
+      uint16_t* dst = a.recent + (seq_head * W + (pos - ns) % W) * 2 * kHeadDim + kind * kHeadDim;
+      dst[lane] = static_cast<uint16_t>(rb0);
+      dst[lane + 64] = static_cast<uint16_t>(rb1);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_quantize_append(const kvq_dims& d, float /*sm_scale*/, const kvq_layer& layer,
+                           const kvq_cache& cache, int32_t batch, const int32_t* start_pos,
+                           const int32_t* cu_new, int32_t total_new, const uint16_t* k_new,
+                           const uint16_t* v_new, void* stream) {
+  AppendArgs a{};
+  a.R[0] = layer.R_K;
+  a.R[1] = layer.R_V;
+  a.clip[0] = layer.clip_K;
+  a.clip[1] = layer.clip_V;
+  a.pool = cache.pool;
+  a.num_pages = cache.num_pages;
+  a.sink = cache.sink;
+  a.recent = cache.recent;
+  a.block_table = cache.block_table;
+  a.bt_stride = cache.bt_stride;
+  a.n_kv_heads = d.n_kv_heads;
+  a.page_size = d.page_size;
+  a.n_sink = d.n_sink;
+  a.n_recent = d.n_recent;
+  a.batch = batch;
+  a.start_pos = start_pos;
+  a.cu_new = cu_new;
+  a.total_new = total_new;
+  a.x_new[0] = k_new;
+  a.x_new[1] = v_new;
+  dim3 grid((total_new + kTokensPerBlock - 1) / kTokensPerBlock, d.n_kv_heads, 2);
+  hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+const char* hip_error_name(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+}  // namespace kvq

@@ -1,0 +1,63 @@
+// Device helpers shared by the libkvq2 HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq2_internal.h"
+
+namespace kvq {
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+__device__ __forceinline__ uint32_t float_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Byte offset of the 1152-byte chunk holding position `pos` of sequence b,
+// KV head h; -1 if the block-table entry is outside [0, num_pages).
+__device__ __forceinline__ int64_t chunk_offset(const int32_t* block_table, int32_t bt_stride,
+                                                int64_t num_pages, int n_kv_heads, int page_size,
+                                                int b, int h, int pos) {
+  if (pos < 0) return -1;
+  const int lp = pos / page_size;
+  if (lp >= bt_stride) return -1;
+  const int32_t page = block_table[int64_t(b) * bt_stride + lp];
+  if (page < 0 || page >= num_pages) return -1;
+  const int cpp = page_size / kChunkTokens;
+  return ((int64_t(page) * n_kv_heads + h) * cpp + (pos % page_size) / kChunkTokens) *
+         int64_t(kChunkBytes);
+}
+
+}  // namespace kvq

@@ -1,0 +1,167 @@
+// libkvq2 host side: argument validation, decode planning and the public
+// entry points of the online path.  Validation runs before any HIP call so
+// that every error is reported without touching the device.
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kvq2_internal.h"
+
+namespace kvq {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks common to the online calls.
+int check_dims(const kvq_dims* d) {
+  if (d == nullptr) return KVQ_ERR_ARG;
+  if (d->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (d->n_kv_heads < 1 || d->n_q_heads < 1) return KVQ_ERR_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return KVQ_ERR_ARG;
+  if (d->n_q_heads / d->n_kv_heads > kMaxGroup) return KVQ_ERR_UNSUPPORTED;
+  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64) return KVQ_ERR_UNSUPPORTED;
+  if (d->n_sink < 0 || d->n_recent < 1) return KVQ_ERR_ARG;
+  if (!std::isfinite(d->sm_scale)) return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+int check_layer(const kvq_layer* l) {
+  if (l == nullptr || l->R_K == nullptr || l->R_V == nullptr) return KVQ_ERR_ARG;
+  if (!aligned16(l->R_K) || !aligned16(l->R_V)) return KVQ_ERR_ARG;
+  for (float c : {l->clip_K, l->clip_V})
+    if (!(c > 0.0f) || !(c <= kMaxClip)) return KVQ_ERR_ARG;   // also rejects NaN
+  return KVQ_OK;
+}
+
+int check_cache(const kvq_dims* d, const kvq_cache* c) {
+  if (c == nullptr || c->pool == nullptr || c->recent == nullptr || c->block_table == nullptr)
+    return KVQ_ERR_ARG;
+  if (d->n_sink > 0 && c->sink == nullptr) return KVQ_ERR_ARG;
+  if (!aligned16(c->pool) || !aligned16(c->recent) || !aligned16(c->block_table)) return KVQ_ERR_ARG;
+  if (c->sink != nullptr && !aligned16(c->sink)) return KVQ_ERR_ARG;
+  if (c->num_pages < 1 || c->bt_stride < 1) return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+float resolved_scale(const kvq_dims* d) {
+  return d->sm_scale > 0.0f ? d->sm_scale : 1.0f / std::sqrt(static_cast<float>(kHeadDim));
+}
+
+int env_int(const char* name, int fallback) {
+  const char* s = std::getenv(name);
+  if (s == nullptr || *s == '\0') return fallback;
+  return std::atoi(s);
+}
+
+}  // namespace
+
+void set_last_error(const char* msg) { g_last_error = msg ? msg : ""; }
+
+DecodeKernel selected_decode_kernel() {
+  // KVQ_DECODE_KERNEL=valu selects the plain VALU kernel (kept as the
+  // measured comparison point for the MFMA kernel); default is MFMA.
+  const char* s = std::getenv("KVQ_DECODE_KERNEL");
+  if (s != nullptr && std::strcmp(s, "valu") == 0) return kDecodeValu;
+  return kDecodeMfma;
+}
+
+DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len) {
+  DecodePlan p{};
+  const int64_t int2_end = std::max<int64_t>(d.n_sink, int64_t(max_seq_len) - d.n_recent);
+  const int64_t first_chunk = d.n_sink / kChunkTokens;
+  const int64_t last_chunk = (int2_end + kChunkTokens - 1) / kChunkTokens;   // exclusive
+  const int64_t n_chunks = int2_end > d.n_sink ? last_chunk - first_chunk : 0;
+  const int64_t heads = int64_t(batch) * d.n_kv_heads;
+  // Enough work-groups to fill 256 CUs several times over, but no split
+  // shorter than 16 chunks (256 tokens).
+  int64_t ns = (2048 + heads - 1) / std::max<int64_t>(heads, 1);
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, n_chunks / 16));
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, 512));
+  const int forced = env_int("KVQ_NSPLIT", 0);
+  if (forced > 0) ns = std::min(forced, 4096);
+  if (n_chunks == 0) ns = 1;
+  p.n_split_int2 = static_cast<int>(ns);
+  p.n_split = p.n_split_int2 + 1;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  p.ticket_bytes = ((size_t(heads) * sizeof(int32_t) + 255) / 256) * 256;
+  p.partial_bytes = size_t(heads) * p.n_split * G * kPartialStride * sizeof(float);
+  p.total_bytes = p.ticket_bytes + p.partial_bytes;
+  return p;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_ARG: return "KVQ_ERR_ARG: invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: unsupported shape";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE: workspace too small";
+    case KVQ_ERR_NUMERIC: return "KVQ_ERR_NUMERIC: numerical failure";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP: HIP runtime error";
+    default: return "KVQ_ERR_UNKNOWN";
+  }
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+int kvq_quantize_append(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
+                        int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
+                        int32_t total_new, int32_t max_new, const uint16_t* k_new,
+                        const uint16_t* v_new, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != KVQ_OK) return rc;
+  if ((rc = check_layer(layer)) != KVQ_OK) return rc;
+  if ((rc = check_cache(dims, cache)) != KVQ_OK) return rc;
+  if (batch < 1 || total_new < 0 || max_new < 0 || max_new > total_new) return KVQ_ERR_ARG;
+  if (start_pos == nullptr || cu_new == nullptr) return KVQ_ERR_ARG;
+  if (total_new == 0) return KVQ_OK;
+  if (k_new == nullptr || v_new == nullptr || !aligned16(k_new) || !aligned16(v_new))
+    return KVQ_ERR_ARG;
+  int err = launch_quantize_append(*dims, resolved_scale(dims), *layer, *cache, batch, start_pos,
+                                   cu_new, total_new, k_new, v_new, stream);
+  if (err != 0) {
+    set_last_error(hip_error_name(err));
+    return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_dims* dims, int32_t batch, int32_t max_seq_len) {
+  if (check_dims(dims) != KVQ_OK || batch < 1 || max_seq_len < 0) return 0;
+  return make_decode_plan(*dims, batch, max_seq_len).total_bytes;
+}
+
+int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
+                         int32_t batch, const int32_t* seq_len, int32_t max_seq_len,
+                         const uint16_t* q, float* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int rc = check_dims(dims);
+  if (rc != KVQ_OK) return rc;
+  if ((rc = check_layer(layer)) != KVQ_OK) return rc;
+  if ((rc = check_cache(dims, cache)) != KVQ_OK) return rc;
+  if (batch < 1 || max_seq_len < 0 || seq_len == nullptr) return KVQ_ERR_ARG;
+  if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
+  if (int64_t(max_seq_len) > int64_t(cache->bt_stride) * dims->page_size) return KVQ_ERR_ARG;
+  const DecodePlan plan = make_decode_plan(*dims, batch, max_seq_len);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan.total_bytes)
+    return KVQ_ERR_WORKSPACE;
+  int err = launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
+                          max_seq_len, q, out, workspace, plan, selected_decode_kernel(), stream);
+  if (err != 0) {
+    set_last_error(hip_error_name(err));
+    return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal declarations shared by the libkvq2 sources (host validation,
+// calibration and the HIP launchers).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvq2.h"
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kChunkTokens = 16;       // a page is a whole number of 16-token chunks
+constexpr int kChunkBytes = 1152;      // 512 K codes + 512 V codes + 64 + 64 params
+constexpr int kKCodesOff = 0;
+constexpr int kVCodesOff = 512;
+constexpr int kKParamsOff = 1024;
+constexpr int kVParamsOff = 1088;
+constexpr int kMaxGroup = 16;          // query heads per KV head supported
+constexpr float kMaxClip = 16384.0f;   // keeps 2c/3 and c inside fp16 range
+constexpr int kPartialStride = 132;    // floats per (split, query head) partial:
+                                       // m, l, 2 pad, o'[128]
+
+// Resolved decode geometry shared by the workspace query and the launch.
+struct DecodePlan {
+  int n_split_int2;   // work-groups per (sequence, KV head) over INT2 chunks
+  int n_split;        // n_split_int2 + 1 (the last one takes the bf16 segments)
+  size_t ticket_bytes;
+  size_t partial_bytes;
+  size_t total_bytes;
+};
+
+DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len);
+
+// Kernel variants of the decode path.
+enum DecodeKernel { kDecodeMfma = 0, kDecodeValu = 1 };
+DecodeKernel selected_decode_kernel();
+
+// Launchers (defined in the .hip sources).  They return a hipError_t value
+// (0 = success) so that the host validation code needs no HIP headers.
+int launch_quantize_append(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
+                           const kvq_cache& cache, int32_t batch, const int32_t* start_pos,
+                           const int32_t* cu_new, int32_t total_new, const uint16_t* k_new,
+                           const uint16_t* v_new, void* stream);
+
+int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
+                  const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
+                  int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
+                  const DecodePlan& plan, DecodeKernel which, void* stream);
+
+const char* hip_error_name(int err);
+void set_last_error(const char* msg);
+
+}  // namespace kvq

@@ -1,0 +1,126 @@
+"""GPU parity of libkvq2 against the CPU oracle, through the C ABI.
+
+Cache bytes (INT2 codes, fp16 scale/zero, bf16 sink and ring) must match the
+oracle bit for bit; decode outputs within 2e-3 max normwise relative error
+(per output row: ||o - o_ref||_inf / ||o_ref||_inf), fp32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, Scenario, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _kernels():
+    return ["mfma", "valu"]
+
+
+@pytest.fixture(params=_kernels())
+def kernel(request, monkeypatch):
+    monkeypatch.setenv("KVQ_DECODE_KERNEL", request.param)
+    return request.param
+
+
+CASES = [
+    # Hq, Hkv, P, n_sink, W, lens
+    (4, 2, 16, 4, 128, [1024]),                        # the tiny workload's shape
+    (4, 2, 16, 4, 8, [70, 45, 0, 1, 4, 12, 13, 300]),  # ragged batch incl. empty and all-bf16
+    (8, 1, 32, 0, 16, [200, 17, 33]),                  # no sink, G = 8, page 32
+    (2, 2, 64, 20, 5, [400, 26, 130]),                 # G = 1, page 64, sink > 16
+    (16, 1, 16, 4, 1, [97, 5]),                        # G = 16, W = 1
+    (6, 2, 16, 3, 32, [333, 64]),                      # G = 3 (padded group)
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"h{c[0]}x{c[1]}_P{c[2]}_s{c[3]}_w{c[4]}")
+def test_bulk_append_bytes_and_decode(case, kernel):
+    Hq, Hkv, P, ns, W, lens = case
+    say(f"[case] {case} kernel={kernel}")
+    sc = Scenario(Hq, Hkv, P, ns, W, lens, seed=len(lens) * 13 + Hq, fill=0xA5)
+    sc.fill_to(pieces=3)
+    assert sc.cache_bytes_equal() == (True, True, True)
+    out, ref, _ = sc.decode()
+    e = rel_err(out, ref)
+    say(f"  rel_err={e:.3e}")
+    assert e <= TOL
+
+
+def test_decode_steps_with_single_token_appends(kernel):
+    """Decode loop: append one token per sequence (evicting ring tokens into
+    INT2), decode, repeat; compare bytes and outputs after each step."""
+    sc = Scenario(4, 2, 16, 4, 8, [40, 20, 9], seed=5)
+    sc.append([30, 11, 3])
+    for step in range(6):
+        sc.append([1, 1, 1])
+        assert sc.cache_bytes_equal() == (True, True, True), f"step {step}"
+        out, ref, _ = sc.decode(q_seed=step)
+        assert rel_err(out, ref) <= TOL, f"step {step}"
+
+
+def test_token_by_token_equals_bulk():
+    a = Scenario(4, 2, 16, 4, 16, [150, 77], seed=11)
+    b = Scenario(4, 2, 16, 4, 16, [150, 77], seed=11)
+    a.fill_to(pieces=1)
+    for _ in range(150):
+        b.append([1 if b.cur[0] < 150 else 0, 1 if b.cur[1] < 77 else 0])
+    torch.cuda.synchronize()
+    assert torch.equal(a.dc.pool, b.dc.pool)
+    assert torch.equal(a.dc.sink, b.dc.sink)
+    assert torch.equal(a.dc.recent, b.dc.recent)
+    assert b.cache_bytes_equal() == (True, True, True)
+
+
+def test_decode_deterministic_and_page_permutation_invariant(kernel):
+    sc = Scenario(4, 2, 16, 4, 32, [900, 500], seed=21)
+    sc.fill_to()
+    out1, ref, ws = sc.decode()
+    out2, _, _ = sc.decode()
+    assert np.array_equal(out1, out2)
+    # move every page to a new physical slot: same logical cache, same output bits
+    perm = np.random.default_rng(5).permutation(sc.num_pages)
+    pool = sc.dc.pool.clone()
+    sc.dc.pool[torch.from_numpy(perm).cuda().long()] = pool
+    bt = torch.where(sc.dc.block_table >= 0,
+                     torch.from_numpy(perm).cuda().int()[sc.dc.block_table.clamp(min=0).long()],
+                     sc.dc.block_table)
+    sc.dc.block_table.copy_(bt)
+    out3, _, _ = sc.decode()
+    assert np.array_equal(out1, out3)
+    assert rel_err(out1, ref) <= TOL
+
+
+def test_shared_prefix_pages():
+    """Two sequences whose first pages are the same physical pages (a shared,
+    read-only prefix) decode exactly like private copies."""
+    sc = Scenario(4, 2, 16, 4, 8, [200, 200], seed=3)
+    sc.k_all[1][:96] = sc.k_all[0][:96]
+    sc.v_all[1][:96] = sc.v_all[0][:96]
+    sc.fill_to(pieces=1)
+    out_priv, ref, _ = sc.decode()
+    shared = sc.dc.block_table.clone()
+    shared[1, :6] = shared[0, :6]                 # 96 tokens = 6 pages of 16
+    sc.dc.block_table.copy_(shared)
+    out_shared, _, _ = sc.decode()
+    assert np.array_equal(out_priv, out_shared)
+    assert rel_err(out_shared, ref) <= TOL
+
+
+def test_workspace_reuse_keeps_counters_at_zero(kernel):
+    sc = Scenario(4, 2, 16, 4, 8, [300, 100], seed=8)
+    sc.fill_to()
+    out1, ref, ws = sc.decode()
+    # The same workspace serves a second call; arrival counters are back at zero.
+    import long_context_decode_kvq_amd.kvq2 as K
+    seq = torch.tensor(sc.cur, dtype=torch.int32, device="cuda")
+    from gpu_helpers import dev_u16
+    from long_context_decode_kvq_amd.workloads import normal_bits
+    q = normal_bits(sc.seed * 31 + 99, (sc.B, 4, 128))
+    out = torch.empty((sc.B, 4, 128), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        K.decode_attention(sc.kd, sc.layer, sc.dc.handle, sc.B, seq, max(sc.cur), dev_u16(q), out, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), out1)
+    n_heads = sc.B * 2
+    assert int(ws[: 4 * n_heads].view(torch.int32).abs().sum()) == 0
