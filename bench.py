@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of one INT2 KV-cache decode step on one MI355X.
+
+A step is the whole hot path for one new token per sequence: quantize-append
+(rotate, evict the oldest recent token into INT2, write the ring) followed by
+fused split-K decode attention over the sink, INT2 and recent segments.
+
+Default workload: 28 sequences x 100000-token contexts, 32 query / 8 KV heads,
+head_dim 128, sink 4, recent 256, page 16, physical pages a seeded random
+permutation; one layer.  Inputs are seeded synthetic tensors drawn on the
+device; the cache is built before timing (inputs resident in HBM).
+
+Prints one JSON line: value = algorithmic bytes per step / step time (GB/s),
+ms_per_step, a roofline object for the decode kernel (algorithmic bytes per
+launch / its average duration, from HIP events recorded on the launch stream
+around every timed launch) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT2 paged decode-attention HBM GB/s (% of peak) + µs/step at 100K ctx"
+HBM_PEAK_GBS = 8000.0
+HEAD_DIM = 128
+INT2_BYTES = 72          # per (token, KV head): 2 x 32 code bytes + 2 x (fp16 s, fp16 z)
+BF16_BYTES = 512         # per (token, KV head): 2 x 128 bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def segment_counts(L, ns, W):
+    n_s = min(L, ns)
+    n_i = max(0, L - W - ns)
+    return n_s, n_i, L - n_s - n_i
+
+
+def decode_bytes(w, lens):
+    """Algorithmic HBM bytes of one decode launch (what the method must move)."""
+    tot = 0
+    for L in lens:
+        _, n_i, _ = segment_counts(int(L), w.n_sink, w.n_recent)
+        n_b = int(L) - n_i
+        tot += w.n_kv_heads * (INT2_BYTES * n_i + BF16_BYTES * n_b)
+        tot += 4 * math.ceil(int(L) / w.page_size)                  # block-table entries
+    tot += w.batch * w.n_q_heads * HEAD_DIM * (2 + 4)               # q bf16 in, out fp32
+    tot += 2 * w.n_kv_heads * HEAD_DIM * HEAD_DIM * 4               # R_K, R_V
+    return tot
+
+
+def append_bytes(w, lens_before):
+    """Algorithmic HBM bytes of one single-token quantize-append launch."""
+    per_vec = 256 + 256                                             # new bf16 in, ring write
+    tot = 0
+    for L in lens_before:
+        evict = int(L) - w.n_recent >= w.n_sink and int(L) >= w.n_sink
+        tot += w.n_kv_heads * 2 * (per_vec + ((256 + 36) if evict else 0))
+    tot += 2 * w.n_kv_heads * HEAD_DIM * HEAD_DIM * 4               # R_K, R_V
+    return tot
+
+
+def build_cache(w, kvq2, W, lens_before, n_steps, device):
+    """Calibrate, allocate and fill the cache to `lens_before` tokens per sequence."""
+    import numpy as np
+    import torch
+
+    t0 = time.time()
+    kd = kvq2.dims(w.n_q_heads, w.n_kv_heads, w.page_size, w.n_sink, w.n_recent)
+    q_c, k_c, v_c = W.calibration_tokens(w)
+    R_K, R_V, clip_K, clip_V = kvq2.calibrate(kd, q_c, k_c, v_c, 0.999)
+    log(f"[bench] calibrated on {q_c.shape[0]} tokens in {time.time() - t0:.1f}s "
+        f"(clip_K={clip_K:.3f}, clip_V={clip_V:.3f})")
+    final = lens_before + n_steps
+    bt, n_pages, _ = W.page_assignment(w, final)
+    dc = kvq2.DeviceCache(kd, w.batch, n_pages, bt, device=device)
+    dR_K = torch.from_numpy(R_K).to(device)
+    dR_V = torch.from_numpy(R_V).to(device)
+    lay = kvq2.layer(dR_K, dR_V, clip_K, clip_V)
+    t0 = time.time()
+    chunk = 8192
+    done = np.zeros(w.batch, np.int64)
+    while True:
+        todo = np.minimum(lens_before - done, chunk)
+        if todo.sum() == 0:
+            break
+        ks, vs = [], []
+        for b in range(w.batch):
+            if todo[b]:
+                k, v = W.sequence_kv_device(w, b, int(done[b]), int(todo[b]), device)
+                ks.append(k)
+                vs.append(v)
+        cu = np.zeros(w.batch + 1, np.int32)
+        cu[1:] = np.cumsum(todo)
+        kvq2.quantize_append(kd, lay, dc.handle, w.batch,
+                             torch.from_numpy(done.astype(np.int32)).to(device),
+                             torch.from_numpy(cu).to(device), int(cu[-1]), int(todo.max()),
+                             torch.cat(ks), torch.cat(vs))
+        done += todo
+    torch.cuda.synchronize()
+    log(f"[bench] built cache: {w.batch} x {int(lens_before.max())} tokens, {n_pages} pages "
+        f"({dc.pool.numel() / 2**30:.2f} GiB pool) in {time.time() - t0:.1f}s")
+    return kd, dc, lay, (dR_K, dR_V, R_K, R_V, clip_K, clip_V)
+
+
+def cpu_baseline(w, W, seconds_budget=30.0):
+    """The CPU oracle on a bounded sample of the workload: one (sequence, KV
+    head) pair at the full context, one step (append one token + decode for
+    its query heads), single-threaded."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    L = int(w.seq_lens()[0])
+    with threadpool_limits(limits=1):
+        q_c, k_c, v_c = W.calibration_tokens(w, 256)
+        cal = O.calibrate(q_c[:, :w.group], k_c[:, :1], v_c[:, :1], w.group, 1,
+                          1 / math.sqrt(HEAD_DIM), 0.999)
+        k, v = W.sequence_kv_device(w, 0, 0, L + 2, "cuda")
+        k = k[:, :1].cpu().numpy().view(np.uint16)
+        v = v[:, :1].cpu().numpy().view(np.uint16)
+        od = O.Dims(w.group, 1, w.page_size, w.n_sink, w.n_recent)
+        reps = 3
+        k, v = k[:L + reps - 1], v[:L + reps - 1]
+        npg = math.ceil((L + reps) / w.page_size)
+        oc = O.OracleCache(od, 1, npg, np.arange(npg, dtype=np.int32)[None])
+        t0 = time.perf_counter()
+        oc.append(cal.R_K, cal.R_V, cal.clip_K, cal.clip_V, 0, 0, k[:L - 1], v[:L - 1])
+        build_s = time.perf_counter() - t0
+        q = W.decode_queries_device(w, 0, "cuda")[:1, :w.group].cpu().numpy().view(np.uint16)
+        times = []
+        for r in range(reps):
+            t0 = time.perf_counter()
+            p = L - 1 + r
+            oc.append(cal.R_K, cal.R_V, cal.clip_K, cal.clip_V, 0, p, k[p:p + 1], v[p:p + 1])
+            oc.decode(cal.R_K, cal.R_V, [p + 1], q)
+            times.append(time.perf_counter() - t0)
+        step_s = float(np.median(times))
+    _, n_i, _ = segment_counts(L, w.n_sink, w.n_recent)
+    sample_bytes = (INT2_BYTES * n_i + BF16_BYTES * (L - n_i) + w.group * HEAD_DIM * 6
+                    + 2 * HEAD_DIM * HEAD_DIM * 4)
+    return {
+        "value": sample_bytes / step_s / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one (sequence, KV head) of the workload at context {L}: append 1 token + "
+                   f"decode {w.group} query heads, NumPy fp64 oracle, 1 thread; median of {reps} "
+                   f"steps {step_s:.2f}s (cache build {build_s:.1f}s untimed)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="conc_28x100k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(one process, one MI355X). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from long_context_decode_kvq_amd import kvq2
+    from long_context_decode_kvq_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    device = torch.device("cuda:0")
+    n_steps = args.warmup + args.steps
+    lens_before = w.seq_lens() - 1               # the first step appends token L-1
+    kd, dc, lay, keep = build_cache(w, kvq2, W, lens_before, n_steps, device)
+
+    # Small caches would be served from the 256 MB Infinity Cache: rotate
+    # independent pool copies so every step reads its pages from HBM.
+    pool_bytes = dc.pool.numel()
+    copies = 1 if pool_bytes >= 512 * 2**20 else int(math.ceil(512 * 2**20 / pool_bytes))
+    pools = [dc.pool] + [dc.pool.clone() for _ in range(copies - 1)]
+    handles = [dc.handle] + [kvq2.cache(p, dc.num_pages, dc.sink if w.n_sink > 0 else None,
+                                        dc.recent, dc.block_table) for p in pools[1:]]
+
+    max_len = int(lens_before.max()) + n_steps
+    ws = torch.zeros(kvq2.decode_workspace_bytes(kd, w.batch, max_len), dtype=torch.uint8,
+                     device=device)
+    out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=device)
+    cu1 = torch.arange(w.batch + 1, dtype=torch.int32, device=device)
+    starts = [torch.from_numpy((lens_before + k).astype(np.int32)).to(device) for k in range(n_steps)]
+    seqs = [torch.from_numpy((lens_before + k + 1).astype(np.int32)).to(device) for k in range(n_steps)]
+    qs = [W.decode_queries_device(w, k, device) for k in range(n_steps)]
+    new_kv = [W.sequence_kv_device(w, b, int(lens_before[b]), n_steps, device) for b in range(w.batch)]
+    k_new = [torch.stack([new_kv[b][0][k] for b in range(w.batch)]).contiguous() for k in range(n_steps)]
+    v_new = [torch.stack([new_kv[b][1][k] for b in range(w.batch)]).contiguous() for k in range(n_steps)]
+    stream = torch.cuda.current_stream()
+
+    def step(k, events=None):
+        h = handles[k % copies]
+        if events is not None:
+            events[0].record(stream)
+        kvq2.quantize_append(kd, lay, h, w.batch, starts[k], cu1, w.batch, 1, k_new[k], v_new[k],
+                             stream)
+        if events is not None:
+            events[1].record(stream)
+        kvq2.decode_attention(kd, lay, h, w.batch, seqs[k], max_len, qs[k], out, ws, stream)
+        if events is not None:
+            events[2].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    app_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    step_bytes = []
+    dec_bytes = []
+    for i in range(args.steps):
+        k = args.warmup + i
+        lb = lens_before + k
+        db = decode_bytes(w, lb + 1)
+        dec_bytes.append(db)
+        step_bytes.append(db + append_bytes(w, lb))
+    value = float(np.sum(step_bytes)) / (ms_per_step * 1e-3 * args.steps) / 1e9
+    achieved = float(np.mean(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us); "
+        f"decode {dec_avg_ms * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); append {np.mean(app_ms) * 1e3:.1f} us; "
+        f"decode {achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(w, W)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} GB/s in {time.time() - t0:.1f}s")
+
+    kernel = os.environ.get("KVQ_DECODE_KERNEL", "mfma")
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "context": int(lens_before.max()) + 1,
+            "context_note": "step k decodes at context + k (one appended token per step)",
+            "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": HEAD_DIM,
+            "page_size": w.page_size, "n_sink": w.n_sink, "n_recent": w.n_recent,
+            "layers": 1, "decode_kernel": kernel, "pool_copies": copies,
+            "us_per_step": round(ms_per_step * 1e3, 2),
+            "decode_us": round(dec_avg_ms * 1e3, 2),
+            "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
+            "step_pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

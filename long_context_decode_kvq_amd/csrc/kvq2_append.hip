@@ -5,7 +5,7 @@
 // One wave (64 lanes) handles one new (token, KV head, K|V) head-vector;
 // lane l owns channels l and l + 64.  A work-group of four waves shares one
 // (KV head, K|V) pair and stages that 64 KiB rotation matrix in LDS once for
-// the 16 tokens it handles.
+// the tokens it handles (16 for decode-size appends, 256 for bulk appends).
 //
 // Per vector:
 //   1. If the token is written to the recent ring and the slot's previous
@@ -19,7 +19,6 @@
 namespace kvq {
 namespace {
 
-constexpr int kTokensPerBlock = 16;
 constexpr int kWaves = 4;
 
 struct AppendArgs {
@@ -36,6 +35,7 @@ struct AppendArgs {
   const int32_t* start_pos;
   const int32_t* cu_new;
   int total_new;
+  int tokens_per_block;        // multiple of kWaves
   const uint16_t* x_new[2];
 };
 
@@ -101,8 +101,9 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
   const float clip = a.clip[kind];
   const int W = a.n_recent;
   const int ns = a.n_sink;
-  for (int it = 0; it < kTokensPerBlock / kWaves; ++it) {
-    const int n = blockIdx.x * kTokensPerBlock + wave * (kTokensPerBlock / kWaves) + it;
+  const int per_wave = a.tokens_per_block / kWaves;
+  for (int it = 0; it < per_wave; ++it) {
+    const int n = blockIdx.x * a.tokens_per_block + wave * per_wave + it;
     if (n >= a.total_new) break;
     // Sequence of token n: the largest b with cu_new[b] <= n.
     int lo = 0, hi = a.batch;
@@ -192,7 +193,10 @@ int launch_quantize_append(const kvq_dims& d, float /*sm_scale*/, const kvq_laye
   a.total_new = total_new;
   a.x_new[0] = k_new;
   a.x_new[1] = v_new;
-  dim3 grid((total_new + kTokensPerBlock - 1) / kTokensPerBlock, d.n_kv_heads, 2);
+  // Small (decode-step) appends: 16 tokens per work-group for parallelism;
+  // bulk appends: 256 so that each work-group stages R once per 256 vectors.
+  a.tokens_per_block = total_new <= 8192 ? 16 : 256;
+  dim3 grid((total_new + a.tokens_per_block - 1) / a.tokens_per_block, d.n_kv_heads, 2);
   hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());

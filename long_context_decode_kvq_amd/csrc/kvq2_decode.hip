@@ -1,6 +1,8 @@
 // Decode dispatch: fills the kernel arguments from the validated ABI
 // structures, carves the caller's workspace into arrival counters and
 // split-K partials, and launches the selected decode kernel.
+#include <cmath>
+
 #include "kvq2_decode_common.h"
 
 namespace kvq {
@@ -28,6 +30,14 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.n_sink = d.n_sink;
   a.n_recent = d.n_recent;
   a.alpha = sm_scale * kLog2e;
+  // Every V scale is fp16((max - min) / 3) of values clipped to +-clip_V, so
+  // s_V <= (2/3) clip_V (1 + 2^-11); sigma_v maps that bound to <= 1.
+  a.log2_sigma_v = -static_cast<int>(
+      std::ceil(std::log2(static_cast<double>(layer.clip_V) * (2.0 / 3.0) * 1.001)));
+  a.sigma_v = std::ldexp(1.0f, a.log2_sigma_v);
+  const int cpp = d.page_size / kChunkTokens;
+  a.log2_cpp = cpp == 1 ? 0 : cpp == 2 ? 1 : 2;
+  a.page_bytes = int64_t(d.n_kv_heads) * cpp * kChunkBytes;
   a.seq_len = seq_len;
   a.q = q;
   a.out = out;

@@ -12,6 +12,7 @@
 namespace kvq {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kCombineSlice = 64;   // splits staged per combine pass
 
 struct DecodeArgs {
   const float* R_K;
@@ -24,6 +25,10 @@ struct DecodeArgs {
   int32_t bt_stride;
   int n_q_heads, n_kv_heads, group, page_size, n_sink, n_recent;
   float alpha;                 // sm_scale * log2(e): logits are kept in base-2 units
+  float sigma_v;               // power of two with sigma_v * s_V <= 1 for every V scale
+  int log2_sigma_v;            // log2(sigma_v)
+  int log2_cpp;                // log2(page_size / 16)
+  int64_t page_bytes;          // bytes of one physical page: Hkv * page_size / 16 * 1152
   const int32_t* seq_len;
   const uint16_t* q;
   float* out;
@@ -33,16 +38,33 @@ struct DecodeArgs {
   int n_split;
 };
 
-// Chunk range [c_begin, c_end) of INT2 split `s` for a sequence of length L.
-__device__ __forceinline__ void int2_chunk_range(const DecodeArgs& a, int L, int s, int& c_begin,
-                                                 int& c_end, int& int2_end) {
-  int2_end = max(a.n_sink, L - a.n_recent);
-  const int first = a.n_sink / kChunkTokens;
-  const int last = (int2_end + kChunkTokens - 1) / kChunkTokens;
-  const int n = int2_end > a.n_sink ? last - first : 0;
+// INT2 work of a sequence of length L is split in two parts:
+//  * whole tiles of `npt` fully valid 16-token chunks [cf, cl), cut into
+//    n_split_int2 contiguous tile ranges (one per split work-group);
+//  * the few INT2 positions outside them (the partial chunk after the sink,
+//    the partial chunk before the recent window and a sub-tile remainder),
+//    which the work-group of the bf16 segments handles token by token.
+struct Int2Range {
+  int int2_end;   // INT2 positions are [n_sink, int2_end)
+  int cf, cl;     // tiled chunks [cf, cl), cl - cf a multiple of npt
+};
+
+__device__ __forceinline__ Int2Range int2_range(const DecodeArgs& a, int L, int npt) {
+  Int2Range r;
+  r.int2_end = max(a.n_sink, L - a.n_recent);
+  r.cf = (a.n_sink + kChunkTokens - 1) / kChunkTokens;
+  const int full_end = r.int2_end / kChunkTokens;
+  r.cl = full_end > r.cf ? r.cf + npt * ((full_end - r.cf) / npt) : r.cf;
+  return r;
+}
+
+// Tile range [t_begin, t_end) of INT2 split s.
+__device__ __forceinline__ void split_tiles(const DecodeArgs& a, const Int2Range& r, int npt, int s,
+                                            int& t_begin, int& t_end) {
+  const int n = (r.cl - r.cf) / npt;
   const int per = (n + a.n_split_int2 - 1) / a.n_split_int2;
-  c_begin = first + min(n, s * per);
-  c_end = first + min(n, (s + 1) * per);
+  t_begin = min(n, s * per);
+  t_end = min(n, (s + 1) * per);
 }
 
 // q'[g][i] = alpha * sum_j R_K[h][j][i] q[b][hG+g][j] into LDS, plus
@@ -74,6 +96,163 @@ __device__ void rotate_queries(const DecodeArgs& a, int b, int h, float (*qraw)[
   __syncthreads();
 }
 
+// Online-softmax update of one 16-token tile for a wave whose lane (t, qq)
+// = (lane / 4, lane % 4) holds the logit of token t in lg[g] (-inf when
+// masked; the four lanes of a token hold the same value).  Updates the
+// running (m, l) per head, returns the correction factor per head and
+// leaves p = exp2(logit - m) in lg.
+template <int GP>
+__device__ __forceinline__ void softmax_tile16(int G, int qq, float* lg, float* corr, float* m,
+                                               float* l) {
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (g >= G) { corr[g] = 1.f; lg[g] = 0.f; continue; }
+    float tm = lg[g];
+    tm = fmaxf(tm, __shfl_xor(tm, 4));
+    tm = fmaxf(tm, __shfl_xor(tm, 8));
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    const float mn = fmaxf(m[g], tm);
+    if (mn == -INFINITY) { corr[g] = 1.f; lg[g] = 0.f; continue; }
+    corr[g] = exp2f(m[g] - mn);
+    const float p = lg[g] == -INFINITY ? 0.f : exp2f(lg[g] - mn);
+    const float ps = wave_sum((qq == 0) ? p : 0.f);
+    l[g] = l[g] * corr[g] + ps;
+    m[g] = mn;
+    lg[g] = p;
+  }
+}
+
+// Token-by-token path for the tokens outside the tiled INT2 chunks: the bf16
+// sink [0, min(L, n_sink)), the INT2 head tail [n_sink, min(16 cf, int2_end)),
+// the INT2 end tail [16 cl, int2_end) and the bf16 recent window
+// [max(n_sink, L - W), L); tiles of 16 tokens per wave, plain fp32.
+// Lane (t, qq) dots 32 channels of token t's key with q' (LDS); the lane
+// owns channels 2*lane, 2*lane+1 of o'.  INT2 tokens are dequantized in
+// registers: key dot = s_K (q'.c) + z_K sum(q'), value = z_V + s_V c.
+template <int GP>
+__device__ void token_path(const DecodeArgs& a, int b, int h, int L, const Int2Range& rg,
+                           const float (*qs)[kHeadDim], const float* qsum,
+                           float (*pbuf)[16][GP], float* m, float* l, float* acc0, float* acc1) {
+  const int G = a.group;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = lane >> 2, qq = lane & 3;
+  const int n_sk = min(L, a.n_sink);
+  const int h_end = min(rg.cf * kChunkTokens, rg.int2_end);
+  const int n_hd = max(0, h_end - a.n_sink);
+  const int e_begin = rg.cl * kChunkTokens;
+  const int n_en = max(0, rg.int2_end - e_begin);
+  const int r_begin = max(a.n_sink, L - a.n_recent);
+  const int n_rc = max(0, L - r_begin);
+  const int n_all = n_sk + n_hd + n_en + n_rc;
+  const int64_t sh_base = int64_t(b) * a.n_kv_heads + h;
+  // position of virtual token idx
+  auto position = [&](int idx) -> int {
+    if (idx < n_sk) return idx;
+    idx -= n_sk;
+    if (idx < n_hd) return a.n_sink + idx;
+    idx -= n_hd;
+    if (idx < n_en) return e_begin + idx;
+    return r_begin + (idx - n_en);
+  };
+  auto bf16_ptr = [&](int pos) -> const uint16_t* {
+    if (pos < a.n_sink) return a.sink + (sh_base * a.n_sink + pos) * 2 * kHeadDim;
+    return a.recent + (sh_base * a.n_recent + (pos - a.n_sink) % a.n_recent) * 2 * kHeadDim;
+  };
+  auto is_int2 = [&](int pos) { return pos >= a.n_sink && pos < rg.int2_end; };
+  for (int tile = wave; tile * 16 < n_all; tile += 4) {
+    const int idx = tile * 16 + t;
+    const bool valid = idx < n_all;
+    const int pos = position(valid ? idx : 0);
+    // partial dot over this lane's 32 channels; the quad reduction follows
+    float dot[GP], ksc = 1.f, kzr = 0.f;
+#pragma unroll
+    for (int g = 0; g < GP; ++g) dot[g] = 0.f;
+    if (valid && is_int2(pos)) {
+      const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
+                                       a.page_size, b, h, pos);
+      const uint8_t* ch = a.pool + (off < 0 ? 0 : off);
+      const int ts = pos % kChunkTokens;
+      const uint2 kc = *reinterpret_cast<const uint2*>(ch + kKCodesOff + 32 * ts + 8 * qq);
+      const uint32_t kp = *reinterpret_cast<const uint32_t*>(ch + kKParamsOff + 4 * ts);
+      ksc = f16_bits_to_float(kp & 0xFFFFu);
+      kzr = f16_bits_to_float(kp >> 16);
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g < G) {
+          const float* qv = &qs[g][32 * qq];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) dot[g] = fmaf(qv[k], float((kc.x >> (2 * k)) & 3u), dot[g]);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) dot[g] = fmaf(qv[16 + k], float((kc.y >> (2 * k)) & 3u), dot[g]);
+        }
+      }
+    } else if (valid) {
+      const uint16_t* kp = bf16_ptr(pos) + 32 * qq;
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g < G) {
+#pragma unroll
+          for (int k = 0; k < 32; ++k) dot[g] = fmaf(qs[g][32 * qq + k], bf16_bits_to_float(kp[k]), dot[g]);
+        }
+      }
+    }
+    float lg[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      float d = dot[g];
+      d += __shfl_xor(d, 1);
+      d += __shfl_xor(d, 2);
+      lg[g] = (valid && g < G) ? fmaf(ksc, d, kzr * qsum[g]) : -INFINITY;
+    }
+    float corr[GP];
+    softmax_tile16<GP>(G, qq, lg, corr, m, l);
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (qq == 0) pbuf[wave][t][g] = lg[g];
+      acc0[g] *= corr[g];
+      acc1[g] *= corr[g];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int nt = min(16, n_all - tile * 16);
+    float v0[16], v1[16];
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {   // all loads first: one memory latency per tile
+      v0[tt] = 0.f;
+      v1[tt] = 0.f;
+      if (tt < nt) {
+        const int pp = position(tile * 16 + tt);
+        if (is_int2(pp)) {
+          const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
+                                           a.page_size, b, h, pp);
+          const uint8_t* ch = a.pool + (off < 0 ? 0 : off);
+          const int ts = pp % kChunkTokens, cg = lane >> 1;
+          const uint32_t byte = ch[kVCodesOff + 32 * (cg & 15) + 8 * (ts >> 2) + 4 * (cg >> 4) + (ts & 3)];
+          const uint32_t vp = *reinterpret_cast<const uint32_t*>(ch + kVParamsOff + 4 * ts);
+          const float sv = f16_bits_to_float(vp & 0xFFFFu), zv = f16_bits_to_float(vp >> 16);
+          const int sh = 4 * (lane & 1);
+          v0[tt] = fmaf(sv, float((byte >> sh) & 3u), zv);
+          v1[tt] = fmaf(sv, float((byte >> (sh + 2)) & 3u), zv);
+        } else {
+          const uint32_t v2 = *reinterpret_cast<const uint32_t*>(bf16_ptr(pp) + kHeadDim + 2 * lane);
+          v0[tt] = bf16_bits_to_float(v2 & 0xFFFFu);
+          v1[tt] = bf16_bits_to_float(v2 >> 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        const float p = tt < nt ? pbuf[wave][tt][g] : 0.f;
+        acc0[g] = fmaf(p, v0[tt], acc0[g]);
+        acc1[g] = fmaf(p, v1[tt], acc1[g]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Merge the softmax states of the 4 waves of a work-group (m, l per head and
 // unnormalized o'[128] per head, staged in LDS) and store the work-group's
 // partial for split `s`.  Then take an arrival ticket; the last work-group of
@@ -86,52 +265,127 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
   const int tid = threadIdx.x;
   const int64_t head = int64_t(b) * a.n_kv_heads + h;
   float* part = a.partials + (head * a.n_split + s) * G * kPartialStride;
-  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][g]);
-    float o = 0.0f, l = 0.0f;
-    if (M != -INFINITY) {
-      for (int w = 0; w < 4; ++w) {
-        const float f = exp2f(wm[w][g] - M);
-        o += f * wo[w][g][c];
-        l += f * wl[w][g];
+  // Merged partial -> LDS (wo[0] is free once every thread has read its
+  // inputs), then one wave stores it, makes it visible device-wide (one
+  // agent-scope release per work-group) and takes the arrival ticket.
+  float* stage = &wo[0][0][0];
+  float merged[(GP * kHeadDim + 255) / 256];
+  float Ms[(GP * kHeadDim + 255) / 256], Ls[(GP * kHeadDim + 255) / 256];
+#pragma unroll
+  for (int k = 0; k < (GP * kHeadDim + 255) / 256; ++k) {
+    const int i = tid + 256 * k;
+    merged[k] = 0.f;
+    Ms[k] = -INFINITY;
+    Ls[k] = 0.f;
+    if (i < G * kHeadDim) {
+      const int g = i / kHeadDim, c = i % kHeadDim;
+      float M = -INFINITY;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][g]);
+      float o = 0.0f, l = 0.0f;
+      if (M != -INFINITY) {
+        for (int w = 0; w < 4; ++w) {
+          const float f = exp2f(wm[w][g] - M);
+          o += f * wo[w][g][c];
+          l += f * wl[w][g];
+        }
       }
-    }
-    part[g * kPartialStride + 4 + c] = o;
-    if (c == 0) {
-      part[g * kPartialStride + 0] = M;
-      part[g * kPartialStride + 1] = l;
+      merged[k] = o;
+      Ms[k] = M;
+      Ls[k] = l;
     }
   }
-  // Release: every thread makes its partial writes visible device-wide
-  // before the work-group's arrival is counted.
-  __threadfence();
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < (GP * kHeadDim + 255) / 256; ++k) {
+    const int i = tid + 256 * k;
+    if (i < G * kHeadDim) {
+      const int g = i / kHeadDim, c = i % kHeadDim;
+      stage[g * kPartialStride + 4 + c] = merged[k];
+      if (c == 0) {
+        stage[g * kPartialStride + 0] = Ms[k];
+        stage[g * kPartialStride + 1] = Ls[k];
+      }
+    }
+  }
   __syncthreads();
   __shared__ int is_last;
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.tickets[head], 1);
-    is_last = (prev == a.n_split - 1);
+  if (tid < 64) {
+    for (int i = tid; i < G * kPartialStride; i += 64) part[i] = stage[i];
+    __threadfence();   // release of this wave's stores, once per work-group
+    if (tid == 0) {
+      const int prev = atomicAdd(&a.tickets[head], 1);
+      is_last = (prev == a.n_split - 1);
+    }
   }
   __syncthreads();
   if (!is_last) return;
   __threadfence();   // acquire: see every other work-group's partials
 
+  // Split weights f_i = 2^(m_i - M) / sum_k 2^(m_k - M) l_k, staged in LDS
+  // in slices of kCombineSlice splits so that all loads of a slice are in
+  // flight together.
   const float* base = a.partials + head * a.n_split * G * kPartialStride;
-  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    float M = -INFINITY;
-    for (int t = 0; t < a.n_split; ++t) M = fmaxf(M, base[(t * G + g) * kPartialStride]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
-      for (int t = 0; t < a.n_split; ++t) {
-        const float* p = base + (t * G + g) * kPartialStride;
-        const float f = exp2f(p[0] - M);
-        num += f * p[4 + c];
-        den += f * p[1];
+  __shared__ float s_m[kCombineSlice][GP];
+  __shared__ float s_l[kCombineSlice][GP];
+  __shared__ float s_M[GP], s_den[GP];
+  const int wave = tid >> 6, lane = tid & 63;
+  if (tid < GP) { s_M[tid] = -INFINITY; s_den[tid] = 0.f; }
+  __syncthreads();
+  for (int s0 = 0; s0 < a.n_split; s0 += kCombineSlice) {      // pass 1: M per head
+    const int ns = min(kCombineSlice, a.n_split - s0);
+    for (int i = tid; i < ns * G; i += blockDim.x) {
+      const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
+      s_m[i / G][i % G] = p[0];
+    }
+    __syncthreads();
+    for (int g = wave; g < G; g += 4) {
+      float mx = -INFINITY;
+      for (int i = lane; i < ns; i += 64) mx = fmaxf(mx, s_m[i][g]);
+      mx = wave_max(mx);
+      if (lane == 0) s_M[g] = fmaxf(s_M[g], mx);
+    }
+    __syncthreads();
+  }
+  constexpr int KO = (GP * kHeadDim + 255) / 256;             // outputs per thread
+  float acc[KO];
+#pragma unroll
+  for (int k = 0; k < KO; ++k) acc[k] = 0.f;
+  for (int s0 = 0; s0 < a.n_split; s0 += kCombineSlice) {      // pass 2: weighted sums
+    const int ns = min(kCombineSlice, a.n_split - s0);
+    for (int i = tid; i < ns * G; i += blockDim.x) {
+      const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
+      const float M = s_M[i % G];
+      const float f = M == -INFINITY ? 0.f : exp2f(p[0] - M);
+      s_m[i / G][i % G] = f;
+      s_l[i / G][i % G] = f * p[1];
+    }
+    __syncthreads();
+    for (int g = wave; g < G; g += 4) {
+      float dn = 0.f;
+      for (int i = lane; i < ns; i += 64) dn += s_l[i][g];
+      dn = wave_sum(dn);
+      if (lane == 0) s_den[g] += dn;
+    }
+#pragma unroll
+    for (int k = 0; k < KO; ++k) {
+      const int o = tid + k * blockDim.x;
+      if (o < G * kHeadDim) {
+        const int g = o / kHeadDim, c = o % kHeadDim;
+        float v = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < ns; ++i) v = fmaf(s_m[i][g], base[((s0 + i) * G + g) * kPartialStride + 4 + c], v);
+        acc[k] += v;
       }
     }
-    ocomb[g][c] = den > 0.0f ? num / den : 0.0f;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < KO; ++k) {
+    const int o = tid + k * blockDim.x;
+    if (o < G * kHeadDim) {
+      const int g = o / kHeadDim, c = o % kHeadDim;
+      ocomb[g][c] = s_den[g] > 0.f ? acc[k] / s_den[g] : 0.f;
+    }
   }
   __syncthreads();
   // o = R_V o' (row-major R_V: o_i = sum_j R_V[i][j] o'_j)
@@ -139,16 +393,16 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int g = i / kHeadDim, c = i % kHeadDim;
     const float4* row = reinterpret_cast<const float4*>(R + c * kHeadDim);
-    float acc = 0.0f;
+    float o = 0.0f;
 #pragma unroll 4
     for (int j = 0; j < kHeadDim / 4; ++j) {
       const float4 r = row[j];
-      acc = fmaf(r.x, ocomb[g][4 * j + 0], acc);
-      acc = fmaf(r.y, ocomb[g][4 * j + 1], acc);
-      acc = fmaf(r.z, ocomb[g][4 * j + 2], acc);
-      acc = fmaf(r.w, ocomb[g][4 * j + 3], acc);
+      o = fmaf(r.x, ocomb[g][4 * j + 0], o);
+      o = fmaf(r.y, ocomb[g][4 * j + 1], o);
+      o = fmaf(r.z, ocomb[g][4 * j + 2], o);
+      o = fmaf(r.w, ocomb[g][4 * j + 3], o);
     }
-    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] = acc;
+    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] = o;
   }
   if (tid == 0) a.tickets[head] = 0;   // ready for the next call on this workspace
 }

@@ -38,40 +38,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; zacc[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
 
   const int t = lane >> 2, qq = lane & 3;
-  // Online-softmax update for one 16-token tile whose per-lane logits are in
-  // `lg` (lane (t, qq) holds token t; -inf for masked tokens).  Returns the
-  // correction factor per head and leaves p in `lg`.
-  auto softmax_tile = [&](float* lg, float* corr) {
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      if (g >= G) { corr[g] = 1.f; lg[g] = 0.f; continue; }
-      float tm = lg[g];
-      tm = fmaxf(tm, __shfl_xor(tm, 4));
-      tm = fmaxf(tm, __shfl_xor(tm, 8));
-      tm = fmaxf(tm, __shfl_xor(tm, 16));
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mn = fmaxf(m[g], tm);
-      if (mn == -INFINITY) { corr[g] = 1.f; lg[g] = 0.f; continue; }
-      corr[g] = exp2f(m[g] - mn);
-      const float p = exp2f(lg[g] - mn);
-      float ps = (qq == 0) ? p : 0.f;
-      ps = wave_sum(ps);
-      l[g] = l[g] * corr[g] + ps;
-      m[g] = mn;
-      lg[g] = p;
-    }
-  };
 
+  const Int2Range rg = int2_range(a, L, 1);
   if (s < a.n_split_int2) {
-    int c_begin, c_end, int2_end;
-    int2_chunk_range(a, L, s, c_begin, c_end, int2_end);
-    for (int c = c_begin + wave; c < c_end; c += 4) {
-      const int pos = c * kChunkTokens + t;
+    int t_begin, t_end;
+    split_tiles(a, rg, 1, s, t_begin, t_end);
+    for (int c = rg.cf + t_begin + wave; c < rg.cf + t_end; c += 4) {
       const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
                                        a.page_size, b, h, c * kChunkTokens);
       if (off < 0) continue;   // invalid page entry: the chunk is skipped
       const uint8_t* ch = a.pool + off;
-      const bool valid = pos >= a.n_sink && pos < int2_end;
       const uint2 kc = *reinterpret_cast<const uint2*>(ch + kKCodesOff + 32 * t + 8 * qq);
       const uint32_t kp = *reinterpret_cast<const uint32_t*>(ch + kKParamsOff + 4 * t);
       const uint32_t vp = *reinterpret_cast<const uint32_t*>(ch + kVParamsOff + 4 * t);
@@ -89,12 +65,12 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         dot += __shfl_xor(dot, 1);
         dot += __shfl_xor(dot, 2);
         const float sk = f16_bits_to_float(kp & 0xFFFFu), zk = f16_bits_to_float(kp >> 16);
-        lg[g] = valid ? fmaf(sk, dot, zk * qsum[g]) : -INFINITY;
+        lg[g] = (g < G) ? fmaf(sk, dot, zk * qsum[g]) : -INFINITY;
       }
       float corr[GP];
-      softmax_tile(lg, corr);
-      const float sv = valid ? f16_bits_to_float(vp & 0xFFFFu) : 0.f;
-      const float zv = valid ? f16_bits_to_float(vp >> 16) : 0.f;
+      softmax_tile16<GP>(G, qq, lg, corr, m, l);
+      const float sv = f16_bits_to_float(vp & 0xFFFFu);
+      const float zv = f16_bits_to_float(vp >> 16);
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
         if (qq == 0) wbuf[wave][t][g] = lg[g] * sv;
@@ -124,54 +100,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
   } else {
-    // bf16 sink and recent tokens, in tiles of 16 per wave.
-    const int n_sk = min(L, a.n_sink);
-    const int r_begin = max(a.n_sink, L - a.n_recent);
-    const int n_bf = n_sk + max(0, L - r_begin);
-    const int64_t sh_base = int64_t(b) * a.n_kv_heads + h;
-    auto token_ptr = [&](int idx) -> const uint16_t* {
-      const int pos = idx < n_sk ? idx : r_begin + (idx - n_sk);
-      if (pos < a.n_sink) return a.sink + (sh_base * a.n_sink + pos) * 2 * kHeadDim;
-      return a.recent + (sh_base * a.n_recent + (pos - a.n_sink) % a.n_recent) * 2 * kHeadDim;
-    };
-    for (int tile = wave; tile * 16 < n_bf; tile += 4) {
-      const int idx = tile * 16 + t;
-      const bool valid = idx < n_bf;
-      float lg[GP];
-      const uint16_t* kp = token_ptr(valid ? idx : 0) + 32 * qq;
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        float dot = 0.f;
-        if (g < G && valid) {
-#pragma unroll
-          for (int k = 0; k < 32; ++k) dot = fmaf(qs[g][32 * qq + k], bf16_bits_to_float(kp[k]), dot);
-        }
-        dot += __shfl_xor(dot, 1);
-        dot += __shfl_xor(dot, 2);
-        lg[g] = valid ? dot : -INFINITY;
-      }
-      float corr[GP];
-      softmax_tile(lg, corr);
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        if (qq == 0) pbuf[wave][t][g] = lg[g];
-        acc0[g] *= corr[g];
-        acc1[g] *= corr[g];
-      }
-      __builtin_amdgcn_wave_barrier();
-      const int nt = min(16, n_bf - tile * 16);
-      for (int tt = 0; tt < nt; ++tt) {
-        const uint32_t v2 = *reinterpret_cast<const uint32_t*>(token_ptr(tile * 16 + tt) + kHeadDim + 2 * lane);
-        const float v0 = bf16_bits_to_float(v2 & 0xFFFFu), v1 = bf16_bits_to_float(v2 >> 16);
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-          const float p = pbuf[wave][tt][g];
-          acc0[g] = fmaf(p, v0, acc0[g]);
-          acc1[g] = fmaf(p, v1, acc1[g]);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
+    token_path<GP>(a, b, h, L, rg, qs, qsum, pbuf, m, l, acc0, acc1);
   }
 
   // Wave state -> LDS (o' = acc + zero term on every channel).

@@ -60,4 +60,22 @@ __device__ __forceinline__ int64_t chunk_offset(const int32_t* block_table, int3
          int64_t(kChunkBytes);
 }
 
+// Same, for a wave-uniform position: the block-table entry is read through the
+// scalar data cache (the table is read-only while a kernel runs).
+__device__ __forceinline__ int64_t chunk_offset_uniform(const int32_t* block_table,
+                                                        int32_t bt_stride, int64_t num_pages,
+                                                        int n_kv_heads, int page_size, int b,
+                                                        int h, int pos) {
+  pos = __builtin_amdgcn_readfirstlane(pos);
+  if (pos < 0) return -1;
+  const int lp = pos / page_size;
+  if (lp >= bt_stride) return -1;
+  typedef const int32_t __attribute__((address_space(4))) const_i32;
+  const int32_t page = ((const_i32*)block_table)[int64_t(b) * bt_stride + lp];
+  if (page < 0 || page >= num_pages) return -1;
+  const int cpp = page_size / kChunkTokens;
+  return ((int64_t(page) * n_kv_heads + h) * cpp + (pos % page_size) / kChunkTokens) *
+         int64_t(kChunkBytes);
+}
+
 }  // namespace kvq

@@ -77,10 +77,11 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   const int64_t last_chunk = (int2_end + kChunkTokens - 1) / kChunkTokens;   // exclusive
   const int64_t n_chunks = int2_end > d.n_sink ? last_chunk - first_chunk : 0;
   const int64_t heads = int64_t(batch) * d.n_kv_heads;
-  // Enough work-groups to fill 256 CUs several times over, but no split
-  // shorter than 16 chunks (256 tokens).
-  int64_t ns = (2048 + heads - 1) / std::max<int64_t>(heads, 1);
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, n_chunks / 16));
+  // About 1536 INT2 work-groups (two rounds of three per CU on 256 CUs), but
+  // no split shorter than 64 chunks (1024 tokens): the prologue (query
+  // rotation) and the split combine are paid per work-group.
+  int64_t ns = (1536 + heads - 1) / std::max<int64_t>(heads, 1);
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, n_chunks / 64));
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, 512));
   const int forced = env_int("KVQ_NSPLIT", 0);
   if (forced > 0) ns = std::min(forced, 4096);

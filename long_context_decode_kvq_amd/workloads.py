@@ -175,3 +175,53 @@ def page_assignment(w: Workload, seq_lens: np.ndarray, extra_pages: int = 0):
         for p in range(shared_pages):
             bt[b, p] = owner[(sharers[0], p)]
     return bt, total, sharers
+
+
+# --------------------------------------------------------------------------
+# Device-side draws for the large workloads (torch's GPU generator).  The
+# same seeds give the same values on every call, so a sub-range (one
+# sequence, one block of tokens) can be re-drawn and copied to the host.
+# --------------------------------------------------------------------------
+
+DEVICE_BLOCK = 4096
+
+
+def sequence_kv_device(w: Workload, b: int, offset: int, length: int, device="cuda"):
+    """(k, v) bf16 bit patterns as int16 tensors [length][Hkv][128] on `device`.
+
+    Token block i (DEVICE_BLOCK tokens) of sequence b is drawn from a torch
+    generator seeded with (7000 + 100*index + b) * 100003 + i.  With a shared
+    prefix, sequences that share it draw their first `shared_prefix` tokens
+    from the first sharer's seed.
+    """
+    scale = torch.from_numpy(k_channel_scales(w)).to(device)[None]
+    out_k, out_v = [], []
+    first = offset // DEVICE_BLOCK
+    last = (offset + length - 1) // DEVICE_BLOCK
+    for i in range(first, last + 1):
+        bb = b
+        if w.shared_prefix and (i + 1) * DEVICE_BLOCK <= w.shared_prefix:
+            bb = _shared_owner(w, b)
+        gen = torch.Generator(device=device)
+        gen.manual_seed((7000 + 100 * w.index + bb) * 100003 + i)
+        shape = (DEVICE_BLOCK, w.n_kv_heads, HEAD_DIM)
+        k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * scale
+        v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        out_k.append(k.to(torch.bfloat16).view(torch.int16))
+        out_v.append(v.to(torch.bfloat16).view(torch.int16))
+    k = torch.cat(out_k)[offset - first * DEVICE_BLOCK: offset - first * DEVICE_BLOCK + length]
+    v = torch.cat(out_v)[offset - first * DEVICE_BLOCK: offset - first * DEVICE_BLOCK + length]
+    return k.contiguous(), v.contiguous()
+
+
+def _shared_owner(w: Workload, b: int) -> int:
+    _, _, sharers = page_assignment(w, w.seq_lens())
+    return sharers[0] if b in sharers else b
+
+
+def decode_queries_device(w: Workload, step: int, device="cuda") -> torch.Tensor:
+    """q bf16 bits (int16 tensor) [B][Hq][128] for decode step `step`."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(9000 + 100 * w.index + step)
+    q = torch.randn((w.batch, w.n_q_heads, HEAD_DIM), generator=gen, device=device)
+    return q.to(torch.bfloat16).view(torch.int16).contiguous()
