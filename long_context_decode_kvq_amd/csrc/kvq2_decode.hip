@@ -7,6 +7,86 @@
 
 namespace kvq {
 
+namespace {
+
+// Query rotation pre-pass, one work-group per (KV head, sequence):
+// q'[g] = alpha * R_K[h]^T q[b][hG+g] (OSCAR summary sec. 2.2-B: the query is
+// rotated once instead of un-rotating every cached key), plus sum(q'[g]) and
+// the exponent e with 2^-e max|q'[g]| < 1 used to scale f16 MFMA operands.
+__global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
+  __shared__ float qraw[kMaxGroup][kHeadDim];
+  __shared__ float qs[kMaxGroup][kHeadDim];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int G = a.group;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
+    const int g = i / kHeadDim, c = i % kHeadDim;
+    qraw[g][c] = bf16_bits_to_float(a.q[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c]);
+  }
+  __syncthreads();
+  const float* R = a.R_K + int64_t(h) * kHeadDim * kHeadDim;
+  float* dst = a.qrot + (int64_t(b) * a.n_q_heads + int64_t(h) * G) * kQStride;
+  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
+    const int g = i / kHeadDim, c = i % kHeadDim;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int j = 0; j < kHeadDim; ++j) acc = fmaf(R[j * kHeadDim + c], qraw[g][j], acc);
+    acc *= a.alpha;
+    qs[g][c] = acc;
+    dst[g * kQStride + c] = acc;
+  }
+  __syncthreads();
+  __shared__ float qsum[kMaxGroup];
+  __shared__ int qexp[kMaxGroup];
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int g = wave; g < G; g += blockDim.x / 64) {
+    const float v0 = qs[g][lane], v1 = qs[g][lane + 64];
+    const float sum = wave_sum(v0 + v1);
+    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    if (lane == 0) {
+      const int e = mx > 0.f ? ilogbf(mx) + 1 : 0;
+      dst[g * kQStride + kHeadDim] = sum;
+      dst[g * kQStride + kHeadDim + 1] = float(e);
+      qsum[g] = sum;
+      qexp[g] = e;
+    }
+  }
+  __syncthreads();
+  // QK operand of the MFMA kernel in its per-lane layout: lane (gq, n) holds
+  // column n = 2GP p + GP t + g (t = 0: f16 hi part, 1: lo part of q'[g]
+  // scaled by 2^-e_g 2^(8 - 2s)) for the 32 k-slots of its lane group.
+  if (a.gp == 0) return;
+  const int GP = a.gp;
+  uint32_t* bq = a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords;
+  {
+    const int kk = tid >> 6;                 // 4 k-steps x 64 lanes
+    const int gq = lane >> 4, n = lane & 15;
+    const int j = n % (2 * GP), g = j % GP;
+    const bool hi_col = j < GP, ok = g < G;
+    const float down = ok ? ldexpf(1.0f, -qexp[g]) : 0.f;
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+      for (int e = 0; e < 2; ++e) {
+        int ch, sc;
+        kslot_channel(gq, kk, 2 * q + e, ch, sc);
+        const float v = ok ? qs[g][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
+        const _Float16 vh = static_cast<_Float16>(v);
+        const _Float16 vl = static_cast<_Float16>(v - static_cast<float>(vh));
+        const uint32_t bits = __builtin_bit_cast(uint16_t, hi_col ? vh : vl);
+        word |= bits << (16 * e);
+      }
+      bq[lane * 16 + kk * 4 + q] = word;
+    }
+    if (kk == 0) {
+      const float qscale = ok ? ldexpf(1.0f, 16 + qexp[g]) : 1.0f;
+      reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane] = qscale;
+      reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane + 1] = ok ? qsum[g] / qscale : 0.f;
+    }
+  }
+}
+
+}  // namespace
+
 int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
 int launch_decode_mfma(const DecodeArgs& a, int batch, void* stream);
 
@@ -42,9 +122,20 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.q = q;
   a.out = out;
   a.tickets = static_cast<int32_t*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ticket_bytes);
+  a.work_counter = a.tickets + int64_t(batch) * d.n_kv_heads;
+  a.batch = batch;
+  char* ws = static_cast<char*>(workspace);
+  a.qrot = reinterpret_cast<float*>(ws + plan.ticket_bytes);
+  a.bq = reinterpret_cast<uint32_t*>(ws + plan.ticket_bytes + plan.qrot_bytes);
+  a.partials = reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes);
+  const int G = a.group;
+  a.gp = (which == kDecodeValu || G > 8) ? 0 : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
   a.n_split_int2 = plan.n_split_int2;
   a.n_split = plan.n_split;
+  hipLaunchKernelGGL(rotate_q_kernel, dim3(d.n_kv_heads, batch), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  const int err = static_cast<int>(hipGetLastError());
+  if (err != 0) return err;
   if (which == kDecodeValu) return launch_decode_valu(a, batch, stream);
   return launch_decode_mfma(a, batch, stream);
 }

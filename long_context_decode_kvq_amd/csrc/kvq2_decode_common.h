@@ -33,6 +33,11 @@ struct DecodeArgs {
   const uint16_t* q;
   float* out;
   int32_t* tickets;            // [B * Hkv]
+  int32_t* work_counter;       // [2]: next work item, work-groups finished
+  int batch;
+  float* qrot;                 // [B][Hq][kQStride]: alpha R_K^T q, its sum, f16 exponent
+  uint32_t* bq;                // [B * Hkv][kBqWords]: QK MFMA operand and lane constants
+  int gp;                      // MFMA head-group width (2, 4 or 8)
   float* partials;             // [B][Hkv][n_split][G][kPartialStride]
   int n_split_int2;
   int n_split;
@@ -67,31 +72,30 @@ __device__ __forceinline__ void split_tiles(const DecodeArgs& a, const Int2Range
   t_end = min(n, (s + 1) * per);
 }
 
-// q'[g][i] = alpha * sum_j R_K[h][j][i] q[b][hG+g][j] into LDS, plus
-// qsum[g] = sum_i q'[g][i].  All 256 threads take part; ends with a barrier.
+// QK k-slot -> channel map of the MFMA decode kernel: k-slot i (pair q = i/2,
+// element e = i%2) of k-step kk for lane group gq holds channel
+// 32gq + 16(kk/2) + local, where the code was extracted at scale 2^(2s - 24)
+// (one AND per f16 pair, see the MFMA kernel).
+__device__ __forceinline__ void kslot_channel(int gq, int kk, int i, int& ch, int& s) {
+  const int q = i >> 1, e = i & 1;
+  const int local = (kk & 1) ? (4 + q + 8 * e) : (q + 8 * e);
+  ch = 32 * gq + 16 * (kk >> 1) + local;
+  s = (kk & 1) ? (q == 0 ? 4 : q) : q;
+}
+
+// The rotated queries of (b, h), computed once per call by the rotation
+// pre-pass, into LDS: q'[g][:] (alpha folded in), qsum[g] = sum_i q'[g][i]
+// and qexp[g] with 2^-qexp[g] max|q'[g]| < 1.  Ends with a barrier.
 template <int GP>
-__device__ void rotate_queries(const DecodeArgs& a, int b, int h, float (*qraw)[kHeadDim],
-                               float (*qs)[kHeadDim], float* qsum) {
+__device__ void load_queries(const DecodeArgs& a, int b, int h, float (*qs)[kHeadDim],
+                             float* qsum, int* qexp) {
   const int G = a.group;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    qraw[g][c] = bf16_bits_to_float(a.q[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c]);
-  }
-  __syncthreads();
-  const float* R = a.R_K + int64_t(h) * kHeadDim * kHeadDim;
-  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int j = 0; j < kHeadDim; ++j) acc = fmaf(R[j * kHeadDim + c], qraw[g][j], acc);
-    qs[g][c] = acc * a.alpha;
-  }
-  __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int g = wave; g < G; g += blockDim.x / 64) {
-    const float v = wave_sum(qs[g][lane] + qs[g][lane + 64]);
-    if (lane == 0) qsum[g] = v;
+  const float* src = a.qrot + (int64_t(b) * a.n_q_heads + int64_t(h) * G) * kQStride;
+  for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x)
+    qs[i / kHeadDim][i % kHeadDim] = src[(i / kHeadDim) * kQStride + i % kHeadDim];
+  if (threadIdx.x < G) {
+    qsum[threadIdx.x] = src[threadIdx.x * kQStride + kHeadDim];
+    qexp[threadIdx.x] = static_cast<int>(src[threadIdx.x * kQStride + kHeadDim + 1]);
   }
   __syncthreads();
 }

@@ -22,10 +22,11 @@
 // output gives lane (gq, n) tokens 4gq..4gq+3 of column n, which is exactly
 // the PV A-operand layout (row n, tokens 4gq..4gq+3), so the softmax weights
 // never leave their lanes.  With GP query heads per KV head (padded to a
-// power of two <= 8), columns are (chunk p, hi/lo t, head g) with
+// power of two in 2..8), columns are (chunk p, hi/lo t, head g) with
 // n = 2GP*p + GP*t + g: one QK tile covers 16 / (2GP) chunks.  The running
 // max is updated lazily: a tile is rescaled only when a logit exceeds the
 // running max by more than 8 (base-2 units), so p <= 256.
+#include <algorithm>
 #include <type_traits>
 
 #include "kvq2_decode_common.h"
@@ -70,43 +71,102 @@ __device__ __forceinline__ void k_operands(uint32_t w, half8_t& even, half8_t& o
   odd = __builtin_bit_cast(half8_t, o);
 }
 
-// Channel and scale exponent of k-slot i (pair q = i/2, element e = i%2) of
-// QK k-step kk for lane group gq: channel = 32gq + 16(kk/2) + local, value
-// scale 2^(2s - 24).
-__device__ __forceinline__ void kslot_channel(int gq, int kk, int i, int& ch, int& s) {
-  const int q = i >> 1, e = i & 1;
-  const int local = (kk & 1) ? (4 + q + 8 * e) : (q + 8 * e);
-  ch = 32 * gq + 16 * (kk >> 1) + local;
-  s = (kk & 1) ? (q == 0 ? 4 : q) : q;
+// Tile geometry: 16 / (2 GP) chunks per tile.  In LDS a tile is stored as
+// [codes of chunk 0..NPT-1 (1024 B each)][scale/zero params (128 B each)];
+// at least 256 B of params space so one 64-lane dword DMA always fits.
+template <int GP>
+struct Geo {
+  static constexpr int NPT = 16 / (2 * GP);
+  static constexpr int PARAM_BYTES = NPT >= 2 ? NPT * 128 : 256;
+  static constexpr int TILE = NPT * 1024 + PARAM_BYTES;
+  static constexpr int RING = NPT >= 4 ? 2 : (NPT == 2 ? 3 : 6);   // tiles per wave ring
+};
+
+// One LDS array per ring position (all waves' slots for that position), so
+// that the wait before reading a slot covers only that slot's DMA loads.
+template <int GP, int K>
+__device__ __forceinline__ uint8_t* ring_slot(int wave) {
+  __shared__ __attribute__((aligned(16))) uint8_t slot[4][Geo<GP>::TILE];
+  return slot[wave];
 }
 
 template <int GP>
-struct Tile {
-  static constexpr int NPT = 16 / (2 * GP);
-  uint2 kc[NPT];
-  uint2 vc[NPT];
-  uint4 kp;       // K (scale, zero) of tokens 4gq..4gq+3 of this lane's chunk
-  uint4 vp;       // V (scale, zero)
-  int64_t off[NPT];   // chunk byte offsets; -1 = masked chunk (loads read chunk 0)
-};
+__device__ __forceinline__ uint8_t* ring_slot_k(int k, int wave) {
+  // k is a compile-time constant after unrolling
+  if (k == 0) return ring_slot<GP, 0>(wave);
+  if (k == 1) return ring_slot<GP, 1>(wave);
+  if (k == 2) return ring_slot<GP, 2>(wave);
+  if (k == 3) return ring_slot<GP, 3>(wave);
+  if (k == 4) return ring_slot<GP, 4>(wave);
+  return ring_slot<GP, 5>(wave);
+}
 
+// Direct HBM -> LDS loads and the LDS reads of a tile are written in
+// assembly so that the compiler does not serialise them: it cannot tell the
+// ring slots apart and would otherwise wait for every outstanding DMA before
+// any LDS read.  The kernel waits explicitly (vmcnt) for the one tile it
+// reads; no other vector-memory instruction is issued inside the tile loop.
+// M0 holds the LDS destination; lane i writes size bytes at M0 + size * i.
+
+// 16 bytes per lane from sbase + voff.
+__device__ __forceinline__ void dma_x4(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory", "m0");
+}
+
+// 4 bytes per lane from a per-lane address.
+__device__ __forceinline__ void dma_x1(const uint8_t* vaddr, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(vaddr), "s"(lds)
+      : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// One work item: INT2 split s < n_split_int2 of (b, h), or (s == n_split_int2)
+// the token-by-token part of (b, h).  Leaves its partial in the workspace;
+// the last item of (b, h) to finish combines them and writes `out`.
 template <int GP>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NPT = Tile<GP>::NPT;   // 16-token chunks per tile
-  __shared__ float qraw[GP][kHeadDim];
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, const int h,
+                                            const int s) {
+  constexpr int NPT = Geo<GP>::NPT;    // 16-token chunks per tile
+  constexpr int RING = Geo<GP>::RING;
+  constexpr int TILE = Geo<GP>::TILE;
   __shared__ float qs[GP][kHeadDim];
   __shared__ float qsum[GP];
+  __shared__ int qexp[GP];
   __shared__ float pbuf[4][16][GP];
   __shared__ float wm[4][GP], wl[4][GP];
-  __shared__ float wo[4][GP][kHeadDim];
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Per-wave o' staging of the epilogue; it reuses ring position 0 when that
+  // is large enough (the ring is idle by then).
+  constexpr bool kWoInRing = 4 * TILE >= int(4 * GP * kHeadDim * sizeof(float));
+  __shared__ float wo_own[kWoInRing ? 1 : 4][kWoInRing ? 1 : GP][kHeadDim];
+  float (*wo)[GP][kHeadDim] =
+      kWoInRing ? reinterpret_cast<float (*)[GP][kHeadDim]>(ring_slot<GP, 0>(0))
+                : reinterpret_cast<float (*)[GP][kHeadDim]>(&wo_own[0][0][0]);
   const int G = a.group;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  // The lane id passes through an empty asm statement so that the per-lane
+  // constants derived from it are recomputed per item rather than hoisted out
+  // of the persistent item loop (which would keep them live throughout).
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int gq = lane >> 4, n = lane & 15;
   const int L = a.seq_len[b];
 
-  rotate_queries<GP>(a, b, h, qraw, qs, qsum);
+  load_queries<GP>(a, b, h, qs, qsum, qexp);
 
   const Int2Range rg = int2_range(a, L, NPT);
   if (s == a.n_split_int2) {
@@ -123,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();
-    finish_work_group<GP>(a, b, h, s, wm, wl, wo, qraw);
+    finish_work_group<GP>(a, b, h, s, wm, wl, wo, qs);
     return;
   }
 
@@ -134,30 +194,19 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   const int g_col = j % GP;          // query head of this column
   const bool g_ok = g_col < G;
 
-  // Per-head normalisation 2^-e of q' (max |q'| <= 1 after scaling).
-  float qscale, qbar;
+  // QK operand (q' hi/lo in f16, per-lane layout) and this column's logit
+  // scale, both prepared by the rotation pre-pass.
   half8_t Bq[4];
+  float qscale, qbar_s;
   {
-    float mx = 0.f;
-    if (g_ok) {
-      for (int c = 0; c < kHeadDim; ++c) mx = fmaxf(mx, fabsf(qs[g_col][c]));
-    }
-    const int e = mx > 0.f ? ilogbf(mx) + 1 : 0;
-    const float down = ldexpf(1.0f, -e);
-    qscale = ldexpf(1.0f, 16 + e);
-    qbar = g_ok ? qsum[g_col] : 0.f;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords + lane * 16);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int ch, sc;
-        kslot_channel(gq, kk, i, ch, sc);
-        const float v = g_ok ? qs[g_col][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
-        const _Float16 hi = static_cast<_Float16>(v);
-        const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
-        Bq[kk][i] = is_hi ? hi : lo;
-      }
-    }
+    for (int kk = 0; kk < 4; ++kk) Bq[kk] = __builtin_bit_cast(half8_t, src[kk]);
+    const float2 lq = reinterpret_cast<const float2*>(
+        a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords + 64 * 16)[lane];
+    qscale = lq.x;
+    qbar_s = lq.y;
   }
 
   int t_begin, t_end;
@@ -180,18 +229,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   float m_eff = g_ok ? -INFINITY : INFINITY;
   float thr = g_ok ? -INFINITY : INFINITY;
   float l_lane = 0.f, z_lane = 0.f;
-  const float qbar_s = qbar / qscale;
 
   const uint8_t* pool = a.pool;
-  // Chunk byte offsets of a tile (wave-uniform, scalar arithmetic).  Every
-  // chunk of a tile in the split's range is fully valid; tiles past the range
-  // (prefetch overrun) and invalid page entries read chunk 0 (memory-safe;
-  // the former are never computed, the latter are a caller error).
+  // Chunk byte offsets (wave-uniform, scalar arithmetic).  Every chunk of a
+  // tile in the split's range is fully valid; tiles past the range (prefetch
+  // overrun) and invalid page entries read chunk 0 (memory-safe; the former
+  // are never computed, the latter are a caller error).
   typedef const int32_t __attribute__((address_space(4))) const_i32;
   const_i32* bt_row = (const_i32*)(a.block_table + int64_t(b) * a.bt_stride);
   const int cpp_mask = (1 << a.log2_cpp) - 1;
   const int64_t head_off = int64_t(h) * (cpp_mask + 1) * kChunkBytes;
-  // Page numbers of a tile's chunks (-1 outside the split or the table).
   struct Pages { int32_t pg[NPT]; };
   auto fetch_pages = [&](int tile, Pages& P) {
 #pragma unroll
@@ -200,40 +247,86 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       P.pg[p] = (tile < n_tiles && lp < a.bt_stride) ? bt_row[lp] : -1;
     }
   };
-  auto tile_offsets = [&](int tile, const Pages& P, Tile<GP>& t) {
+  // DMA one tile from HBM into an LDS slot: NPT 64-lane x 16 B loads of the
+  // code bytes, then 64-lane dword loads of the params of two chunks each.
+  auto issue_tile = [&](int tile, const Pages& P, uint8_t* slot) {
+    int64_t off[NPT];
 #pragma unroll
     for (int p = 0; p < NPT; ++p) {
       const int c = c_begin + tile * NPT + p;
       const int32_t page = P.pg[p];
-      t.off[p] = (page >= 0 && page < a.num_pages)
-                     ? int64_t(page) * a.page_bytes + head_off + int64_t(c & cpp_mask) * kChunkBytes
-                     : int64_t(0);
+      off[p] = (page >= 0 && page < a.num_pages)
+                   ? int64_t(page) * a.page_bytes + head_off + int64_t(c & cpp_mask) * kChunkBytes
+                   : int64_t(0);
+    }
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot));
+#pragma unroll
+    for (int p = 0; p < NPT; ++p) dma_x4(pool + off[p], 16u * lane, lds + 1024u * p);
+#pragma unroll
+    for (int i = 0; i < (NPT + 1) / 2; ++i) {
+      const int p0 = 2 * i, p1 = NPT > 1 ? 2 * i + 1 : 0;
+      const int64_t o = (lane >> 5) ? off[p1] : off[p0];
+      dma_x1(pool + o + kKParamsOff + 4 * (lane & 31), lds + 1024u * NPT + 256u * i);
     }
   };
-  auto load_tile = [&](Tile<GP>& t) {
-#pragma unroll
-    for (int p = 0; p < NPT; ++p) {
-      const uint8_t* ch = pool + t.off[p];
-      t.kc[p] = *reinterpret_cast<const uint2*>(ch + kKCodesOff + 32 * n + 8 * gq);
-      t.vc[p] = *reinterpret_cast<const uint2*>(ch + kVCodesOff + 32 * n + 8 * gq);
+  constexpr int kDmaPerTile = NPT + (NPT + 1) / 2;
+  // One tile from its LDS slot: QK on the matrix cores, lazy online softmax
+  // on the hi lanes, PV on the matrix cores.
+  auto compute_tile = [&](const uint8_t* slot) {
+    // this tile's DMA is complete once at most (RING-1) tiles of DMA remain
+    wait_vmcnt<(RING - 1) * kDmaPerTile>();
+    uint2 kc[NPT], vc[NPT];
+    uint4 kp, vp;
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot));
+    const uint32_t acode = lds + 32u * n + 8u * gq;
+    const uint32_t aprm = lds + 1024u * NPT + 128u * pblk + 16u * gq;
+    if constexpr (NPT == 1) {
+      asm volatile(
+          "ds_read_b64 %0, %4\n\t"
+          "ds_read_b64 %1, %4 offset:512\n\t"
+          "ds_read_b128 %2, %5\n\t"
+          "ds_read_b128 %3, %5 offset:64\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(kc[0]), "=v"(vc[0]), "=v"(kp), "=v"(vp)
+          : "v"(acode), "v"(aprm)
+          : "memory");
+    } else if constexpr (NPT == 2) {
+      asm volatile(
+          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %1, %6 offset:512\n\t"
+          "ds_read_b64 %2, %6 offset:1024\n\t"
+          "ds_read_b64 %3, %6 offset:1536\n\t"
+          "ds_read_b128 %4, %7\n\t"
+          "ds_read_b128 %5, %7 offset:64\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(kc[0]), "=v"(vc[0]), "=v"(kc[1]), "=v"(vc[1]), "=v"(kp), "=v"(vp)
+          : "v"(acode), "v"(aprm)
+          : "memory");
+    } else {
+      static_assert(NPT == 4, "tile geometry");
+      asm volatile(
+          "ds_read_b64 %0, %10\n\t"
+          "ds_read_b64 %1, %10 offset:512\n\t"
+          "ds_read_b64 %2, %10 offset:1024\n\t"
+          "ds_read_b64 %3, %10 offset:1536\n\t"
+          "ds_read_b64 %4, %10 offset:2048\n\t"
+          "ds_read_b64 %5, %10 offset:2560\n\t"
+          "ds_read_b64 %6, %10 offset:3072\n\t"
+          "ds_read_b64 %7, %10 offset:3584\n\t"
+          "ds_read_b128 %8, %11\n\t"
+          "ds_read_b128 %9, %11 offset:64\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(kc[0]), "=v"(vc[0]), "=v"(kc[1]), "=v"(vc[1]), "=v"(kc[2]), "=v"(vc[2]),
+            "=v"(kc[3]), "=v"(vc[3]), "=v"(kp), "=v"(vp)
+          : "v"(acode), "v"(aprm)
+          : "memory");
     }
-    int64_t mine = t.off[0];
-#pragma unroll
-    for (int p = 1; p < NPT; ++p) mine = (pblk == p) ? t.off[p] : mine;
-    const uint8_t* ch = pool + mine;
-    t.kp = *reinterpret_cast<const uint4*>(ch + kKParamsOff + 16 * gq);
-    t.vp = *reinterpret_cast<const uint4*>(ch + kVParamsOff + 16 * gq);
-  };
-
-  // One tile: QK on the matrix cores, lazy online softmax on the hi lanes,
-  // PV on the matrix cores.
-  auto compute_tile = [&](const Tile<GP>& t) {
     float4_t cq[NPT];
 #pragma unroll
     for (int p = 0; p < NPT; ++p) {
       half8_t a0, a1, a2, a3;
-      k_operands(t.kc[p].x, a0, a1);
-      k_operands(t.kc[p].y, a2, a3);
+      k_operands(kc[p].x, a0, a1);
+      k_operands(kc[p].y, a2, a3);
       float4_t c = {0.f, 0.f, 0.f, 0.f};
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[0], c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[1], c, 0, 0, 0);
@@ -250,8 +343,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float d = c4[r] + dpp_f<0x100 + GP>(c4[r]);          // hi + lo columns
-      const uint32_t kpr = r == 0 ? t.kp.x : r == 1 ? t.kp.y : r == 2 ? t.kp.z : t.kp.w;
-      const uint32_t vpr = r == 0 ? t.vp.x : r == 1 ? t.vp.y : r == 2 ? t.vp.z : t.vp.w;
+      const uint32_t kpr = r == 0 ? kp.x : r == 1 ? kp.y : r == 2 ? kp.z : kp.w;
+      const uint32_t vpr = r == 0 ? vp.x : r == 1 ? vp.y : r == 2 ? vp.z : vp.w;
       lg[r] = fmaf(f16lo(kpr), d, f16hi(kpr) * qbar_s);          // lg' = s_K d + z_K sum(q')/qscale
       svb[r] = vpr;
       zv[r] = f16hi(vpr);
@@ -260,14 +353,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     float tmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     if (__any(is_hi && g_ok && tmax > thr)) {
       const float tm = (is_hi && g_ok) ? tmax * qscale : -INFINITY;
-      float corr[GP], m_new[GP];
+      float corr[GP];
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
         const float mg = wave_max(g_col == g ? tm : -INFINITY);
         const float mo = m_h[g];
-        m_new[g] = fmaxf(mo, mg);
-        corr[g] = (m_new[g] == -INFINITY) ? 1.f : exp2f(mo - m_new[g]);
-        m_h[g] = m_new[g];
+        const float mn = fmaxf(mo, mg);
+        corr[g] = (mn == -INFINITY) ? 1.f : exp2f(mo - mn);
+        m_h[g] = mn;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -309,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     for (int p = 0; p < NPT; ++p) {
       const u32x2_t ap = {pblk == p ? av0 : 0u, pblk == p ? av1 : 0u};
       const half4_t A = __builtin_bit_cast(half4_t, ap);
-      const uint32_t d0 = t.vc[p].x, d1 = t.vc[p].y;
+      const uint32_t d0 = vc[p].x, d1 = vc[p].y;
       const uint32_t d0s = d0 >> 8, d1s = d1 >> 8;
 #pragma unroll
       for (int J = 0; J < 8; ++J) {
@@ -322,36 +415,32 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- tile loop: a ring of kRing tile buffers, loads kRing-1 tiles ahead --
-  // Every step issues its prefetch unconditionally (tiles past the end read
-  // chunk 0 and are never computed), so the number of loads in flight is the
-  // same on every path and each tile waits only for its own loads.
-  constexpr int kRing = 3;
+  // ---- tile loop: a ring of RING LDS tile slots per wave, DMA RING-1 tiles
+  // ahead.  Every step issues its DMA unconditionally (tiles past the end
+  // read chunk 0 and are never computed), so the number of loads in flight
+  // is the same on every path; page lookups run one step ahead of the DMA.
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;     // tiles wave, wave+4, ...
   if (my_tiles > 0) {
-    // Page lookups run one step ahead of the loads that need them, and the
-    // loads kRing-1 tiles ahead of the tile being computed.
-    Tile<GP> buf[kRing];
     Pages pn;
 #pragma unroll
-    for (int k = 0; k < kRing - 1; ++k) {
+    for (int k = 0; k < RING - 1; ++k) {
       fetch_pages(wave + 4 * k, pn);
-      tile_offsets(wave + 4 * k, pn, buf[k]);
-      load_tile(buf[k]);
+      issue_tile(wave + 4 * k, pn, ring_slot_k<GP>(k, wave));
     }
-    fetch_pages(wave + 4 * (kRing - 1), pn);
-    for (int k0 = 0; k0 < my_tiles; k0 += kRing) {
+    fetch_pages(wave + 4 * (RING - 1), pn);
+    for (int k0 = 0; k0 < my_tiles; k0 += RING) {
 #pragma unroll
-      for (int k = 0; k < kRing; ++k) {
-        const int kn = (k + kRing - 1) % kRing;
-        const int ahead = wave + 4 * (k0 + k + kRing - 1);
-        tile_offsets(ahead, pn, buf[kn]);
-        load_tile(buf[kn]);
+      for (int k = 0; k < RING; ++k) {
+        const int kn = (k + RING - 1) % RING;
+        const int ahead = wave + 4 * (k0 + k + RING - 1);
+        issue_tile(ahead, pn, ring_slot_k<GP>(kn, wave));
         fetch_pages(ahead + 4, pn);
-        if (k0 + k < my_tiles) compute_tile(buf[k]);
+        if (k0 + k < my_tiles) compute_tile(ring_slot_k<GP>(k, wave));
       }
     }
+    wait_vmcnt<0>();     // drain DMA before the ring memory is reused
   }
+  __syncthreads();
 
   // ---- wave epilogue: per-head l, z and o' into LDS -----------------------
   float l_h[GP], z_h[GP];
@@ -391,7 +480,44 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       if (g < G) { wm[wave][g] = m_h[g] - log2_sigma; wl[wave][g] = l_h[g]; }
   }
   __syncthreads();
-  finish_work_group<GP>(a, b, h, s, wm, wl, wo, qraw);
+  finish_work_group<GP>(a, b, h, s, wm, wl, wo, qs);
+}
+
+// Persistent decode: as many work-groups as the GPU holds at once; each
+// takes items from a device counter (INT2 splits first, the short
+// token-by-token items last, so they fill the tail).  The last work-group to
+// leave resets the counters for the next call on this workspace.
+// Occupancy target: four work-groups (16 waves) per CU for GP <= 4.
+template <int GP>
+__global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ int item_sh;
+  const int pairs = a.batch * a.n_kv_heads;
+  const int n_int2_items = pairs * a.n_split_int2;
+  const int n_items = n_int2_items + pairs;
+  for (;;) {
+    __syncthreads();   // the previous item is done with every LDS buffer
+    if (threadIdx.x == 0) item_sh = atomicAdd(a.work_counter, 1);
+    __syncthreads();
+    const int item = item_sh;
+    if (item >= n_items) break;
+    int pair, s;
+    if (item < n_int2_items) {
+      pair = item / a.n_split_int2;
+      s = item - pair * a.n_split_int2;
+    } else {
+      pair = item - n_int2_items;
+      s = a.n_split_int2;
+    }
+    decode_item<GP>(a, pair / a.n_kv_heads, pair % a.n_kv_heads, s);
+  }
+  if (threadIdx.x == 0) {
+    __threadfence();
+    if (atomicAdd(a.work_counter + 1, 1) == int(gridDim.x) - 1) {
+      __threadfence();
+      a.work_counter[0] = 0;
+      a.work_counter[1] = 0;
+    }
+  }
 }
 
 }  // namespace
@@ -400,16 +526,47 @@ int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
 
 // Group sizes up to 8 run on the matrix cores; 9..16 query heads per KV head
 // (two MFMA row blocks of hi/lo would not fit 16 rows) use the VALU kernel.
+namespace {
+
+// Work-groups of `kernel` the current device holds at once (cached per
+// device and kernel).
+template <int GP>
+int resident_work_groups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<GP>, 256, 0) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+      cus = 256;
+      per_cu = 1;
+    }
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
+}
+
+template <int GP>
+int launch_persistent(const DecodeArgs& a, int batch, hipStream_t st) {
+  const int items = batch * a.n_kv_heads * (a.n_split_int2 + 1);
+  const int grid = std::max(1, std::min(items, resident_work_groups<GP>()));
+  hipLaunchKernelGGL(decode_mfma_kernel<GP>, dim3(grid), dim3(256), 0, st, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
 int launch_decode_mfma(const DecodeArgs& a, int batch, void* stream) {
   const int G = a.group;
   if (G > 8) return launch_decode_valu(a, batch, stream);
-  dim3 grid(a.n_split, a.n_kv_heads, batch);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (G <= 1) hipLaunchKernelGGL(decode_mfma_kernel<1>, grid, dim3(256), 0, st, a);
-  else if (G <= 2) hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(256), 0, st, a);
-  else if (G <= 4) hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(decode_mfma_kernel<8>, grid, dim3(256), 0, st, a);
-  return static_cast<int>(hipGetLastError());
+  // G = 1 runs the two-head kernel with one padding head.
+  if (G <= 2) return launch_persistent<2>(a, batch, st);
+  if (G <= 4) return launch_persistent<4>(a, batch, st);
+  return launch_persistent<8>(a, batch, st);
 }
 
 }  // namespace kvq

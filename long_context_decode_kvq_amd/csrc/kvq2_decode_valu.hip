@@ -19,9 +19,9 @@ namespace {
 
 template <int GP>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
-  __shared__ float qraw[GP][kHeadDim];
   __shared__ float qs[GP][kHeadDim];
   __shared__ float qsum[GP];
+  __shared__ int qexp[GP];
   __shared__ float wbuf[4][16][GP];          // p * s_V of each token of the wave's chunk
   __shared__ float pbuf[4][16][GP];          // p of each bf16 token
   __shared__ float wm[4][GP], wl[4][GP];
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int L = a.seq_len[b];
 
-  rotate_queries<GP>(a, b, h, qraw, qs, qsum);
+  load_queries<GP>(a, b, h, qs, qsum, qexp);
 
   float m[GP], l[GP], zacc[GP], acc0[GP], acc1[GP];
 #pragma unroll
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  finish_work_group<GP>(a, b, h, s, wm, wl, wo, qraw);
+  finish_work_group<GP>(a, b, h, s, wm, wl, wo, qs);
 }
 
 }  // namespace

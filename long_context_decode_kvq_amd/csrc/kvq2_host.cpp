@@ -77,11 +77,11 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   const int64_t last_chunk = (int2_end + kChunkTokens - 1) / kChunkTokens;   // exclusive
   const int64_t n_chunks = int2_end > d.n_sink ? last_chunk - first_chunk : 0;
   const int64_t heads = int64_t(batch) * d.n_kv_heads;
-  // About 1536 INT2 work-groups (two rounds of three per CU on 256 CUs), but
-  // no split shorter than 64 chunks (1024 tokens): the prologue (query
-  // rotation) and the split combine are paid per work-group.
-  int64_t ns = (1536 + heads - 1) / std::max<int64_t>(heads, 1);
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, n_chunks / 64));
+  // About two work items per resident work-group of the persistent decode
+  // (2048 = 256 CUs x 4 x 2), but no split shorter than 256 chunks (4096
+  // tokens): the item prologue and the split combine are paid per item.
+  int64_t ns = (2048 + heads - 1) / std::max<int64_t>(heads, 1);
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, n_chunks / 256));
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, 512));
   const int forced = env_int("KVQ_NSPLIT", 0);
   if (forced > 0) ns = std::min(forced, 4096);
@@ -89,9 +89,12 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   p.n_split_int2 = static_cast<int>(ns);
   p.n_split = p.n_split_int2 + 1;
   const int G = d.n_q_heads / d.n_kv_heads;
-  p.ticket_bytes = ((size_t(heads) * sizeof(int32_t) + 255) / 256) * 256;
+  // arrival tickets [B * Hkv] + the persistent kernel's two work counters
+  p.ticket_bytes = ((size_t(heads + 2) * sizeof(int32_t) + 255) / 256) * 256;
+  p.qrot_bytes = size_t(batch) * d.n_q_heads * kQStride * sizeof(float);
+  p.bq_bytes = size_t(heads) * kBqWords * sizeof(uint32_t);
   p.partial_bytes = size_t(heads) * p.n_split * G * kPartialStride * sizeof(float);
-  p.total_bytes = p.ticket_bytes + p.partial_bytes;
+  p.total_bytes = p.ticket_bytes + p.qrot_bytes + p.bq_bytes + p.partial_bytes;
   return p;
 }
 

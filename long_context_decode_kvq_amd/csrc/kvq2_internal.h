@@ -20,12 +20,17 @@ constexpr int kMaxGroup = 16;          // query heads per KV head supported
 constexpr float kMaxClip = 16384.0f;   // keeps 2c/3 and c inside fp16 range
 constexpr int kPartialStride = 132;    // floats per (split, query head) partial:
                                        // m, l, 2 pad, o'[128]
+constexpr int kQStride = 132;          // floats per rotated query: q'[128], sum(q'),
+                                       // f16 scaling exponent, 2 pad
+constexpr int kBqWords = 64 * 16 + 64 * 2;   // u32 words per (b, h) of the QK operand block
 
 // Resolved decode geometry shared by the workspace query and the launch.
 struct DecodePlan {
   int n_split_int2;   // work-groups per (sequence, KV head) over INT2 chunks
   int n_split;        // n_split_int2 + 1 (the last one takes the bf16 segments)
   size_t ticket_bytes;
+  size_t qrot_bytes;    // rotated queries [B][Hq][kQStride] fp32
+  size_t bq_bytes;      // QK MFMA operand per (b, h): [64 lanes][16 dwords] + [64][2] fp32
   size_t partial_bytes;
   size_t total_bytes;
 };
