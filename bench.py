@@ -111,12 +111,57 @@ def build_cache(w, kvq2, W, lens_before, n_steps, device):
     return kd, dc, lay, (dR_K, dR_V, R_K, R_V, clip_K, clip_V)
 
 
-def cpu_baseline(w, W, seconds_budget=30.0):
-    """The CPU oracle on a bounded sample of the workload: one (sequence, KV
-    head) pair at the full context, one step (append one token + decode for
-    its query heads), single-threaded."""
-    import numpy as np
+# HBM traffic of the decode kernel from rocprofv3 counters (see profiles/):
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the bench command, each
+# scaled by bytes / counter measured on a plain device copy of known size
+# (`bench.py --copy-probe`).  The counters are tied to a hash of the kernel
+# sources; after any source change the figure is stale and reported as null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_conc_28x100k_traffic.txt")
+KERNEL_SOURCES = ("kvq2_decode.hip", "kvq2_decode_mfma.hip", "kvq2_decode_common.h",
+                  "kvq2_device.h", "kvq2_internal.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_decode_kvq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(l.split(":", 1) for l in fh.read().splitlines() if ":" in l and not l.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("workload") != workload or kv.get("source_hash") != kernel_source_hash():
+            return None
+        fetch = float(kv["decode_fetch_kib"]) * 1024 * float(kv["copy_fetch_bytes_per_kib"]) / 1024
+        write = float(kv["decode_write_kib"]) * 1024 * float(kv["copy_write_bytes_per_kib"]) / 1024
+        return fetch + write
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(n_bytes=1 << 30, reps=5):
+    """A plain device copy of known size, to calibrate FETCH_SIZE / WRITE_SIZE."""
     import torch
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[copy-probe] {reps} copies of {n_bytes} bytes")
+
+
+def cpu_baseline(w, W, seconds_budget=10.0, max_steps=100):
+    """The CPU oracle on a bounded sample of the workload: one (sequence, KV
+    head) pair at the full context, decode steps (append one token + decode
+    its query heads) repeated until about `seconds_budget` of timed work,
+    single-threaded.  The oracle's bulk build of the pair's cache is untimed."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as O
@@ -126,37 +171,35 @@ def cpu_baseline(w, W, seconds_budget=30.0):
         q_c, k_c, v_c = W.calibration_tokens(w, 256)
         cal = O.calibrate(q_c[:, :w.group], k_c[:, :1], v_c[:, :1], w.group, 1,
                           1 / math.sqrt(HEAD_DIM), 0.999)
-        k, v = W.sequence_kv_device(w, 0, 0, L + 2, "cuda")
+        k, v = W.sequence_kv_device(w, 0, 0, L + max_steps, "cuda")
         k = k[:, :1].cpu().numpy().view(np.uint16)
         v = v[:, :1].cpu().numpy().view(np.uint16)
         od = O.Dims(w.group, 1, w.page_size, w.n_sink, w.n_recent)
-        reps = 3
-        k, v = k[:L + reps - 1], v[:L + reps - 1]
-        npg = math.ceil((L + reps) / w.page_size)
+        npg = math.ceil((L + max_steps) / w.page_size)
         oc = O.OracleCache(od, 1, npg, np.arange(npg, dtype=np.int32)[None])
         t0 = time.perf_counter()
         oc.append(cal.R_K, cal.R_V, cal.clip_K, cal.clip_V, 0, 0, k[:L - 1], v[:L - 1])
         build_s = time.perf_counter() - t0
         q = W.decode_queries_device(w, 0, "cuda")[:1, :w.group].cpu().numpy().view(np.uint16)
-        times = []
-        for r in range(reps):
+        timed, steps, nbytes = 0.0, 0, 0
+        while steps < max_steps and timed < seconds_budget:
             t0 = time.perf_counter()
-            p = L - 1 + r
+            p = L - 1 + steps
             oc.append(cal.R_K, cal.R_V, cal.clip_K, cal.clip_V, 0, p, k[p:p + 1], v[p:p + 1])
             oc.decode(cal.R_K, cal.R_V, [p + 1], q)
-            times.append(time.perf_counter() - t0)
-        step_s = float(np.median(times))
-    _, n_i, _ = segment_counts(L, w.n_sink, w.n_recent)
-    sample_bytes = (INT2_BYTES * n_i + BF16_BYTES * (L - n_i) + w.group * HEAD_DIM * 6
-                    + 2 * HEAD_DIM * HEAD_DIM * 4)
+            timed += time.perf_counter() - t0
+            _, n_i, _ = segment_counts(p + 1, w.n_sink, w.n_recent)
+            nbytes += (INT2_BYTES * n_i + BF16_BYTES * (p + 1 - n_i) + w.group * HEAD_DIM * 6
+                       + 2 * HEAD_DIM * HEAD_DIM * 4)
+            steps += 1
     return {
-        "value": sample_bytes / step_s / 1e9,
+        "value": nbytes / timed / 1e9,
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"one (sequence, KV head) of the workload at context {L}: append 1 token + "
-                   f"decode {w.group} query heads, NumPy fp64 oracle, 1 thread; median of {reps} "
-                   f"steps {step_s:.2f}s (cache build {build_s:.1f}s untimed)"),
+        "sample": (f"one (sequence, KV head) of the workload at context {L}: {steps} steps of "
+                   f"append 1 token + decode {w.group} query heads, NumPy fp64 oracle, 1 thread, "
+                   f"{timed:.1f}s timed (cache build {build_s:.1f}s untimed)"),
     }
 
 
@@ -167,7 +210,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="conc_28x100k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="print the decode kernel source hash and exit")
     args = ap.parse_args()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(one process, one MI355X). Run with --gpus 1.", file=sys.stderr)
@@ -175,6 +225,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     from long_context_decode_kvq_amd import kvq2
     from long_context_decode_kvq_amd import workloads as W
@@ -288,7 +342,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
         "cpu_baseline": cpu,
     }

@@ -314,16 +314,17 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
   __syncthreads();
   __shared__ int is_last;
   if (tid < 64) {
-    for (int i = tid; i < G * kPartialStride; i += 64) part[i] = stage[i];
-    __threadfence();   // release of this wave's stores, once per work-group
+    for (int i = tid; i < G * kPartialStride; i += 64) store_agent(part + i, stage[i]);
+    wait_global_stores();   // the partial is complete before the ticket is taken
     if (tid == 0) {
-      const int prev = atomicAdd(&a.tickets[head], 1);
+      const int prev = fetch_add_agent(&a.tickets[head], 1);
       is_last = (prev == a.n_split - 1);
     }
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();   // acquire: see every other work-group's partials
+  // Every other partial of (b, h) is complete; they are read with
+  // device-coherent loads below.
 
   // Split weights f_i = 2^(m_i - M) / sum_k 2^(m_k - M) l_k, staged in LDS
   // in slices of kCombineSlice splits so that all loads of a slice are in
@@ -339,7 +340,7 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
     const int ns = min(kCombineSlice, a.n_split - s0);
     for (int i = tid; i < ns * G; i += blockDim.x) {
       const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
-      s_m[i / G][i % G] = p[0];
+      s_m[i / G][i % G] = load_agent(p);
     }
     __syncthreads();
     for (int g = wave; g < G; g += 4) {
@@ -359,9 +360,9 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
     for (int i = tid; i < ns * G; i += blockDim.x) {
       const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
       const float M = s_M[i % G];
-      const float f = M == -INFINITY ? 0.f : exp2f(p[0] - M);
+      const float f = M == -INFINITY ? 0.f : exp2f(load_agent(p) - M);
       s_m[i / G][i % G] = f;
-      s_l[i / G][i % G] = f * p[1];
+      s_l[i / G][i % G] = f * load_agent(p + 1);
     }
     __syncthreads();
     for (int g = wave; g < G; g += 4) {
@@ -377,7 +378,8 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
         const int g = o / kHeadDim, c = o % kHeadDim;
         float v = 0.f;
 #pragma unroll 8
-        for (int i = 0; i < ns; ++i) v = fmaf(s_m[i][g], base[((s0 + i) * G + g) * kPartialStride + 4 + c], v);
+        for (int i = 0; i < ns; ++i)
+          v = fmaf(s_m[i][g], load_agent(base + ((s0 + i) * G + g) * kPartialStride + 4 + c), v);
         acc[k] += v;
       }
     }
@@ -408,7 +410,7 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
     }
     a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] = o;
   }
-  if (tid == 0) a.tickets[head] = 0;   // ready for the next call on this workspace
+  if (tid == 0) store_agent(&a.tickets[head], 0);   // ready for the next call on this workspace
 }
 
 }  // namespace kvq

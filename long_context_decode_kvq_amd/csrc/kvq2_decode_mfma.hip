@@ -207,6 +207,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords + 64 * 16)[lane];
     qscale = lq.x;
     qbar_s = lq.y;
+    // Pass the loaded values through empty asm statements: the compiler
+    // waits for the loads here, once, instead of inside the tile loop, where
+    // its vmcnt wait would also drain the in-flight tile DMA.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(Bq[kk]));
+    asm volatile("" : "+v"(qscale), "+v"(qbar_s));
   }
 
   int t_begin, t_end;
@@ -496,9 +502,9 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
   const int n_items = n_int2_items + pairs;
   for (;;) {
     __syncthreads();   // the previous item is done with every LDS buffer
-    if (threadIdx.x == 0) item_sh = atomicAdd(a.work_counter, 1);
+    if (threadIdx.x == 0) item_sh = fetch_add_agent(a.work_counter, 1);
     __syncthreads();
-    const int item = item_sh;
+    const int item = __builtin_amdgcn_readfirstlane(item_sh);
     if (item >= n_items) break;
     int pair, s;
     if (item < n_int2_items) {
@@ -511,11 +517,10 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
     decode_item<GP>(a, pair / a.n_kv_heads, pair % a.n_kv_heads, s);
   }
   if (threadIdx.x == 0) {
-    __threadfence();
-    if (atomicAdd(a.work_counter + 1, 1) == int(gridDim.x) - 1) {
-      __threadfence();
-      a.work_counter[0] = 0;
-      a.work_counter[1] = 0;
+    if (fetch_add_agent(a.work_counter + 1, 1) == int(gridDim.x) - 1) {
+      // every work-group has taken its final (out-of-range) item
+      store_agent(a.work_counter, 0);
+      store_agent(a.work_counter + 1, 0);
     }
   }
 }

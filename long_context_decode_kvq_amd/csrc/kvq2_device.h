@@ -45,6 +45,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Device-coherent global accesses for data handed between work-groups of one
+// launch (split partials, tickets, work counters).  The XCDs of the GPU have
+// separate L2 caches; a generic device-scope fence makes plain stores
+// visible by writing back (and, for acquire, invalidating) the issuing XCD's
+// L2, which is expensive when many work-groups do it.  Agent-scope atomic
+// loads and stores are coherent across the XCDs by themselves, so data
+// published only through them needs just completion ordering: the writer
+// waits for its stores (vmcnt) before it takes the arrival ticket.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int fetch_add_agent(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every global store issued so far by this wave has completed.
+__device__ __forceinline__ void wait_global_stores() {
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+}
+
 // Byte offset of the 1152-byte chunk holding position `pos` of sequence b,
 // KV head h; -1 if the block-table entry is outside [0, num_pages).
 __device__ __forceinline__ int64_t chunk_offset(const int32_t* block_table, int32_t bt_stride,
