@@ -43,6 +43,23 @@ def _run(cmd):
     return out
 
 
+# Every embedded GPU code object is kept below 256 KiB.  The only two
+# library builds that were followed by a GPU memory fault (reported before
+# any of their new kernels had been launched) were also the only ones with a
+# larger code object; the cause is not known, so the size is held below it.
+MAX_CODE_OBJECT_BYTES = 256 * 1024
+
+
+def _check_code_object_size(obj: str) -> None:
+    r = subprocess.run(["readelf", "-S", "-W", obj], stdout=subprocess.PIPE, text=True)
+    for line in r.stdout.splitlines():
+        if ".hip_fatbin" in line:
+            size = int(line.split("PROGBITS")[1].split()[2], 16)
+            if size >= MAX_CODE_OBJECT_BYTES:
+                raise RuntimeError(f"{os.path.basename(obj)}: GPU code object of {size} bytes "
+                                   f"(limit {MAX_CODE_OBJECT_BYTES}); split the translation unit")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     hip, cpp = _sources()
@@ -60,6 +77,8 @@ def build(verbose: bool = False) -> str:
             if o.strip():
                 print(o)
     objs = [os.path.join(OBJ, f + ".o") for f in hip + cpp]
+    for f in hip:
+        _check_code_object_size(os.path.join(OBJ, f + ".o"))
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs, "-pthread"])
     os.replace(tmp, LIB)

@@ -131,6 +131,8 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   const int G = a.group;
   a.gp = (which == kDecodeValu || G > 8) ? 0 : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
   a.n_split_int2 = plan.n_split_int2;
+  a.n_split_big = plan.n_split_big;
+  a.n_split_small = plan.n_split_small;
   a.n_split = plan.n_split;
   hipLaunchKernelGGL(rotate_q_kernel, dim3(d.n_kv_heads, batch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);

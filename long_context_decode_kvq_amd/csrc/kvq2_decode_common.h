@@ -39,7 +39,9 @@ struct DecodeArgs {
   uint32_t* bq;                // [B * Hkv][kBqWords]: QK MFMA operand and lane constants
   int gp;                      // MFMA head-group width (2, 4 or 8)
   float* partials;             // [B][Hkv][n_split][G][kPartialStride]
-  int n_split_int2;
+  int n_split_int2;            // INT2 splits per (b, h) = n_split_big + n_split_small
+  int n_split_big;             // splits over the first 3/4 of the tiles (scheduled first)
+  int n_split_small;           // splits over the last 1/4 (scheduled after every big one)
   int n_split;
 };
 
@@ -63,13 +65,23 @@ __device__ __forceinline__ Int2Range int2_range(const DecodeArgs& a, int L, int 
   return r;
 }
 
-// Tile range [t_begin, t_end) of INT2 split s.
+// Tile range [t_begin, t_end) of INT2 split s.  Splits s < n_split_big
+// share the first 3/4 of the n tiles evenly, the n_split_small others the
+// rest: the work queue hands out every big split before any small one, so
+// the launch ends on short items (with n_split_small = 0, one even split).
 __device__ __forceinline__ void split_tiles(const DecodeArgs& a, const Int2Range& r, int npt, int s,
                                             int& t_begin, int& t_end) {
   const int n = (r.cl - r.cf) / npt;
-  const int per = (n + a.n_split_int2 - 1) / a.n_split_int2;
-  t_begin = min(n, s * per);
-  t_end = min(n, (s + 1) * per);
+  const int nb = a.n_split_big, nsm = a.n_split_small;
+  const int n_big = nsm > 0 ? (3 * n) / 4 : n;   // tiles of the big splits
+  if (s < nb) {
+    t_begin = int(int64_t(n_big) * s / nb);
+    t_end = int(int64_t(n_big) * (s + 1) / nb);
+  } else {
+    const int j = s - nb;
+    t_begin = n_big + int(int64_t(n - n_big) * j / nsm);
+    t_end = n_big + int(int64_t(n - n_big) * (j + 1) / nsm);
+  }
 }
 
 // QK k-slot -> channel map of the MFMA decode kernel: k-slot i (pair q = i/2,

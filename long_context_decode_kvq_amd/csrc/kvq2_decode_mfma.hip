@@ -490,14 +490,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
 }
 
 // Persistent decode: as many work-groups as the GPU holds at once; each
-// takes items from a device counter (INT2 splits first, the short
-// token-by-token items last, so they fill the tail).  The last work-group to
+// takes items from a device counter: the big INT2 splits of every (b, h),
+// then the small ones, then the token-by-token items.  The last work-group to
 // leave resets the counters for the next call on this workspace.
 // Occupancy target: four work-groups (16 waves) per CU for GP <= 4.
 template <int GP>
 __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ int item_sh;
   const int pairs = a.batch * a.n_kv_heads;
+  const int n_big_items = pairs * a.n_split_big;
   const int n_int2_items = pairs * a.n_split_int2;
   const int n_items = n_int2_items + pairs;
   for (;;) {
@@ -507,9 +508,13 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
     const int item = __builtin_amdgcn_readfirstlane(item_sh);
     if (item >= n_items) break;
     int pair, s;
-    if (item < n_int2_items) {
-      pair = item / a.n_split_int2;
-      s = item - pair * a.n_split_int2;
+    if (item < n_big_items) {
+      pair = item / a.n_split_big;
+      s = item - pair * a.n_split_big;
+    } else if (item < n_int2_items) {
+      const int i = item - n_big_items;
+      pair = i / a.n_split_small;
+      s = a.n_split_big + (i - pair * a.n_split_small);
     } else {
       pair = item - n_int2_items;
       s = a.n_split_int2;

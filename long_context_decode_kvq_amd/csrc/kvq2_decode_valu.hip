@@ -123,8 +123,8 @@ int launch_decode_valu(const DecodeArgs& a, int batch, void* stream) {
   dim3 grid(a.n_split, a.n_kv_heads, batch);
   const int G = a.group;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (G <= 1) hipLaunchKernelGGL(decode_valu_kernel<1>, grid, dim3(256), 0, st, a);
-  else if (G <= 2) hipLaunchKernelGGL(decode_valu_kernel<2>, grid, dim3(256), 0, st, a);
+  // G = 1 runs the two-head instantiation with one padding head.
+  if (G <= 2) hipLaunchKernelGGL(decode_valu_kernel<2>, grid, dim3(256), 0, st, a);
   else if (G <= 4) hipLaunchKernelGGL(decode_valu_kernel<4>, grid, dim3(256), 0, st, a);
   else if (G <= 8) hipLaunchKernelGGL(decode_valu_kernel<8>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(decode_valu_kernel<16>, grid, dim3(256), 0, st, a);

@@ -77,16 +77,23 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   const int64_t last_chunk = (int2_end + kChunkTokens - 1) / kChunkTokens;   // exclusive
   const int64_t n_chunks = int2_end > d.n_sink ? last_chunk - first_chunk : 0;
   const int64_t heads = int64_t(batch) * d.n_kv_heads;
-  // About two work items per resident work-group of the persistent decode
-  // (2048 = 256 CUs x 4 x 2), but no split shorter than 256 chunks (4096
-  // tokens): the item prologue and the split combine are paid per item.
-  int64_t ns = (2048 + heads - 1) / std::max<int64_t>(heads, 1);
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, n_chunks / 256));
-  ns = std::max<int64_t>(1, std::min<int64_t>(ns, 512));
-  const int forced = env_int("KVQ_NSPLIT", 0);
-  if (forced > 0) ns = std::min(forced, 4096);
-  if (n_chunks == 0) ns = 1;
-  p.n_split_int2 = static_cast<int>(ns);
+  // Even splits: about two work items per resident work-group of the
+  // persistent decode (2048 = 256 CUs x 4 x 2), but no split shorter than
+  // 256 chunks (4096 tokens): the item prologue and the combine are paid per
+  // item.  (Big-then-small splits, n_split_small > 0, are supported; with
+  // resident work-groups of different age on one CU they finish late, since
+  // the instruction arbiter favours the oldest waves.)
+  int64_t nb = (2048 + heads - 1) / std::max<int64_t>(heads, 1), nsm = 0;
+  nb = std::min<int64_t>(nb, std::max<int64_t>(1, n_chunks / 256));
+  nb = std::max<int64_t>(1, std::min<int64_t>(nb, 512));
+  const int forced = env_int("KVQ_NSPLIT", 0);          // even split override (tuning)
+  if (forced > 0) { nb = std::min(forced, 4096); nsm = 0; }
+  const int forced_small = env_int("KVQ_NSPLIT_SMALL", -1);
+  if (forced > 0 && forced_small > 0) nsm = std::min(forced_small, 4096);
+  if (n_chunks == 0) { nb = 1; nsm = 0; }
+  p.n_split_big = static_cast<int>(nb);
+  p.n_split_small = static_cast<int>(nsm);
+  p.n_split_int2 = p.n_split_big + p.n_split_small;
   p.n_split = p.n_split_int2 + 1;
   const int G = d.n_q_heads / d.n_kv_heads;
   // arrival tickets [B * Hkv] + the persistent kernel's two work counters

@@ -26,7 +26,9 @@ constexpr int kBqWords = 64 * 16 + 64 * 2;   // u32 words per (b, h) of the QK o
 
 // Resolved decode geometry shared by the workspace query and the launch.
 struct DecodePlan {
-  int n_split_int2;   // work-groups per (sequence, KV head) over INT2 chunks
+  int n_split_int2;   // work items per (sequence, KV head) over INT2 chunk tiles
+  int n_split_big;    //   of which cover the first 3/4 of the tiles (queued first)
+  int n_split_small;  //   and the last 1/4 (queued after all big ones)
   int n_split;        // n_split_int2 + 1 (the last one takes the bf16 segments)
   size_t ticket_bytes;
   size_t qrot_bytes;    // rotated queries [B][Hq][kQStride] fp32
