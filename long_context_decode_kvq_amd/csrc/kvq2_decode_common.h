@@ -139,15 +139,26 @@ __device__ __forceinline__ void softmax_tile16(int G, int qq, float* lg, float* 
   }
 }
 
-// Token-by-token path for the tokens outside the tiled INT2 chunks: the bf16
-// sink [0, min(L, n_sink)), the INT2 head tail [n_sink, min(16 cf, int2_end)),
-// the INT2 end tail [16 cl, int2_end) and the bf16 recent window
-// [max(n_sink, L - W), L); tiles of 16 tokens per wave, plain fp32.
+// Number of tokens of the token-by-token list of a sequence of length L: the
+// bf16 sink [0, min(L, n_sink)), the INT2 head tail [n_sink, min(16 cf,
+// int2_end)), the INT2 end tail [16 cl, int2_end) and the bf16 recent window
+// [max(n_sink, L - W), L), in that order.
+__device__ __forceinline__ int token_list_size(const DecodeArgs& a, int L, const Int2Range& rg) {
+  const int n_sk = min(L, a.n_sink);
+  const int n_hd = max(0, min(rg.cf * kChunkTokens, rg.int2_end) - a.n_sink);
+  const int n_en = max(0, rg.int2_end - rg.cl * kChunkTokens);
+  const int n_rc = max(0, L - max(a.n_sink, L - a.n_recent));
+  return n_sk + n_hd + n_en + n_rc;
+}
+
+// Token-by-token path over 16-token tiles tile_first, tile_first + tile_step,
+// ... (below tile_end) of that list, one tile per wave step, plain fp32.
 // Lane (t, qq) dots 32 channels of token t's key with q' (LDS); the lane
 // owns channels 2*lane, 2*lane+1 of o'.  INT2 tokens are dequantized in
 // registers: key dot = s_K (q'.c) + z_K sum(q'), value = z_V + s_V c.
 template <int GP>
 __device__ void token_path(const DecodeArgs& a, int b, int h, int L, const Int2Range& rg,
+                           int tile_first, int tile_end, int tile_step,
                            const float (*qs)[kHeadDim], const float* qsum,
                            float (*pbuf)[16][GP], float* m, float* l, float* acc0, float* acc1) {
   const int G = a.group;
@@ -176,7 +187,7 @@ __device__ void token_path(const DecodeArgs& a, int b, int h, int L, const Int2R
     return a.recent + (sh_base * a.n_recent + (pos - a.n_sink) % a.n_recent) * 2 * kHeadDim;
   };
   auto is_int2 = [&](int pos) { return pos >= a.n_sink && pos < rg.int2_end; };
-  for (int tile = wave; tile * 16 < n_all; tile += 4) {
+  for (int tile = tile_first; tile < tile_end && tile * 16 < n_all; tile += tile_step) {
     const int idx = tile * 16 + t;
     const bool valid = idx < n_all;
     const int pos = position(valid ? idx : 0);

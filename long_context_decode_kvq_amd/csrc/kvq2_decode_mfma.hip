@@ -8,7 +8,8 @@
 //   QK:  S^T[token][col] = sum_ch codes[token][ch] * Bq[ch][col]
 //        (16x16x32 f16, four k-steps cover the 128 channels)
 //   PV:  O[row][ch]     += sum_tok W[row][tok] * codes[tok][ch]
-//        (16x16x16 f16, eight 16-channel tiles)
+//        (16x16x32 f16 over two chunks, or 16x16x16 for one; eight
+//        16-channel tiles)
 // Dequantization is folded: logit = s_K * (q'.c) + z_K * sum(q'), and
 // o' = sum (p s_V) c + (sum p z_V) on every channel, so codes enter the MFMA
 // as small integers.  A code c in bits 2k..2k+1 of a 16-bit half is turned
@@ -135,9 +136,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// One work item: INT2 split s < n_split_int2 of (b, h), or (s == n_split_int2)
-// the token-by-token part of (b, h).  Leaves its partial in the workspace;
-// the last item of (b, h) to finish combines them and writes `out`.
+// One work item: INT2 split s of (b, h) and its share of the token-by-token
+// list.  Leaves its partial in the workspace; the last item of (b, h) to
+// finish combines them and writes `out`.
 template <int GP>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, const int h,
                                             const int s) {
@@ -169,23 +170,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   load_queries<GP>(a, b, h, qs, qsum, qexp);
 
   const Int2Range rg = int2_range(a, L, NPT);
-  if (s == a.n_split_int2) {
-    float m[GP], l[GP], acc0[GP], acc1[GP];
-#pragma unroll
-    for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
-    token_path<GP>(a, b, h, L, rg, qs, qsum, pbuf, m, l, acc0, acc1);
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      if (g < G) {
-        wo[wave][g][2 * lane] = acc0[g];
-        wo[wave][g][2 * lane + 1] = acc1[g];
-        if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
-      }
-    }
-    __syncthreads();
-    finish_work_group<GP>(a, b, h, s, wm, wl, wo, qs);
-    return;
-  }
 
   // ---- per-lane roles --------------------------------------------------
   const int j = n % (2 * GP);        // column within its chunk block
@@ -277,8 +261,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   };
   constexpr int kDmaPerTile = NPT + (NPT + 1) / 2;
   // One tile from its LDS slot: QK on the matrix cores, lazy online softmax
-  // on the hi lanes, PV on the matrix cores.
-  auto compute_tile = [&](const uint8_t* slot) {
+  // on the hi lanes, PV on the matrix cores.  `after_reads` runs once the
+  // tile's LDS reads have completed: the next block-table lookup is issued
+  // there, so that no lgkmcnt wait of this tile covers it and its latency
+  // overlaps the tile's arithmetic.
+  auto compute_tile = [&](const uint8_t* slot, auto&& after_reads) {
     // this tile's DMA is complete once at most (RING-1) tiles of DMA remain
     wait_vmcnt<(RING - 1) * kDmaPerTile>();
     uint2 kc[NPT], vc[NPT];
@@ -327,6 +314,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           : "v"(acode), "v"(aprm)
           : "memory");
     }
+    after_reads();
     float4_t cq[NPT];
 #pragma unroll
     for (int p = 0; p < NPT; ++p) {
@@ -404,11 +392,32 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     const uint32_t lo02s = dpp_u<0x110 + GP>(lo02), lo13s = dpp_u<0x110 + GP>(lo13);
     const uint32_t av0 = is_hi ? hi02 : lo02s;
     const uint32_t av1 = is_hi ? hi13 : lo13s;
+    if constexpr (NPT >= 2) {
+      // Two chunks per 16x16x32 product: k-slots 0-3 hold tokens 4gq..4gq+3
+      // of chunk pp, slots 4-7 the same tokens of chunk pp + 1; a row (a
+      // column of the QK tile) carries weights only in the half of its own
+      // chunk, so each row still accumulates its own chunk's tokens.
 #pragma unroll
-    for (int p = 0; p < NPT; ++p) {
-      const u32x2_t ap = {pblk == p ? av0 : 0u, pblk == p ? av1 : 0u};
+      for (int pp = 0; pp < NPT; pp += 2) {
+        const u32x4_t ap = {pblk == pp ? av0 : 0u, pblk == pp ? av1 : 0u,
+                            pblk == pp + 1 ? av0 : 0u, pblk == pp + 1 ? av1 : 0u};
+        const half8_t A = __builtin_bit_cast(half8_t, ap);
+        const uint32_t e0 = vc[pp].x, e1 = vc[pp].y, f0 = vc[pp + 1].x, f1 = vc[pp + 1].y;
+        const uint32_t e0s = e0 >> 8, e1s = e1 >> 8, f0s = f0 >> 8, f1s = f1 >> 8;
+#pragma unroll
+        for (int J = 0; J < 8; ++J) {
+          const uint32_t mask = 0x00030003u << (2 * (J & 3));
+          const uint32_t d = J < 4 ? e0 : e1, ds = J < 4 ? e0s : e1s;
+          const uint32_t f = J < 4 ? f0 : f1, fs = J < 4 ? f0s : f1s;
+          const u32x4_t bv = {d & mask, ds & mask, f & mask, fs & mask};
+          cpv[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bv),
+                                                          cpv[J], 0, 0, 0);
+        }
+      }
+    } else {
+      const u32x2_t ap = {av0, av1};
       const half4_t A = __builtin_bit_cast(half4_t, ap);
-      const uint32_t d0 = vc[p].x, d1 = vc[p].y;
+      const uint32_t d0 = vc[0].x, d1 = vc[0].y;
       const uint32_t d0s = d0 >> 8, d1s = d1 >> 8;
 #pragma unroll
       for (int J = 0; J < 8; ++J) {
@@ -440,8 +449,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         const int kn = (k + RING - 1) % RING;
         const int ahead = wave + 4 * (k0 + k + RING - 1);
         issue_tile(ahead, pn, ring_slot_k<GP>(kn, wave));
-        fetch_pages(ahead + 4, pn);
-        if (k0 + k < my_tiles) compute_tile(ring_slot_k<GP>(k, wave));
+        if (k0 + k < my_tiles)
+          compute_tile(ring_slot_k<GP>(k, wave), [&] { fetch_pages(ahead + 4, pn); });
+        else
+          fetch_pages(ahead + 4, pn);
       }
     }
     wait_vmcnt<0>();     // drain DMA before the ring memory is reused
@@ -485,13 +496,46 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     for (int g = 0; g < GP; ++g)
       if (g < G) { wm[wave][g] = m_h[g] - log2_sigma; wl[wave][g] = l_h[g]; }
   }
+
+  // ---- this item's share of the token-by-token list ---------------------
+  // The list's 16-token tiles are dealt out evenly over the splits of
+  // (b, h); wave w takes tiles first + w, first + w + 4, ...  Its fp32 state
+  // is merged into the wave's LDS state (wm, wl, wo are all scaled to the
+  // same running max).  The tile DMA is drained, so the token loads do not
+  // disturb the vmcnt bookkeeping of the ring.
+  {
+    const int n_tt = (token_list_size(a, L, rg) + 15) / 16;
+    const int per = (n_tt + a.n_split_int2 - 1) / a.n_split_int2;
+    const int first = s * per, end = min(n_tt, first + per);
+    if (first + wave < end) {
+      float m[GP], l[GP], acc0[GP], acc1[GP];
+#pragma unroll
+      for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
+      token_path<GP>(a, b, h, L, rg, first + wave, end, 4, qs, qsum, pbuf, m, l, acc0, acc1);
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g < G) {
+          const float mo = wm[wave][g], lo = wl[wave][g];
+          const float mn = fmaxf(mo, m[g]);
+          const float f1 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+          const float f2 = m[g] == -INFINITY ? 0.f : exp2f(m[g] - mn);
+          const float o0 = wo[wave][g][2 * lane], o1 = wo[wave][g][2 * lane + 1];
+          wo[wave][g][2 * lane] = f1 * o0 + f2 * acc0[g];
+          wo[wave][g][2 * lane + 1] = f1 * o1 + f2 * acc1[g];
+          __builtin_amdgcn_wave_barrier();
+          if (lane == 0) { wm[wave][g] = mn; wl[wave][g] = f1 * lo + f2 * l[g]; }
+        }
+      }
+    }
+  }
   __syncthreads();
   finish_work_group<GP>(a, b, h, s, wm, wl, wo, qs);
 }
 
 // Persistent decode: as many work-groups as the GPU holds at once; each
 // takes items from a device counter: the big INT2 splits of every (b, h),
-// then the small ones, then the token-by-token items.  The last work-group to
+// then the small ones.  Each item also takes its share of the (b, h)'s
+// token-by-token list, after its INT2 tiles.  The last work-group to
 // leave resets the counters for the next call on this workspace.
 // Occupancy target: four work-groups (16 waves) per CU for GP <= 4.
 template <int GP>
@@ -499,8 +543,7 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
   __shared__ int item_sh;
   const int pairs = a.batch * a.n_kv_heads;
   const int n_big_items = pairs * a.n_split_big;
-  const int n_int2_items = pairs * a.n_split_int2;
-  const int n_items = n_int2_items + pairs;
+  const int n_items = pairs * a.n_split_int2;
   for (;;) {
     __syncthreads();   // the previous item is done with every LDS buffer
     if (threadIdx.x == 0) item_sh = fetch_add_agent(a.work_counter, 1);
@@ -511,13 +554,10 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
     if (item < n_big_items) {
       pair = item / a.n_split_big;
       s = item - pair * a.n_split_big;
-    } else if (item < n_int2_items) {
+    } else {
       const int i = item - n_big_items;
       pair = i / a.n_split_small;
       s = a.n_split_big + (i - pair * a.n_split_small);
-    } else {
-      pair = item - n_int2_items;
-      s = a.n_split_int2;
     }
     decode_item<GP>(a, pair / a.n_kv_heads, pair % a.n_kv_heads, s);
   }
@@ -561,7 +601,7 @@ int resident_work_groups() {
 
 template <int GP>
 int launch_persistent(const DecodeArgs& a, int batch, hipStream_t st) {
-  const int items = batch * a.n_kv_heads * (a.n_split_int2 + 1);
+  const int items = batch * a.n_kv_heads * a.n_split_int2;
   const int grid = std::max(1, std::min(items, resident_work_groups<GP>()));
   hipLaunchKernelGGL(decode_mfma_kernel<GP>, dim3(grid), dim3(256), 0, st, a);
   return static_cast<int>(hipGetLastError());

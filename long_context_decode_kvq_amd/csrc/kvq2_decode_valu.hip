@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
   } else {
-    token_path<GP>(a, b, h, L, rg, qs, qsum, pbuf, m, l, acc0, acc1);
+    token_path<GP>(a, b, h, L, rg, wave, 1 << 30, 4, qs, qsum, pbuf, m, l, acc0, acc1);
   }
 
   // Wave state -> LDS (o' = acc + zero term on every channel).

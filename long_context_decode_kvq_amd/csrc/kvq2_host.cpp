@@ -94,7 +94,11 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   p.n_split_big = static_cast<int>(nb);
   p.n_split_small = static_cast<int>(nsm);
   p.n_split_int2 = p.n_split_big + p.n_split_small;
-  p.n_split = p.n_split_int2 + 1;
+  // The MFMA decode deals the token-by-token list out over its INT2 items;
+  // the VALU decode (also used for G > 8) gives it a work-group of its own.
+  const int G_plan = d.n_q_heads / d.n_kv_heads;
+  const bool own_token_item = selected_decode_kernel() == kDecodeValu || G_plan > 8;
+  p.n_split = p.n_split_int2 + (own_token_item ? 1 : 0);
   const int G = d.n_q_heads / d.n_kv_heads;
   // arrival tickets [B * Hkv] + the persistent kernel's two work counters
   p.ticket_bytes = ((size_t(heads + 2) * sizeof(int32_t) + 255) / 256) * 256;
