@@ -15,6 +15,7 @@ namespace {
 // the exponent e with 2^-e max|q'[g]| < 1 used to scale f16 MFMA operands.
 __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
   __shared__ float qraw[kMaxGroup][kHeadDim];
+  __shared__ float part[2][kMaxGroup][kHeadDim];
   __shared__ float qs[kMaxGroup][kHeadDim];
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = a.group;
@@ -24,16 +25,36 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
     qraw[g][c] = bf16_bits_to_float(a.q[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c]);
   }
   __syncthreads();
+  // Thread (half, c) sums j in [64 half, 64 half + 64) for every head of the
+  // group: one coalesced load of R row j feeds G independent FMA chains.
   const float* R = a.R_K + int64_t(h) * kHeadDim * kHeadDim;
+  {
+    const int c = tid & (kHeadDim - 1), half = tid >> 7;
+    float acc[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.0f;
+    for (int j0 = 64 * half; j0 < 64 * half + 64; j0 += 16) {
+      float r[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) r[u] = R[(j0 + u) * kHeadDim + c];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g)
+          if (g < G) acc[g] = fmaf(r[u], qraw[g][j0 + u], acc[g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g)
+      if (g < G) part[half][g][c] = acc[g];
+  }
+  __syncthreads();
   float* dst = a.qrot + (int64_t(b) * a.n_q_heads + int64_t(h) * G) * kQStride;
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int g = i / kHeadDim, c = i % kHeadDim;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int j = 0; j < kHeadDim; ++j) acc = fmaf(R[j * kHeadDim + c], qraw[g][j], acc);
-    acc *= a.alpha;
-    qs[g][c] = acc;
-    dst[g * kQStride + c] = acc;
+    const float v = (part[0][g][c] + part[1][g][c]) * a.alpha;
+    qs[g][c] = v;
+    dst[g * kQStride + c] = v;
   }
   __syncthreads();
   __shared__ float qsum[kMaxGroup];
@@ -85,14 +106,47 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
   }
 }
 
+// Tile prefix of the MFMA decode (one work-group): W_b = max(1, number of
+// whole INT2 tiles of sequence b), tile_prefix[b] = W_0 + ... + W_{b-1}.
+// A sequence with no INT2 tile counts one (empty) tile so that a work-group
+// still takes its token-by-token list.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(DecodeArgs a) {
+  __shared__ int part[1024];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  const int npt = 16 / (2 * a.gp);
+  if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
+  __syncthreads();
+  for (int base = 0; base < a.batch; base += 1024) {
+    const int b = base + tid;
+    int w = 0;
+    if (b < a.batch) {
+      const Int2Range rg = int2_range(a, a.seq_len[b], npt);
+      w = max(1, (rg.cl - rg.cf) / npt);
+    }
+    part[tid] = w;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {      // inclusive scan (Hillis-Steele)
+      const int v = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    if (b < a.batch) a.tile_prefix[b + 1] = carry + part[tid];
+    __syncthreads();
+    if (tid == 1023) carry += part[1023];
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
-int launch_decode_mfma(const DecodeArgs& a, int batch, void* stream);
+int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* stream);
 
 int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                   const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
-                  int32_t /*max_seq_len*/, const uint16_t* q, float* out, void* workspace,
+                  int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
                   const DecodePlan& plan, DecodeKernel which, void* stream) {
   DecodeArgs a{};
   a.R_K = layer.R_K;
@@ -127,7 +181,9 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   char* ws = static_cast<char*>(workspace);
   a.qrot = reinterpret_cast<float*>(ws + plan.ticket_bytes);
   a.bq = reinterpret_cast<uint32_t*>(ws + plan.ticket_bytes + plan.qrot_bytes);
-  a.partials = reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes);
+  a.tile_prefix = reinterpret_cast<int32_t*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes);
+  a.partials = reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes +
+                                        plan.prefix_bytes);
   const int G = a.group;
   a.gp = (which == kDecodeValu || G > 8) ? 0 : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
   a.n_split_int2 = plan.n_split_int2;
@@ -136,10 +192,14 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.n_split = plan.n_split;
   hipLaunchKernelGGL(rotate_q_kernel, dim3(d.n_kv_heads, batch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
-  const int err = static_cast<int>(hipGetLastError());
+  int err = static_cast<int>(hipGetLastError());
   if (err != 0) return err;
-  if (which == kDecodeValu) return launch_decode_valu(a, batch, stream);
-  return launch_decode_mfma(a, batch, stream);
+  if (which == kDecodeValu || a.gp == 0) return launch_decode_valu(a, batch, stream);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream),
+                     a);
+  err = static_cast<int>(hipGetLastError());
+  if (err != 0) return err;
+  return launch_decode_mfma(a, batch, max_seq_len, stream);
 }
 
 }  // namespace kvq

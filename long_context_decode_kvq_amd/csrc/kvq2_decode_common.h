@@ -43,6 +43,10 @@ struct DecodeArgs {
   int n_split_big;             // splits over the first 3/4 of the tiles (scheduled first)
   int n_split_small;           // splits over the last 1/4 (scheduled after every big one)
   int n_split;
+  // MFMA decode: tile_prefix[b] = sum over b' < b of max(1, INT2 tiles of
+  // sequence b') (B + 1 entries, written by a pre-pass); the launch cuts the
+  // concatenated tiles of all (b, h) into equal ranges, one per work-group.
+  int32_t* tile_prefix;
 };
 
 // INT2 work of a sequence of length L is split in two parts:
@@ -282,16 +286,18 @@ __device__ void token_path(const DecodeArgs& a, int b, int h, int L, const Int2R
 
 // Merge the softmax states of the 4 waves of a work-group (m, l per head and
 // unnormalized o'[128] per head, staged in LDS) and store the work-group's
-// partial for split `s`.  Then take an arrival ticket; the last work-group of
-// (b, h) combines all splits, applies o = R_V o' and writes `out`.
+// partial in slot `part_slot` of the workspace.  Then take an arrival ticket
+// of (b, h); the last of its n_parts work-groups combines the partials in
+// slots [base_slot, base_slot + n_parts), applies o = R_V o' and writes `out`.
 template <int GP>
-__device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
+__device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t part_slot,
+                                  int64_t base_slot, int n_parts,
                                   float (*wm)[GP], float (*wl)[GP], float (*wo)[GP][kHeadDim],
-                                  float (*ocomb)[kHeadDim]) {
+                                  float (*ocomb)[kHeadDim], float (*s_m)[GP], float (*s_l)[GP]) {
   const int G = a.group;
   const int tid = threadIdx.x;
   const int64_t head = int64_t(b) * a.n_kv_heads + h;
-  float* part = a.partials + (head * a.n_split + s) * G * kPartialStride;
+  float* part = a.partials + part_slot * G * kPartialStride;
   // Merged partial -> LDS (wo[0] is free once every thread has read its
   // inputs), then one wave stores it, makes it visible device-wide (one
   // agent-scope release per work-group) and takes the arrival ticket.
@@ -341,7 +347,7 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
     wait_global_stores();   // the partial is complete before the ticket is taken
     if (tid == 0) {
       const int prev = fetch_add_agent(&a.tickets[head], 1);
-      is_last = (prev == a.n_split - 1);
+      is_last = (prev == n_parts - 1);
     }
   }
   __syncthreads();
@@ -352,15 +358,14 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
   // Split weights f_i = 2^(m_i - M) / sum_k 2^(m_k - M) l_k, staged in LDS
   // in slices of kCombineSlice splits so that all loads of a slice are in
   // flight together.
-  const float* base = a.partials + head * a.n_split * G * kPartialStride;
-  __shared__ float s_m[kCombineSlice][GP];
-  __shared__ float s_l[kCombineSlice][GP];
+  const float* base = a.partials + base_slot * G * kPartialStride;
+  // s_m, s_l: [kCombineSlice][GP] staging of the split weights (caller's LDS)
   __shared__ float s_M[GP], s_den[GP];
   const int wave = tid >> 6, lane = tid & 63;
   if (tid < GP) { s_M[tid] = -INFINITY; s_den[tid] = 0.f; }
   __syncthreads();
-  for (int s0 = 0; s0 < a.n_split; s0 += kCombineSlice) {      // pass 1: M per head
-    const int ns = min(kCombineSlice, a.n_split - s0);
+  for (int s0 = 0; s0 < n_parts; s0 += kCombineSlice) {      // pass 1: M per head
+    const int ns = min(kCombineSlice, n_parts - s0);
     for (int i = tid; i < ns * G; i += blockDim.x) {
       const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
       s_m[i / G][i % G] = load_agent(p);
@@ -378,8 +383,8 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int s,
   float acc[KO];
 #pragma unroll
   for (int k = 0; k < KO; ++k) acc[k] = 0.f;
-  for (int s0 = 0; s0 < a.n_split; s0 += kCombineSlice) {      // pass 2: weighted sums
-    const int ns = min(kCombineSlice, a.n_split - s0);
+  for (int s0 = 0; s0 < n_parts; s0 += kCombineSlice) {      // pass 2: weighted sums
+    const int ns = min(kCombineSlice, n_parts - s0);
     for (int i = tid; i < ns * G; i += blockDim.x) {
       const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
       const float M = s_M[i % G];

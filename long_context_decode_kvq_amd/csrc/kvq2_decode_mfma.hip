@@ -80,7 +80,7 @@ struct Geo {
   static constexpr int NPT = 16 / (2 * GP);
   static constexpr int PARAM_BYTES = NPT >= 2 ? NPT * 128 : 256;
   static constexpr int TILE = NPT * 1024 + PARAM_BYTES;
-  static constexpr int RING = NPT >= 4 ? 2 : (NPT == 2 ? 3 : 6);   // tiles per wave ring
+  static constexpr int RING = NPT >= 4 ? 2 : (NPT == 2 ? 4 : 6);   // tiles per wave ring
 };
 
 // One LDS array per ring position (all waves' slots for that position), so
@@ -136,20 +136,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// One work item: INT2 split s of (b, h) and its share of the token-by-token
-// list.  Leaves its partial in the workspace; the last item of (b, h) to
-// finish combines them and writes `out`.
+// One piece of (b, h): its INT2 tiles [t_lo, t_hi) (clipped to the tiles
+// the sequence has) and share `piece` of n_pieces of its token-by-token
+// list.  Leaves its partial in slot part_slot; the last of the n_pieces
+// pieces of (b, h) to finish combines slots [base_slot, base_slot +
+// n_pieces) and writes `out`.
 template <int GP>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, const int h,
-                                            const int s) {
+                                            const int t_lo, const int t_hi, const int piece,
+                                            const int n_pieces, const int64_t part_slot,
+                                            const int64_t base_slot) {
   constexpr int NPT = Geo<GP>::NPT;    // 16-token chunks per tile
   constexpr int RING = Geo<GP>::RING;
   constexpr int TILE = Geo<GP>::TILE;
-  __shared__ float qs[GP][kHeadDim];
   __shared__ float qsum[GP];
   __shared__ int qexp[GP];
-  __shared__ float pbuf[4][16][GP];
   __shared__ float wm[4][GP], wl[4][GP];
+  // The rotated queries, the token path's weights and the combine's split
+  // weights are only used after the tile loop: they live in ring position 1
+  // when it is large enough (the LDS then holds four work-groups with a
+  // four-tile ring per wave).
+  constexpr int kAuxBytes = GP * (kHeadDim * 4 + 4 * 16 * 4 + 2 * kCombineSlice * 4);
+  constexpr bool kAuxInRing = RING > 1 && 4 * TILE >= kAuxBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t aux_own[kAuxInRing ? 16 : kAuxBytes];
+  uint8_t* aux = kAuxInRing ? ring_slot<GP, 1>(0) : aux_own;
+  float (*qs)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(aux);
+  float (*pbuf)[16][GP] = reinterpret_cast<float (*)[16][GP]>(aux + GP * kHeadDim * 4);
+  float (*cmb_m)[GP] = reinterpret_cast<float (*)[GP]>(aux + GP * (kHeadDim * 4 + 4 * 16 * 4));
+  float (*cmb_l)[GP] =
+      reinterpret_cast<float (*)[GP]>(aux + GP * (kHeadDim * 4 + 4 * 16 * 4 + kCombineSlice * 4));
   // Per-wave o' staging of the epilogue; it reuses ring position 0 when that
   // is large enough (the ring is idle by then).
   constexpr bool kWoInRing = 4 * TILE >= int(4 * GP * kHeadDim * sizeof(float));
@@ -166,9 +181,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   asm volatile("" : "+v"(lane));
   const int gq = lane >> 4, n = lane & 15;
   const int L = a.seq_len[b];
-
-  load_queries<GP>(a, b, h, qs, qsum, qexp);
-
   const Int2Range rg = int2_range(a, L, NPT);
 
   // ---- per-lane roles --------------------------------------------------
@@ -199,8 +211,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     asm volatile("" : "+v"(qscale), "+v"(qbar_s));
   }
 
-  int t_begin, t_end;
-  split_tiles(a, rg, NPT, s, t_begin, t_end);
+  const int tiles_all = (rg.cl - rg.cf) / NPT;
+  const int t_begin = min(t_lo, tiles_all), t_end = min(t_hi, tiles_all);
   const int n_tiles = t_end - t_begin;
   const int c_begin = rg.cf + NPT * t_begin;   // first chunk of this split
   const float log2_sigma = float(a.log2_sigma_v);
@@ -449,15 +461,28 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         const int kn = (k + RING - 1) % RING;
         const int ahead = wave + 4 * (k0 + k + RING - 1);
         issue_tile(ahead, pn, ring_slot_k<GP>(kn, wave));
-        if (k0 + k < my_tiles)
+        if (k0 + k < my_tiles) {
+          // Rotating wave priority: the arbiter otherwise serves the oldest
+          // resident waves first, and the work-groups of one CU, which all
+          // carry equal work, would finish far apart.
+          const int pr = (k0 + k + int(blockIdx.x)) & 3;
+          if (pr == 0) __builtin_amdgcn_s_setprio(0);
+          else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+          else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+          else __builtin_amdgcn_s_setprio(3);
           compute_tile(ring_slot_k<GP>(k, wave), [&] { fetch_pages(ahead + 4, pn); });
-        else
+        } else {
           fetch_pages(ahead + 4, pn);
+        }
       }
     }
     wait_vmcnt<0>();     // drain DMA before the ring memory is reused
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
+  // q' of the group's heads for the token path and the combine (ends with a
+  // barrier); the ring is idle from here on.
+  load_queries<GP>(a, b, h, qs, qsum, qexp);
 
   // ---- wave epilogue: per-head l, z and o' into LDS -----------------------
   float l_h[GP], z_h[GP];
@@ -497,16 +522,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       if (g < G) { wm[wave][g] = m_h[g] - log2_sigma; wl[wave][g] = l_h[g]; }
   }
 
-  // ---- this item's share of the token-by-token list ---------------------
-  // The list's 16-token tiles are dealt out evenly over the splits of
+  // ---- this piece's share of the token-by-token list --------------------
+  // The list's 16-token tiles are dealt out evenly over the n_pieces pieces of
   // (b, h); wave w takes tiles first + w, first + w + 4, ...  Its fp32 state
   // is merged into the wave's LDS state (wm, wl, wo are all scaled to the
   // same running max).  The tile DMA is drained, so the token loads do not
   // disturb the vmcnt bookkeeping of the ring.
   {
     const int n_tt = (token_list_size(a, L, rg) + 15) / 16;
-    const int per = (n_tt + a.n_split_int2 - 1) / a.n_split_int2;
-    const int first = s * per, end = min(n_tt, first + per);
+    const int per = (n_tt + n_pieces - 1) / n_pieces;
+    const int first = piece * per, end = min(n_tt, first + per);
     if (first + wave < end) {
       float m[GP], l[GP], acc0[GP], acc1[GP];
 #pragma unroll
@@ -529,43 +554,48 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     }
   }
   __syncthreads();
-  finish_work_group<GP>(a, b, h, s, wm, wl, wo, qs);
+  finish_work_group<GP>(a, b, h, part_slot, base_slot, n_pieces, wm, wl, wo, qs, cmb_m, cmb_l);
 }
 
-// Persistent decode: as many work-groups as the GPU holds at once; each
-// takes items from a device counter: the big INT2 splits of every (b, h),
-// then the small ones.  Each item also takes its share of the (b, h)'s
-// token-by-token list, after its INT2 tiles.  The last work-group to
-// leave resets the counters for the next call on this workspace.
-// Occupancy target: four work-groups (16 waves) per CU for GP <= 4.
+// Decode over equal tile ranges: the INT2 tiles of all (b, h), in order, with
+// W_b = max(1, tiles of sequence b) per (b, h), are cut into gridDim.x
+// equal contiguous ranges, one per work-group (one round of resident
+// work-groups, so no work queue and no tail of late items).  A work-group
+// takes every (b, h) its range touches; piece j of the k work-groups that
+// touch (b, h) also takes share j of its token-by-token list.  Partial slot
+// of (work-group i, pair p) is i + p: the (i, p) overlaps form a monotone
+// path, so the slots are unique and those of one pair are contiguous.
 template <int GP>
 __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ int item_sh;
-  const int pairs = a.batch * a.n_kv_heads;
-  const int n_big_items = pairs * a.n_split_big;
-  const int n_items = pairs * a.n_split_int2;
-  for (;;) {
-    __syncthreads();   // the previous item is done with every LDS buffer
-    if (threadIdx.x == 0) item_sh = fetch_add_agent(a.work_counter, 1);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(item_sh);
-    if (item >= n_items) break;
-    int pair, s;
-    if (item < n_big_items) {
-      pair = item / a.n_split_big;
-      s = item - pair * a.n_split_big;
-    } else {
-      const int i = item - n_big_items;
-      pair = i / a.n_split_small;
-      s = a.n_split_big + (i - pair * a.n_split_small);
-    }
-    decode_item<GP>(a, pair / a.n_kv_heads, pair % a.n_kv_heads, s);
+  const int i = blockIdx.x, nwg = gridDim.x;
+  const int Hkv = a.n_kv_heads, B = a.batch;
+  const int32_t* pre = a.tile_prefix;
+  const int total = Hkv * pre[B];
+  const int q = (total + nwg - 1) / nwg;
+  const int g0 = i * q, g1 = min(g0 + q, total);
+  if (g0 >= g1) return;
+  // sequence holding tile g0: the largest b with Hkv * pre[b] <= g0
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (Hkv * pre[mid] <= g0) lo = mid; else hi = mid;
   }
-  if (threadIdx.x == 0) {
-    if (fetch_add_agent(a.work_counter + 1, 1) == int(gridDim.x) - 1) {
-      // every work-group has taken its final (out-of-range) item
-      store_agent(a.work_counter, 0);
-      store_agent(a.work_counter + 1, 0);
+  int b = lo;
+  int wb = pre[b + 1] - pre[b];
+  int h = (g0 - Hkv * pre[b]) / wb;
+  for (int first = 1;; first = 0) {
+    const int sp = Hkv * pre[b] + h * wb;        // first tile of (b, h)
+    if (sp >= g1) break;
+    if (!first) __syncthreads();   // the previous piece is done with every LDS buffer
+    const int p = b * Hkv + h;
+    const int i0 = sp / q, i1 = (sp + wb - 1) / q;
+    decode_item<GP>(a, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(h),
+                    max(g0, sp) - sp, min(g1, sp + wb) - sp, i - i0, i1 - i0 + 1,
+                    int64_t(i) + p, int64_t(i0) + p);
+    if (++h == Hkv) {
+      h = 0;
+      if (++b == B) break;
+      wb = pre[b + 1] - pre[b];
     }
   }
 }
@@ -599,24 +629,35 @@ int resident_work_groups() {
   return cached[dev];
 }
 
+// Work-groups of the equal-range decode: one round of resident work-groups,
+// but no more than one per kMinTilesPerGroup tiles (bounded above from
+// max_seq_len), so that short or few sequences are not cut into pieces whose
+// fixed cost (prologue, token tiles, partial, combine) dominates.
+constexpr int kMinTilesPerGroup = 128;
+
 template <int GP>
-int launch_persistent(const DecodeArgs& a, int batch, hipStream_t st) {
-  const int items = batch * a.n_kv_heads * a.n_split_int2;
-  const int grid = std::max(1, std::min(items, resident_work_groups<GP>()));
+int launch_chain(const DecodeArgs& a, int batch, int max_seq_len, hipStream_t st) {
+  constexpr int NPT = Geo<GP>::NPT;
+  const int64_t int2_end = std::max<int64_t>(a.n_sink, int64_t(max_seq_len) - a.n_recent);
+  const int64_t tiles = std::max<int64_t>(1, (int2_end / kChunkTokens) / NPT);
+  const int64_t est = int64_t(batch) * a.n_kv_heads * tiles;
+  const int64_t want = (est + kMinTilesPerGroup - 1) / kMinTilesPerGroup;
+  const int grid = int(std::max<int64_t>(
+      1, std::min<int64_t>(want, std::min(kChainGroups, resident_work_groups<GP>()))));
   hipLaunchKernelGGL(decode_mfma_kernel<GP>, dim3(grid), dim3(256), 0, st, a);
   return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace
 
-int launch_decode_mfma(const DecodeArgs& a, int batch, void* stream) {
+int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* stream) {
   const int G = a.group;
   if (G > 8) return launch_decode_valu(a, batch, stream);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // G = 1 runs the two-head kernel with one padding head.
-  if (G <= 2) return launch_persistent<2>(a, batch, st);
-  if (G <= 4) return launch_persistent<4>(a, batch, st);
-  return launch_persistent<8>(a, batch, st);
+  if (G <= 2) return launch_chain<2>(a, batch, max_seq_len, st);
+  if (G <= 4) return launch_chain<4>(a, batch, max_seq_len, st);
+  return launch_chain<8>(a, batch, max_seq_len, st);
 }
 
 }  // namespace kvq

@@ -26,6 +26,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   __shared__ float pbuf[4][16][GP];          // p of each bf16 token
   __shared__ float wm[4][GP], wl[4][GP];
   __shared__ float wo[4][GP][kHeadDim];
+  __shared__ float cm[kCombineSlice][GP], cl[kCombineSlice][GP];
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -114,7 +115,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  finish_work_group<GP>(a, b, h, s, wm, wl, wo, qs);
+  const int64_t head = int64_t(b) * a.n_kv_heads + h;
+  finish_work_group<GP>(a, b, h, head * a.n_split + s, head * a.n_split, a.n_split, wm, wl, wo, qs,
+                        cm, cl);
 }
 
 }  // namespace

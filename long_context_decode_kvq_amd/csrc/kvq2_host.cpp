@@ -104,8 +104,14 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   p.ticket_bytes = ((size_t(heads + 2) * sizeof(int32_t) + 255) / 256) * 256;
   p.qrot_bytes = size_t(batch) * d.n_q_heads * kQStride * sizeof(float);
   p.bq_bytes = size_t(heads) * kBqWords * sizeof(uint32_t);
-  p.partial_bytes = size_t(heads) * p.n_split * G * kPartialStride * sizeof(float);
-  p.total_bytes = p.ticket_bytes + p.qrot_bytes + p.bq_bytes + p.partial_bytes;
+  p.prefix_bytes = ((size_t(batch) + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  // The MFMA decode cuts all (b, h) tiles into at most kChainGroups equal
+  // ranges: a work-group leaves one partial per (b, h) it touches, in slot
+  // group + b * Hkv + h (unique: the (group, pair) overlaps form a monotone
+  // path), so kChainGroups + B * Hkv slots suffice.
+  const size_t slots = own_token_item ? size_t(heads) * p.n_split : size_t(kChainGroups) + heads;
+  p.partial_bytes = slots * G * kPartialStride * sizeof(float);
+  p.total_bytes = p.ticket_bytes + p.qrot_bytes + p.bq_bytes + p.prefix_bytes + p.partial_bytes;
   return p;
 }
 

@@ -33,9 +33,14 @@ struct DecodePlan {
   size_t ticket_bytes;
   size_t qrot_bytes;    // rotated queries [B][Hq][kQStride] fp32
   size_t bq_bytes;      // QK MFMA operand per (b, h): [64 lanes][16 dwords] + [64][2] fp32
+  size_t prefix_bytes;   // MFMA decode: per-sequence tile prefix [B + 1] int32
   size_t partial_bytes;
   size_t total_bytes;
 };
+
+// Upper bound of the MFMA decode's work-group count (resident work-groups of
+// the device, 256 CUs x 4); its partial slots number kChainGroups + B * Hkv.
+constexpr int kChainGroups = 1024;
 
 DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len);
 
