@@ -1,6 +1,7 @@
 // Decode dispatch: fills the kernel arguments from the validated ABI
 // structures, carves the caller's workspace into arrival counters and
 // split-K partials, and launches the selected decode kernel.
+#include <algorithm>
 #include <cmath>
 
 #include "kvq2_decode_common.h"
@@ -9,44 +10,71 @@ namespace kvq {
 
 namespace {
 
-// Query rotation pre-pass, one work-group per (KV head, sequence):
-// q'[g] = alpha * R_K[h]^T q[b][hG+g] (OSCAR summary sec. 2.2-B: the query is
-// rotated once instead of un-rotating every cached key), plus sum(q'[g]) and
-// the exponent e with 2^-e max|q'[g]| < 1 used to scale f16 MFMA operands.
-__global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
-  __shared__ float qraw[kMaxGroup][kHeadDim];
-  __shared__ float part[2][kMaxGroup][kHeadDim];
-  __shared__ float qs[kMaxGroup][kHeadDim];
-  const int h = blockIdx.x, b = blockIdx.y;
+// Pre-pass of the decode, one work-group per (KV head h, sequence b, token
+// slice z):
+//  * q'[g] = alpha R_K[h]^T q[b][hG+g] (OSCAR summary sec. 2.2-B: the query
+//    is rotated once instead of un-rotating every cached key), sum(q'[g])
+//    and the exponent e with 2^-e max|q'[g]| < 1; slice 0 stores them and,
+//    for the MFMA decode, its QK operand block;
+//  * MFMA decode: tokens [64 z, 64 z + 64) of the token-by-token list of
+//    (b, h), one 16-token tile per wave, merged into one partial in slot
+//    tok_slot0 + (b Hkv + h) n_tok_slices + z.  These scattered small reads
+//    run here, before the streaming decode, where their latency is short;
+//  * MFMA decode, work-group (0, 0, 0): the tile prefix of the equal-range
+//    decode.
+// GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.
+template <int GP>
+__global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a) {
+  constexpr int KG = GP > 0 ? GP : kMaxGroup;   // query heads per KV head held
+  __shared__ float qs[KG][kHeadDim];             // q, then q'
+  // rotation half sums [2][KG][128]; then the waves' o' of the token slice
+  __shared__ float buf[(GP > 0 ? 4 * GP : 2 * kMaxGroup) * kHeadDim];
+  __shared__ float qsum[KG];
+  __shared__ int qexp[KG];
+  const int h = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
   const int G = a.group;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    qraw[g][c] = bf16_bits_to_float(a.q[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c]);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float (*part)[KG][kHeadDim] = reinterpret_cast<float (*)[KG][kHeadDim]>(buf);
+  // q of the group's heads; rows g >= G are zero (they take part in the
+  // rotation below without branches)
+#pragma unroll
+  for (int k = 0; k < KG * kHeadDim / 256; ++k) {
+    const int i = tid + 256 * k, g = i / kHeadDim, c = i % kHeadDim;
+    qs[g][c] = g < G ? bf16_bits_to_float(
+                           a.q[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c])
+                     : 0.f;
   }
   __syncthreads();
   // Thread (half, c) sums j in [64 half, 64 half + 64) for every head of the
-  // group: one coalesced load of R row j feeds G independent FMA chains.
+  // group: one coalesced load of R row j feeds KG independent FMA chains.
   const float* R = a.R_K + int64_t(h) * kHeadDim * kHeadDim;
   {
     const int c = tid & (kHeadDim - 1), half = tid >> 7;
-    float acc[kMaxGroup];
+    float acc[KG];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.0f;
-    for (int j0 = 64 * half; j0 < 64 * half + 64; j0 += 16) {
-      float r[16];
+    for (int g = 0; g < KG; ++g) acc[g] = 0.0f;
+    const int j0 = 64 * half;
+    float r[64];   // all 64 loads in flight together
 #pragma unroll
-      for (int u = 0; u < 16; ++u) r[u] = R[(j0 + u) * kHeadDim + c];
+    for (int u = 0; u < 64; ++u) r[u] = R[(j0 + u) * kHeadDim + c];
+    // (empty asm: one wait for all 64 loads instead of a schedule in batches)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < 64; u += 4) asm volatile("" : "+v"(r[u]), "+v"(r[u + 1]), "+v"(r[u + 2]), "+v"(r[u + 3]));
 #pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g)
-          if (g < G) acc[g] = fmaf(r[u], qraw[g][j0 + u], acc[g]);
+    for (int g = 0; g < KG; ++g) {
+      if (GP == 0 && g >= G) break;   // (uniform) the VALU layout holds up to 16 heads
+      const float4* qv = reinterpret_cast<const float4*>(&qs[g][j0]);
+#pragma unroll
+      for (int u4 = 0; u4 < 16; ++u4) {
+        const float4 x = qv[u4];
+        acc[g] = fmaf(r[4 * u4 + 0], x.x, acc[g]);
+        acc[g] = fmaf(r[4 * u4 + 1], x.y, acc[g]);
+        acc[g] = fmaf(r[4 * u4 + 2], x.z, acc[g]);
+        acc[g] = fmaf(r[4 * u4 + 3], x.w, acc[g]);
       }
     }
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g)
-      if (g < G) part[half][g][c] = acc[g];
+    for (int g = 0; g < KG; ++g) part[half][g][c] = acc[g];
   }
   __syncthreads();
   float* dst = a.qrot + (int64_t(b) * a.n_q_heads + int64_t(h) * G) * kQStride;
@@ -54,88 +82,111 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
     const int g = i / kHeadDim, c = i % kHeadDim;
     const float v = (part[0][g][c] + part[1][g][c]) * a.alpha;
     qs[g][c] = v;
-    dst[g * kQStride + c] = v;
+    if (z == 0) dst[g * kQStride + c] = v;
   }
   __syncthreads();
-  __shared__ float qsum[kMaxGroup];
-  __shared__ int qexp[kMaxGroup];
-  const int wave = tid >> 6, lane = tid & 63;
   for (int g = wave; g < G; g += blockDim.x / 64) {
     const float v0 = qs[g][lane], v1 = qs[g][lane + 64];
     const float sum = wave_sum(v0 + v1);
     const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
     if (lane == 0) {
       const int e = mx > 0.f ? ilogbf(mx) + 1 : 0;
-      dst[g * kQStride + kHeadDim] = sum;
-      dst[g * kQStride + kHeadDim + 1] = float(e);
+      if (z == 0) {
+        dst[g * kQStride + kHeadDim] = sum;
+        dst[g * kQStride + kHeadDim + 1] = float(e);
+      }
       qsum[g] = sum;
       qexp[g] = e;
     }
   }
   __syncthreads();
-  // QK operand of the MFMA kernel in its per-lane layout: lane (gq, n) holds
-  // column n = 2GP p + GP t + g (t = 0: f16 hi part, 1: lo part of q'[g]
-  // scaled by 2^-e_g 2^(8 - 2s)) for the 32 k-slots of its lane group.
-  if (a.gp == 0) return;
-  const int GP = a.gp;
-  uint32_t* bq = a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords;
-  {
-    const int kk = tid >> 6;                 // 4 k-steps x 64 lanes
-    const int gq = lane >> 4, n = lane & 15;
-    const int j = n % (2 * GP), g = j % GP;
-    const bool hi_col = j < GP, ok = g < G;
-    const float down = ok ? ldexpf(1.0f, -qexp[g]) : 0.f;
-    for (int q = 0; q < 4; ++q) {
-      uint32_t word = 0;
-      for (int e = 0; e < 2; ++e) {
-        int ch, sc;
-        kslot_channel(gq, kk, 2 * q + e, ch, sc);
-        const float v = ok ? qs[g][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
-        const _Float16 vh = static_cast<_Float16>(v);
-        const _Float16 vl = static_cast<_Float16>(v - static_cast<float>(vh));
-        const uint32_t bits = __builtin_bit_cast(uint16_t, hi_col ? vh : vl);
-        word |= bits << (16 * e);
+  if constexpr (GP > 0) {
+    if (z == 0) {
+      // QK operand of the MFMA kernel in its per-lane layout: lane (gq, n)
+      // holds column n = 2GP p + GP t + g (t = 0: f16 hi part, 1: lo part of
+      // q'[g] scaled by 2^-e_g 2^(8 - 2s)) for the 32 k-slots of its lane group.
+      uint32_t* bq = a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords;
+      const int kk = tid >> 6;                 // 4 k-steps x 64 lanes
+      const int gq = lane >> 4, n = lane & 15;
+      const int j = n % (2 * GP), g = j % GP;
+      const bool hi_col = j < GP, ok = g < G;
+      const float down = ok ? ldexpf(1.0f, -qexp[g]) : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        uint32_t word = 0;
+        for (int e = 0; e < 2; ++e) {
+          int ch, sc;
+          kslot_channel(gq, kk, 2 * q + e, ch, sc);
+          const float v = ok ? qs[g][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
+          const _Float16 vh = static_cast<_Float16>(v);
+          const _Float16 vl = static_cast<_Float16>(v - static_cast<float>(vh));
+          const uint32_t bits = __builtin_bit_cast(uint16_t, hi_col ? vh : vl);
+          word |= bits << (16 * e);
+        }
+        bq[lane * 16 + kk * 4 + q] = word;
       }
-      bq[lane * 16 + kk * 4 + q] = word;
+      if (kk == 0) {
+        const float qscale = ok ? ldexpf(1.0f, 16 + qexp[g]) : 1.0f;
+        reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane] = qscale;
+        reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane + 1] = ok ? qsum[g] / qscale : 0.f;
+      }
     }
-    if (kk == 0) {
-      const float qscale = ok ? ldexpf(1.0f, 16 + qexp[g]) : 1.0f;
-      reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane] = qscale;
-      reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane + 1] = ok ? qsum[g] / qscale : 0.f;
-    }
-  }
-}
-
-// Tile prefix of the MFMA decode (one work-group): W_b = max(1, number of
-// whole INT2 tiles of sequence b), tile_prefix[b] = W_0 + ... + W_{b-1}.
-// A sequence with no INT2 tile counts one (empty) tile so that a work-group
-// still takes its token-by-token list.
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(DecodeArgs a) {
-  __shared__ int part[1024];
-  __shared__ int carry;
-  const int tid = threadIdx.x;
-  const int npt = 16 / (2 * a.gp);
-  if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
-  __syncthreads();
-  for (int base = 0; base < a.batch; base += 1024) {
-    const int b = base + tid;
-    int w = 0;
-    if (b < a.batch) {
-      const Int2Range rg = int2_range(a, a.seq_len[b], npt);
-      w = max(1, (rg.cl - rg.cf) / npt);
-    }
-    part[tid] = w;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {      // inclusive scan (Hillis-Steele)
-      const int v = tid >= d ? part[tid - d] : 0;
+    constexpr int npt = 16 / (2 * GP);
+    if (a.n_tok_slices > 0) {
+      __shared__ float pbuf[4][16][GP];
+      __shared__ float wm[4][GP], wl[4][GP];
+      float (*wo)[GP][kHeadDim] = reinterpret_cast<float (*)[GP][kHeadDim]>(buf);
+      const int L = a.seq_len[b];
+      const Int2Range rg = int2_range(a, L, npt);
+      const TokenList tl = token_list(a, L, rg);
+      float m[GP], l[GP], acc0[GP], acc1[GP];
+#pragma unroll
+      for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
+      token_tile<GP>(a, b, h, tl, rg, 4 * z + wave, qs, qsum, pbuf[wave], m, l, acc0, acc1);
+      // the rotation's half sums in buf are dead since the barrier above
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g < G) {
+          wo[wave][g][2 * lane] = acc0[g];
+          wo[wave][g][2 * lane + 1] = acc1[g];
+          if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
+        }
+      }
       __syncthreads();
-      part[tid] += v;
-      __syncthreads();
+      float* stage = &wo[0][0][0];
+      merge_wave_states<GP>(G, wm, wl, wo, stage);
+      const int64_t head = int64_t(b) * a.n_kv_heads + h;
+      float* out = a.partials + (a.tok_slot0 + head * a.n_tok_slices + z) * G * kPartialStride;
+      for (int i = tid; i < G * kPartialStride; i += blockDim.x) out[i] = stage[i];
     }
-    if (b < a.batch) a.tile_prefix[b + 1] = carry + part[tid];
-    __syncthreads();
-    if (tid == 1023) carry += part[1023];
-    __syncthreads();
+    if (h == 0 && b == 0 && z == 0) {
+      // W_b = max(1, whole INT2 tiles of sequence b) + piece_cost;
+      // tile_prefix[b] = W_0 + ... + W_{b-1} (inclusive Hillis-Steele scan
+      // over blocks of 256 sequences).
+      __shared__ int scan[256];
+      __shared__ int carry;
+      if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
+      __syncthreads();
+      for (int base = 0; base < a.batch; base += 256) {
+        const int bb = base + tid;
+        int w = 0;
+        if (bb < a.batch) {
+          const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
+          w = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
+        }
+        scan[tid] = w;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+          const int v = tid >= d ? scan[tid - d] : 0;
+          __syncthreads();
+          scan[tid] += v;
+          __syncthreads();
+        }
+        if (bb < a.batch) a.tile_prefix[bb + 1] = carry + scan[tid];
+        __syncthreads();
+        if (tid == 255) carry += scan[255];
+        __syncthreads();
+      }
+    }
   }
 }
 
@@ -190,15 +241,18 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.n_split_big = plan.n_split_big;
   a.n_split_small = plan.n_split_small;
   a.n_split = plan.n_split;
-  hipLaunchKernelGGL(rotate_q_kernel, dim3(d.n_kv_heads, batch), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
-  int err = static_cast<int>(hipGetLastError());
+  a.piece_cost = plan.piece_cost;
+  a.n_tok_slices = plan.n_tok_slices;
+  a.tok_slot0 = plan.tok_slot0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 pgrid(d.n_kv_heads, batch, std::max(1, a.n_tok_slices));
+  if (a.gp == 2) hipLaunchKernelGGL(prologue_kernel<2>, pgrid, dim3(256), 0, st, a);
+  else if (a.gp == 4) hipLaunchKernelGGL(prologue_kernel<4>, pgrid, dim3(256), 0, st, a);
+  else if (a.gp == 8) hipLaunchKernelGGL(prologue_kernel<8>, pgrid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(prologue_kernel<0>, pgrid, dim3(256), 0, st, a);
+  const int err = static_cast<int>(hipGetLastError());
   if (err != 0) return err;
-  if (which == kDecodeValu || a.gp == 0) return launch_decode_valu(a, batch, stream);
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream),
-                     a);
-  err = static_cast<int>(hipGetLastError());
-  if (err != 0) return err;
+  if (a.gp == 0) return launch_decode_valu(a, batch, stream);
   return launch_decode_mfma(a, batch, max_seq_len, stream);
 }
 

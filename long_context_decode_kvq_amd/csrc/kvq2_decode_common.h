@@ -43,10 +43,20 @@ struct DecodeArgs {
   int n_split_big;             // splits over the first 3/4 of the tiles (scheduled first)
   int n_split_small;           // splits over the last 1/4 (scheduled after every big one)
   int n_split;
-  // MFMA decode: tile_prefix[b] = sum over b' < b of max(1, INT2 tiles of
-  // sequence b') (B + 1 entries, written by a pre-pass); the launch cuts the
-  // concatenated tiles of all (b, h) into equal ranges, one per work-group.
+  // MFMA decode: tile_prefix[b] = sum over b' < b of W_b' (B + 1 entries,
+  // written by the pre-pass), W_b = max(1, INT2 tiles of sequence b) +
+  // piece_cost; the launch cuts the concatenated W_b of all (b, h) into equal
+  // ranges, one per work-group.  piece_cost virtual tiles at the start of
+  // every (b, h) stand for the fixed cost of one more piece (prologue,
+  // partial, combine), so that a work-group that starts a pair streams fewer
+  // tiles.
   int32_t* tile_prefix;
+  int piece_cost;
+  // MFMA decode: the token-by-token list of (b, h) is cut into n_tok_slices
+  // slices of 64 tokens; the pre-pass leaves the partial of slice z in slot
+  // tok_slot0 + (b Hkv + h) n_tok_slices + z, and the combine takes them in.
+  int n_tok_slices;
+  int64_t tok_slot0;
 };
 
 // INT2 work of a sequence of length L is split in two parts:
@@ -120,18 +130,19 @@ __device__ void load_queries(const DecodeArgs& a, int b, int h, float (*qs)[kHea
 // = (lane / 4, lane % 4) holds the logit of token t in lg[g] (-inf when
 // masked; the four lanes of a token hold the same value).  Updates the
 // running (m, l) per head, returns the correction factor per head and
-// leaves p = exp2(logit - m) in lg.
+// leaves p = exp2(logit - m) in lg.  All 64 lanes must be active.
 template <int GP>
 __device__ __forceinline__ void softmax_tile16(int G, int qq, float* lg, float* corr, float* m,
                                                float* l) {
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
     if (g >= G) { corr[g] = 1.f; lg[g] = 0.f; continue; }
+    // the lanes of a token hold equal values, so the two mirrors pair the
+    // tokens of a row as xor 1 and xor 2 over t would
     float tm = lg[g];
-    tm = fmaxf(tm, __shfl_xor(tm, 4));
-    tm = fmaxf(tm, __shfl_xor(tm, 8));
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = fmaxf(tm, dpp_move<kRowHalfMirror>(tm));
+    tm = fmaxf(tm, dpp_move<kRowMirror>(tm));
+    tm = fmaxf(fmaxf(read_lane(tm, 0), read_lane(tm, 16)), fmaxf(read_lane(tm, 32), read_lane(tm, 48)));
     const float mn = fmaxf(m[g], tm);
     if (mn == -INFINITY) { corr[g] = 1.f; lg[g] = 0.f; continue; }
     corr[g] = exp2f(m[g] - mn);
@@ -143,169 +154,210 @@ __device__ __forceinline__ void softmax_tile16(int G, int qq, float* lg, float* 
   }
 }
 
-// Number of tokens of the token-by-token list of a sequence of length L: the
+// The token-by-token list of a sequence of length L, in this order: the
 // bf16 sink [0, min(L, n_sink)), the INT2 head tail [n_sink, min(16 cf,
 // int2_end)), the INT2 end tail [16 cl, int2_end) and the bf16 recent window
-// [max(n_sink, L - W), L), in that order.
-__device__ __forceinline__ int token_list_size(const DecodeArgs& a, int L, const Int2Range& rg) {
-  const int n_sk = min(L, a.n_sink);
-  const int n_hd = max(0, min(rg.cf * kChunkTokens, rg.int2_end) - a.n_sink);
-  const int n_en = max(0, rg.int2_end - rg.cl * kChunkTokens);
-  const int n_rc = max(0, L - max(a.n_sink, L - a.n_recent));
-  return n_sk + n_hd + n_en + n_rc;
+// [max(n_sink, L - W), L).
+struct TokenList {
+  int n_sk, n_hd, n_en, n_all, e_begin, r_begin;
+};
+
+__device__ __forceinline__ TokenList token_list(const DecodeArgs& a, int L, const Int2Range& rg) {
+  TokenList t;
+  t.n_sk = min(L, a.n_sink);
+  t.n_hd = max(0, min(rg.cf * kChunkTokens, rg.int2_end) - a.n_sink);
+  t.e_begin = rg.cl * kChunkTokens;
+  t.n_en = max(0, rg.int2_end - t.e_begin);
+  t.r_begin = max(a.n_sink, L - a.n_recent);
+  t.n_all = t.n_sk + t.n_hd + t.n_en + max(0, L - t.r_begin);
+  return t;
 }
 
-// Token-by-token path over 16-token tiles tile_first, tile_first + tile_step,
-// ... (below tile_end) of that list, one tile per wave step, plain fp32.
-// Lane (t, qq) dots 32 channels of token t's key with q' (LDS); the lane
-// owns channels 2*lane, 2*lane+1 of o'.  INT2 tokens are dequantized in
-// registers: key dot = s_K (q'.c) + z_K sum(q'), value = z_V + s_V c.
+// Position of entry idx of the list.
+__device__ __forceinline__ int token_position(const DecodeArgs& a, const TokenList& t, int idx) {
+  if (idx < t.n_sk) return idx;
+  idx -= t.n_sk;
+  if (idx < t.n_hd) return a.n_sink + idx;
+  idx -= t.n_hd;
+  if (idx < t.n_en) return t.e_begin + idx;
+  return t.r_begin + (idx - t.n_en);
+}
+
+// Global-memory byte pointer (a plain pointer rebuilt from integers would be
+// generic, and its loads would count against the LDS wait counter too).
+typedef const uint8_t __attribute__((address_space(1))) global_u8;
+
+__device__ __forceinline__ global_u8* read_lane_ptr(const uint8_t* p, int lane) {
+  const uint64_t u = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFu), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+  return reinterpret_cast<global_u8*>((uint64_t(hi) << 32) | lo);
+}
+
+// Entries [16 tile, 16 tile + 16) of the token-by-token list of (b, h),
+// plain fp32 (one wave).  Lane (t, qq) = (lane / 4, lane % 4) dots channels
+// 32 qq .. 32 qq + 31 of token t's key with q' (LDS); the lane owns
+// channels 2 lane, 2 lane + 1 of o'.  Every key and value load of the tile is
+// issued before the first use.  INT2 tokens are dequantized in registers:
+// key dot = s_K (q'.c) + z_K sum(q'), value = z_V + s_V c.  pb: the wave's
+// [16][GP] LDS buffer of softmax weights.  All 64 lanes must be active.
 template <int GP>
-__device__ void token_path(const DecodeArgs& a, int b, int h, int L, const Int2Range& rg,
-                           int tile_first, int tile_end, int tile_step,
-                           const float (*qs)[kHeadDim], const float* qsum,
-                           float (*pbuf)[16][GP], float* m, float* l, float* acc0, float* acc1) {
+__device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& tl,
+                           const Int2Range& rg, int tile, const float (*qs)[kHeadDim],
+                           const float* qsum, float (*pb)[GP], float* m, float* l, float* acc0,
+                           float* acc1) {
+  const int nt = min(16, tl.n_all - tile * 16);
+  if (nt <= 0) return;
   const int G = a.group;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = lane >> 2, qq = lane & 3;
-  const int n_sk = min(L, a.n_sink);
-  const int h_end = min(rg.cf * kChunkTokens, rg.int2_end);
-  const int n_hd = max(0, h_end - a.n_sink);
-  const int e_begin = rg.cl * kChunkTokens;
-  const int n_en = max(0, rg.int2_end - e_begin);
-  const int r_begin = max(a.n_sink, L - a.n_recent);
-  const int n_rc = max(0, L - r_begin);
-  const int n_all = n_sk + n_hd + n_en + n_rc;
-  const int64_t sh_base = int64_t(b) * a.n_kv_heads + h;
-  // position of virtual token idx
-  auto position = [&](int idx) -> int {
-    if (idx < n_sk) return idx;
-    idx -= n_sk;
-    if (idx < n_hd) return a.n_sink + idx;
-    idx -= n_hd;
-    if (idx < n_en) return e_begin + idx;
-    return r_begin + (idx - n_en);
-  };
-  auto bf16_ptr = [&](int pos) -> const uint16_t* {
-    if (pos < a.n_sink) return a.sink + (sh_base * a.n_sink + pos) * 2 * kHeadDim;
-    return a.recent + (sh_base * a.n_recent + (pos - a.n_sink) % a.n_recent) * 2 * kHeadDim;
-  };
-  auto is_int2 = [&](int pos) { return pos >= a.n_sink && pos < rg.int2_end; };
-  for (int tile = tile_first; tile < tile_end && tile * 16 < n_all; tile += tile_step) {
-    const int idx = tile * 16 + t;
-    const bool valid = idx < n_all;
-    const int pos = position(valid ? idx : 0);
-    // partial dot over this lane's 32 channels; the quad reduction follows
-    float dot[GP], ksc = 1.f, kzr = 0.f;
-#pragma unroll
-    for (int g = 0; g < GP; ++g) dot[g] = 0.f;
-    if (valid && is_int2(pos)) {
+  const int lane = threadIdx.x & 63, t = lane >> 2, qq = lane & 3;
+  const int64_t sh = int64_t(b) * a.n_kv_heads + h;
+  // token t: kind (0 none, 1 bf16 row, 2 INT2 chunk slot ts) and base address
+  int kind = 0, ts = 0;
+  const uint8_t* base = a.pool;
+  if (t < nt) {
+    const int pos = token_position(a, tl, tile * 16 + t);
+    if (pos >= a.n_sink && pos < rg.int2_end) {
       const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
                                        a.page_size, b, h, pos);
-      const uint8_t* ch = a.pool + (off < 0 ? 0 : off);
-      const int ts = pos % kChunkTokens;
-      const uint2 kc = *reinterpret_cast<const uint2*>(ch + kKCodesOff + 32 * ts + 8 * qq);
-      const uint32_t kp = *reinterpret_cast<const uint32_t*>(ch + kKParamsOff + 4 * ts);
-      ksc = f16_bits_to_float(kp & 0xFFFFu);
-      kzr = f16_bits_to_float(kp >> 16);
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        if (g < G) {
-          const float* qv = &qs[g][32 * qq];
-#pragma unroll
-          for (int k = 0; k < 16; ++k) dot[g] = fmaf(qv[k], float((kc.x >> (2 * k)) & 3u), dot[g]);
-#pragma unroll
-          for (int k = 0; k < 16; ++k) dot[g] = fmaf(qv[16 + k], float((kc.y >> (2 * k)) & 3u), dot[g]);
-        }
-      }
-    } else if (valid) {
-      const uint16_t* kp = bf16_ptr(pos) + 32 * qq;
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        if (g < G) {
-#pragma unroll
-          for (int k = 0; k < 32; ++k) dot[g] = fmaf(qs[g][32 * qq + k], bf16_bits_to_float(kp[k]), dot[g]);
-        }
-      }
+      kind = 2;
+      ts = pos % kChunkTokens;
+      base = a.pool + (off < 0 ? 0 : off);   // an invalid page entry reads chunk 0 (memory-safe)
+    } else {
+      kind = 1;
+      const uint16_t* row =
+          pos < a.n_sink ? a.sink + (sh * a.n_sink + pos) * 2 * kHeadDim
+                         : a.recent + (sh * a.n_recent + (pos - a.n_sink) % a.n_recent) * 2 * kHeadDim;
+      base = reinterpret_cast<const uint8_t*>(row);
     }
-    float lg[GP];
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      float d = dot[g];
-      d += __shfl_xor(d, 1);
-      d += __shfl_xor(d, 2);
-      lg[g] = (valid && g < G) ? fmaf(ksc, d, kzr * qsum[g]) : -INFINITY;
-    }
-    float corr[GP];
-    softmax_tile16<GP>(G, qq, lg, corr, m, l);
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      if (qq == 0) pbuf[wave][t][g] = lg[g];
-      acc0[g] *= corr[g];
-      acc1[g] *= corr[g];
-    }
-    __builtin_amdgcn_wave_barrier();
-    const int nt = min(16, n_all - tile * 16);
-    float v0[16], v1[16];
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {   // all loads first: one memory latency per tile
-      v0[tt] = 0.f;
-      v1[tt] = 0.f;
-      if (tt < nt) {
-        const int pp = position(tile * 16 + tt);
-        if (is_int2(pp)) {
-          const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
-                                           a.page_size, b, h, pp);
-          const uint8_t* ch = a.pool + (off < 0 ? 0 : off);
-          const int ts = pp % kChunkTokens, cg = lane >> 1;
-          const uint32_t byte = ch[kVCodesOff + 32 * (cg & 15) + 8 * (ts >> 2) + 4 * (cg >> 4) + (ts & 3)];
-          const uint32_t vp = *reinterpret_cast<const uint32_t*>(ch + kVParamsOff + 4 * ts);
-          const float sv = f16_bits_to_float(vp & 0xFFFFu), zv = f16_bits_to_float(vp >> 16);
-          const int sh = 4 * (lane & 1);
-          v0[tt] = fmaf(sv, float((byte >> sh) & 3u), zv);
-          v1[tt] = fmaf(sv, float((byte >> (sh + 2)) & 3u), zv);
-        } else {
-          const uint32_t v2 = *reinterpret_cast<const uint32_t*>(bf16_ptr(pp) + kHeadDim + 2 * lane);
-          v0[tt] = bf16_bits_to_float(v2 & 0xFFFFu);
-          v1[tt] = bf16_bits_to_float(v2 >> 16);
-        }
-      }
-    }
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        const float p = tt < nt ? pbuf[wave][tt][g] : 0.f;
-        acc0[g] = fmaf(p, v0[tt], acc0[g]);
-        acc1[g] = fmaf(p, v1[tt], acc1[g]);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
   }
+  // ---- loads: the key part of token t, then the values of all 16 tokens.
+  // Every load is issued on every path (tokens of the other kind, and
+  // entries past the list, read harmless in-bounds bytes that are not used),
+  // so that no branch separates a load from the next one.
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef const uint32_t __attribute__((address_space(1))) global_u32;
+  typedef const u32x2 __attribute__((address_space(1))) global_u2;
+  typedef const u32x4 __attribute__((address_space(1))) global_u4;
+  global_u8* gbase = reinterpret_cast<global_u8*>(reinterpret_cast<uintptr_t>(base));
+  global_u8* gpool = reinterpret_cast<global_u8*>(reinterpret_cast<uintptr_t>(a.pool));
+  u32x4 kb[4];
+  {
+    global_u4* p = reinterpret_cast<global_u4*>(kind == 1 ? gbase + 64 * qq : gpool);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kb[i] = p[i];
+  }
+  u32x2 kc = *reinterpret_cast<global_u2*>(kind == 2 ? gbase + kKCodesOff + 32 * ts + 8 * qq
+                                                           : gpool);
+  uint32_t kpar = *reinterpret_cast<global_u32*>(kind == 2 ? gbase + kKParamsOff + 4 * ts
+                                                                  : gpool);
+  uint32_t vword[16], vbyte[16];
+  int vkind[16];
+  const int cg = lane >> 1;
+#pragma unroll
+  for (int tt = 0; tt < 16; ++tt) {
+    vkind[tt] = __builtin_amdgcn_readlane(kind, 4 * tt);
+    const int s = __builtin_amdgcn_readlane(ts, 4 * tt);
+    global_u8* bp = read_lane_ptr(base, 4 * tt);
+    // bf16: channels 2 lane, 2 lane + 1 of the value row; INT2: (s_V, z_V)
+    const int woff = vkind[tt] == 1 ? 2 * kHeadDim + 4 * lane : kVParamsOff + 4 * s;
+    const int boff = vkind[tt] == 2 ? kVCodesOff + 32 * (cg & 15) + 8 * (s >> 2) + 4 * (cg >> 4) + (s & 3)
+                                    : 0;
+    vword[tt] = *reinterpret_cast<global_u32*>(bp + woff);
+    vbyte[tt] = bp[boff];
+  }
+  // Empty asm statements take the loaded values here: the compiler would
+  // otherwise sink each load into the branch that uses it, one wait per load.
+  asm volatile("" : "+v"(kb[0]), "+v"(kb[1]), "+v"(kb[2]), "+v"(kb[3]), "+v"(kc), "+v"(kpar));
+#pragma unroll
+  for (int tt = 0; tt < 16; ++tt) asm volatile("" : "+v"(vword[tt]), "+v"(vbyte[tt]));
+  // ---- logits
+  float dot[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) dot[g] = 0.f;
+  if (kind == 1) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (g < G) {
+        const float* qv = &qs[g][32 * qq];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w[4] = {kb[i].x, kb[i].y, kb[i].z, kb[i].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            dot[g] = fmaf(qv[8 * i + 2 * k], bf16_bits_to_float(w[k] & 0xFFFFu), dot[g]);
+            dot[g] = fmaf(qv[8 * i + 2 * k + 1], bf16_bits_to_float(w[k] >> 16), dot[g]);
+          }
+        }
+      }
+    }
+  } else if (kind == 2) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (g < G) {
+        const float* qv = &qs[g][32 * qq];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dot[g] = fmaf(qv[k], float((kc.x >> (2 * k)) & 3u), dot[g]);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dot[g] = fmaf(qv[16 + k], float((kc.y >> (2 * k)) & 3u), dot[g]);
+      }
+    }
+  }
+  const float ksc = kind == 2 ? f16_bits_to_float(kpar & 0xFFFFu) : 1.f;
+  const float kzr = kind == 2 ? f16_bits_to_float(kpar >> 16) : 0.f;
+  float lg[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    float d = dot[g];
+    d += dpp_move<kQuadXor1>(d);
+    d += dpp_move<kQuadXor2>(d);
+    lg[g] = (kind != 0 && g < G) ? fmaf(ksc, d, kzr * qsum[g]) : -INFINITY;
+  }
+  float corr[GP];
+  softmax_tile16<GP>(G, qq, lg, corr, m, l);
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (qq == 0) pb[t][g] = lg[g];
+    acc0[g] *= corr[g];
+    acc1[g] *= corr[g];
+  }
+  __builtin_amdgcn_wave_barrier();
+  // ---- values: o' += p v over the tile's tokens
+  const int vsh = 4 * (lane & 1);
+#pragma unroll
+  for (int tt = 0; tt < 16; ++tt) {
+    if (vkind[tt] == 0) continue;
+    float v0, v1;
+    if (vkind[tt] == 1) {
+      v0 = bf16_bits_to_float(vword[tt] & 0xFFFFu);
+      v1 = bf16_bits_to_float(vword[tt] >> 16);
+    } else {
+      const float sv = f16_bits_to_float(vword[tt] & 0xFFFFu), zv = f16_bits_to_float(vword[tt] >> 16);
+      v0 = fmaf(sv, float((vbyte[tt] >> vsh) & 3u), zv);
+      v1 = fmaf(sv, float((vbyte[tt] >> (vsh + 2)) & 3u), zv);
+    }
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      const float p = pb[tt][g];
+      acc0[g] = fmaf(p, v0, acc0[g]);
+      acc1[g] = fmaf(p, v1, acc1[g]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
-// Merge the softmax states of the 4 waves of a work-group (m, l per head and
-// unnormalized o'[128] per head, staged in LDS) and store the work-group's
-// partial in slot `part_slot` of the workspace.  Then take an arrival ticket
-// of (b, h); the last of its n_parts work-groups combines the partials in
-// slots [base_slot, base_slot + n_parts), applies o = R_V o' and writes `out`.
+// Merge the softmax states (m, l per head, unnormalized o'[128] per head) of
+// the 4 waves of a work-group, staged in LDS, into stage[g * kPartialStride
+// + ...] = (M, l, 2 pad, o'[128]) (stage may alias wo[0]).  Ends with a
+// barrier.
 template <int GP>
-__device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t part_slot,
-                                  int64_t base_slot, int n_parts,
-                                  float (*wm)[GP], float (*wl)[GP], float (*wo)[GP][kHeadDim],
-                                  float (*ocomb)[kHeadDim], float (*s_m)[GP], float (*s_l)[GP]) {
-  const int G = a.group;
+__device__ void merge_wave_states(int G, const float (*wm)[GP], const float (*wl)[GP],
+                                  float (*wo)[GP][kHeadDim], float* stage) {
   const int tid = threadIdx.x;
-  const int64_t head = int64_t(b) * a.n_kv_heads + h;
-  float* part = a.partials + part_slot * G * kPartialStride;
-  // Merged partial -> LDS (wo[0] is free once every thread has read its
-  // inputs), then one wave stores it, makes it visible device-wide (one
-  // agent-scope release per work-group) and takes the arrival ticket.
-  float* stage = &wo[0][0][0];
-  float merged[(GP * kHeadDim + 255) / 256];
-  float Ms[(GP * kHeadDim + 255) / 256], Ls[(GP * kHeadDim + 255) / 256];
+  constexpr int K = (GP * kHeadDim + 255) / 256;
+  float merged[K], Ms[K], Ls[K];
 #pragma unroll
-  for (int k = 0; k < (GP * kHeadDim + 255) / 256; ++k) {
+  for (int k = 0; k < K; ++k) {
     const int i = tid + 256 * k;
     merged[k] = 0.f;
     Ms[k] = -INFINITY;
@@ -329,7 +381,7 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < (GP * kHeadDim + 255) / 256; ++k) {
+  for (int k = 0; k < K; ++k) {
     const int i = tid + 256 * k;
     if (i < G * kHeadDim) {
       const int g = i / kHeadDim, c = i % kHeadDim;
@@ -341,6 +393,28 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
     }
   }
   __syncthreads();
+}
+
+// Merge the 4 waves' states (see merge_wave_states) and store the
+// work-group's partial in slot `part_slot` of the workspace.  Then take an
+// arrival ticket of (b, h); the last of its n_parts work-groups combines the
+// partials in slots [base_slot, base_slot + n_parts) and [tok_slot, tok_slot
+// + n_tok) (the latter written by an earlier kernel), applies o = R_V o' and
+// writes `out`.  ocomb: [GP][kHeadDim], s_m, s_l: [kCombineSlice][GP] LDS.
+template <int GP>
+__device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t part_slot,
+                                  int64_t base_slot, int n_parts, int64_t tok_slot, int n_tok,
+                                  float (*wm)[GP], float (*wl)[GP], float (*wo)[GP][kHeadDim],
+                                  float (*ocomb)[kHeadDim], float (*s_m)[GP], float (*s_l)[GP]) {
+  const int G = a.group;
+  const int tid = threadIdx.x;
+  const int64_t head = int64_t(b) * a.n_kv_heads + h;
+  float* part = a.partials + part_slot * G * kPartialStride;
+  // Merged partial -> LDS (wo[0] is free once every thread has read its
+  // inputs), then one wave stores it, makes it visible device-wide (one
+  // agent-scope release per work-group) and takes the arrival ticket.
+  float* stage = &wo[0][0][0];
+  merge_wave_states<GP>(G, wm, wl, wo, stage);
   __shared__ int is_last;
   if (tid < 64) {
     for (int i = tid; i < G * kPartialStride; i += 64) store_agent(part + i, stage[i]);
@@ -356,20 +430,21 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
   // device-coherent loads below.
 
   // Split weights f_i = 2^(m_i - M) / sum_k 2^(m_k - M) l_k, staged in LDS
-  // in slices of kCombineSlice splits so that all loads of a slice are in
+  // in slices of kCombineSlice partials so that all loads of a slice are in
   // flight together.
-  const float* base = a.partials + base_slot * G * kPartialStride;
-  // s_m, s_l: [kCombineSlice][GP] staging of the split weights (caller's LDS)
+  const int n_all = n_parts + n_tok;
+  auto slot_ptr = [&](int i) -> const float* {
+    const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    return a.partials + s * G * kPartialStride;
+  };
   __shared__ float s_M[GP], s_den[GP];
   const int wave = tid >> 6, lane = tid & 63;
   if (tid < GP) { s_M[tid] = -INFINITY; s_den[tid] = 0.f; }
   __syncthreads();
-  for (int s0 = 0; s0 < n_parts; s0 += kCombineSlice) {      // pass 1: M per head
-    const int ns = min(kCombineSlice, n_parts - s0);
-    for (int i = tid; i < ns * G; i += blockDim.x) {
-      const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
-      s_m[i / G][i % G] = load_agent(p);
-    }
+  for (int s0 = 0; s0 < n_all; s0 += kCombineSlice) {      // pass 1: M per head
+    const int ns = min(kCombineSlice, n_all - s0);
+    for (int i = tid; i < ns * G; i += blockDim.x)
+      s_m[i / G][i % G] = load_agent(slot_ptr(s0 + i / G) + (i % G) * kPartialStride);
     __syncthreads();
     for (int g = wave; g < G; g += 4) {
       float mx = -INFINITY;
@@ -383,10 +458,10 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
   float acc[KO];
 #pragma unroll
   for (int k = 0; k < KO; ++k) acc[k] = 0.f;
-  for (int s0 = 0; s0 < n_parts; s0 += kCombineSlice) {      // pass 2: weighted sums
-    const int ns = min(kCombineSlice, n_parts - s0);
+  for (int s0 = 0; s0 < n_all; s0 += kCombineSlice) {      // pass 2: weighted sums
+    const int ns = min(kCombineSlice, n_all - s0);
     for (int i = tid; i < ns * G; i += blockDim.x) {
-      const float* p = base + ((s0 + i / G) * G + i % G) * kPartialStride;
+      const float* p = slot_ptr(s0 + i / G) + (i % G) * kPartialStride;
       const float M = s_M[i % G];
       const float f = M == -INFINITY ? 0.f : exp2f(load_agent(p) - M);
       s_m[i / G][i % G] = f;
@@ -405,9 +480,9 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
       if (o < G * kHeadDim) {
         const int g = o / kHeadDim, c = o % kHeadDim;
         float v = 0.f;
-#pragma unroll 8
+#pragma unroll 16
         for (int i = 0; i < ns; ++i)
-          v = fmaf(s_m[i][g], load_agent(base + ((s0 + i) * G + g) * kPartialStride + 4 + c), v);
+          v = fmaf(s_m[i][g], load_agent(slot_ptr(s0 + i) + g * kPartialStride + 4 + c), v);
         acc[k] += v;
       }
     }
@@ -422,21 +497,38 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
     }
   }
   __syncthreads();
-  // o = R_V o' (row-major R_V: o_i = sum_j R_V[i][j] o'_j)
-  const float* R = a.R_V + int64_t(h) * kHeadDim * kHeadDim;
-  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
-    const int g = i / kHeadDim, c = i % kHeadDim;
-    const float4* row = reinterpret_cast<const float4*>(R + c * kHeadDim);
-    float o = 0.0f;
-#pragma unroll 4
-    for (int j = 0; j < kHeadDim / 4; ++j) {
-      const float4 r = row[j];
-      o = fmaf(r.x, ocomb[g][4 * j + 0], o);
-      o = fmaf(r.y, ocomb[g][4 * j + 1], o);
-      o = fmaf(r.z, ocomb[g][4 * j + 2], o);
-      o = fmaf(r.w, ocomb[g][4 * j + 3], o);
+  // o = R_V o' (row-major R_V: o_i = sum_j R_V[i][j] o'_j).  Thread (half,
+  // i) loads half of row i once (16 loads in flight) and applies it to every
+  // head; the two halves meet in LDS (wo is free again).
+  {
+    const float* R = a.R_V + int64_t(h) * kHeadDim * kHeadDim;
+    const int i = tid & (kHeadDim - 1), half = tid >> 7;
+    const float4* row = reinterpret_cast<const float4*>(R + i * kHeadDim + 64 * half);
+    float4 r[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = row[j];
+    float* red = &wo[0][0][0];   // [2][GP][kHeadDim]
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (g < G) {
+        const float* oc = &ocomb[g][64 * half];
+        float o = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          o = fmaf(r[j].x, oc[4 * j + 0], o);
+          o = fmaf(r[j].y, oc[4 * j + 1], o);
+          o = fmaf(r[j].z, oc[4 * j + 2], o);
+          o = fmaf(r[j].w, oc[4 * j + 3], o);
+        }
+        red[(half * GP + g) * kHeadDim + i] = o;
+      }
     }
-    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] = o;
+    __syncthreads();
+    for (int k = tid; k < G * kHeadDim; k += blockDim.x) {
+      const int g = k / kHeadDim, c = k % kHeadDim;
+      a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] =
+          red[g * kHeadDim + c] + red[(GP + g) * kHeadDim + c];
+    }
   }
   if (tid == 0) store_agent(&a.tickets[head], 0);   // ready for the next call on this workspace
 }

@@ -136,35 +136,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// One piece of (b, h): its INT2 tiles [t_lo, t_hi) (clipped to the tiles
-// the sequence has) and share `piece` of n_pieces of its token-by-token
-// list.  Leaves its partial in slot part_slot; the last of the n_pieces
-// pieces of (b, h) to finish combines slots [base_slot, base_slot +
-// n_pieces) and writes `out`.
+// One piece of (b, h): the INT2 tiles [t_lo, t_hi) of its range of W_b
+// virtual tiles (the first piece_cost of them stand for no tile; the rest
+// are clipped to the tiles the sequence has).  Leaves its partial in slot
+// part_slot; the last of the n_pieces pieces of (b, h) to finish combines
+// slots [base_slot, base_slot + n_pieces) and the token-list slices that the
+// pre-pass left, and writes `out`.
 template <int GP>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, const int h,
-                                            const int t_lo, const int t_hi, const int piece,
-                                            const int n_pieces, const int64_t part_slot,
+                                            const int t_lo, const int t_hi, const int n_pieces,
+                                            const int64_t part_slot,
                                             const int64_t base_slot) {
   constexpr int NPT = Geo<GP>::NPT;    // 16-token chunks per tile
   constexpr int RING = Geo<GP>::RING;
   constexpr int TILE = Geo<GP>::TILE;
-  __shared__ float qsum[GP];
-  __shared__ int qexp[GP];
   __shared__ float wm[4][GP], wl[4][GP];
-  // The rotated queries, the token path's weights and the combine's split
-  // weights are only used after the tile loop: they live in ring position 1
-  // when it is large enough (the LDS then holds four work-groups with a
-  // four-tile ring per wave).
-  constexpr int kAuxBytes = GP * (kHeadDim * 4 + 4 * 16 * 4 + 2 * kCombineSlice * 4);
+  // The combine's o' and split weights are only used after the tile loop:
+  // they live in ring position 1 when it is large enough (the LDS then holds
+  // four work-groups with a four-tile ring per wave).
+  constexpr int kAuxBytes = GP * (kHeadDim * 4 + 2 * kCombineSlice * 4);
   constexpr bool kAuxInRing = RING > 1 && 4 * TILE >= kAuxBytes;
   __shared__ __attribute__((aligned(16))) uint8_t aux_own[kAuxInRing ? 16 : kAuxBytes];
   uint8_t* aux = kAuxInRing ? ring_slot<GP, 1>(0) : aux_own;
-  float (*qs)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(aux);
-  float (*pbuf)[16][GP] = reinterpret_cast<float (*)[16][GP]>(aux + GP * kHeadDim * 4);
-  float (*cmb_m)[GP] = reinterpret_cast<float (*)[GP]>(aux + GP * (kHeadDim * 4 + 4 * 16 * 4));
-  float (*cmb_l)[GP] =
-      reinterpret_cast<float (*)[GP]>(aux + GP * (kHeadDim * 4 + 4 * 16 * 4 + kCombineSlice * 4));
+  float (*ocomb)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(aux);
+  float (*cmb_m)[GP] = reinterpret_cast<float (*)[GP]>(aux + GP * kHeadDim * 4);
+  float (*cmb_l)[GP] = reinterpret_cast<float (*)[GP]>(aux + GP * (kHeadDim * 4 + kCombineSlice * 4));
   // Per-wave o' staging of the epilogue; it reuses ring position 0 when that
   // is large enough (the ring is idle by then).
   constexpr bool kWoInRing = 4 * TILE >= int(4 * GP * kHeadDim * sizeof(float));
@@ -180,8 +176,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
   const int gq = lane >> 4, n = lane & 15;
-  const int L = a.seq_len[b];
-  const Int2Range rg = int2_range(a, L, NPT);
+  const Int2Range rg = int2_range(a, a.seq_len[b], NPT);
 
   // ---- per-lane roles --------------------------------------------------
   const int j = n % (2 * GP);        // column within its chunk block
@@ -212,7 +207,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   }
 
   const int tiles_all = (rg.cl - rg.cf) / NPT;
-  const int t_begin = min(t_lo, tiles_all), t_end = min(t_hi, tiles_all);
+  const int t_begin = min(max(t_lo - a.piece_cost, 0), tiles_all);
+  const int t_end = min(max(t_hi - a.piece_cost, 0), tiles_all);
   const int n_tiles = t_end - t_begin;
   const int c_begin = rg.cf + NPT * t_begin;   // first chunk of this split
   const float log2_sigma = float(a.log2_sigma_v);
@@ -479,10 +475,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     wait_vmcnt<0>();     // drain DMA before the ring memory is reused
     __builtin_amdgcn_s_setprio(0);
   }
-  __syncthreads();
-  // q' of the group's heads for the token path and the combine (ends with a
-  // barrier); the ring is idle from here on.
-  load_queries<GP>(a, b, h, qs, qsum, qexp);
+  __syncthreads();   // the ring is idle from here on
 
   // ---- wave epilogue: per-head l, z and o' into LDS -----------------------
   float l_h[GP], z_h[GP];
@@ -522,49 +515,20 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       if (g < G) { wm[wave][g] = m_h[g] - log2_sigma; wl[wave][g] = l_h[g]; }
   }
 
-  // ---- this piece's share of the token-by-token list --------------------
-  // The list's 16-token tiles are dealt out evenly over the n_pieces pieces of
-  // (b, h); wave w takes tiles first + w, first + w + 4, ...  Its fp32 state
-  // is merged into the wave's LDS state (wm, wl, wo are all scaled to the
-  // same running max).  The tile DMA is drained, so the token loads do not
-  // disturb the vmcnt bookkeeping of the ring.
-  {
-    const int n_tt = (token_list_size(a, L, rg) + 15) / 16;
-    const int per = (n_tt + n_pieces - 1) / n_pieces;
-    const int first = piece * per, end = min(n_tt, first + per);
-    if (first + wave < end) {
-      float m[GP], l[GP], acc0[GP], acc1[GP];
-#pragma unroll
-      for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
-      token_path<GP>(a, b, h, L, rg, first + wave, end, 4, qs, qsum, pbuf, m, l, acc0, acc1);
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        if (g < G) {
-          const float mo = wm[wave][g], lo = wl[wave][g];
-          const float mn = fmaxf(mo, m[g]);
-          const float f1 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
-          const float f2 = m[g] == -INFINITY ? 0.f : exp2f(m[g] - mn);
-          const float o0 = wo[wave][g][2 * lane], o1 = wo[wave][g][2 * lane + 1];
-          wo[wave][g][2 * lane] = f1 * o0 + f2 * acc0[g];
-          wo[wave][g][2 * lane + 1] = f1 * o1 + f2 * acc1[g];
-          __builtin_amdgcn_wave_barrier();
-          if (lane == 0) { wm[wave][g] = mn; wl[wave][g] = f1 * lo + f2 * l[g]; }
-        }
-      }
-    }
-  }
   __syncthreads();
-  finish_work_group<GP>(a, b, h, part_slot, base_slot, n_pieces, wm, wl, wo, qs, cmb_m, cmb_l);
+  const int64_t head = int64_t(b) * a.n_kv_heads + h;
+  finish_work_group<GP>(a, b, h, part_slot, base_slot, n_pieces,
+                        a.tok_slot0 + head * a.n_tok_slices, a.n_tok_slices, wm, wl, wo, ocomb,
+                        cmb_m, cmb_l);
 }
 
-// Decode over equal tile ranges: the INT2 tiles of all (b, h), in order, with
-// W_b = max(1, tiles of sequence b) per (b, h), are cut into gridDim.x
-// equal contiguous ranges, one per work-group (one round of resident
-// work-groups, so no work queue and no tail of late items).  A work-group
-// takes every (b, h) its range touches; piece j of the k work-groups that
-// touch (b, h) also takes share j of its token-by-token list.  Partial slot
-// of (work-group i, pair p) is i + p: the (i, p) overlaps form a monotone
-// path, so the slots are unique and those of one pair are contiguous.
+// Decode over equal tile ranges: the virtual tiles of all (b, h), in order,
+// W_b = max(1, INT2 tiles of sequence b) + piece_cost per (b, h), are cut
+// into gridDim.x equal contiguous ranges, one per work-group (one round of
+// resident work-groups, so no work queue and no tail of late items).  A
+// work-group takes every (b, h) its range touches.  Partial slot of
+// (work-group i, pair p) is i + p: the (i, p) overlaps form a monotone path,
+// so the slots are unique and those of one pair are contiguous.
 template <int GP>
 __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
   const int i = blockIdx.x, nwg = gridDim.x;
@@ -590,7 +554,7 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
     const int p = b * Hkv + h;
     const int i0 = sp / q, i1 = (sp + wb - 1) / q;
     decode_item<GP>(a, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(h),
-                    max(g0, sp) - sp, min(g1, sp + wb) - sp, i - i0, i1 - i0 + 1,
+                    max(g0, sp) - sp, min(g1, sp + wb) - sp, i1 - i0 + 1,
                     int64_t(i) + p, int64_t(i0) + p);
     if (++h == Hkv) {
       h = 0;

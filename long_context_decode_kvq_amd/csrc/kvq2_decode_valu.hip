@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
           for (int k = 0; k < 16; ++k) dot = fmaf(qv[16 + k], float((kc.y >> (2 * k)) & 3u), dot);
         }
-        dot += __shfl_xor(dot, 1);
-        dot += __shfl_xor(dot, 2);
+        dot += dpp_move<kQuadXor1>(dot);
+        dot += dpp_move<kQuadXor2>(dot);
         const float sk = f16_bits_to_float(kp & 0xFFFFu), zk = f16_bits_to_float(kp >> 16);
         lg[g] = (g < G) ? fmaf(sk, dot, zk * qsum[g]) : -INFINITY;
       }
@@ -101,7 +101,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
   } else {
-    token_path<GP>(a, b, h, L, rg, wave, 1 << 30, 4, qs, qsum, pbuf, m, l, acc0, acc1);
+    const TokenList tl = token_list(a, L, rg);
+    for (int tile = wave; tile * 16 < tl.n_all; tile += 4)
+      token_tile<GP>(a, b, h, tl, rg, tile, qs, qsum, pbuf[wave], m, l, acc0, acc1);
   }
 
   // Wave state -> LDS (o' = acc + zero term on every channel).
@@ -116,8 +118,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int64_t head = int64_t(b) * a.n_kv_heads + h;
-  finish_work_group<GP>(a, b, h, head * a.n_split + s, head * a.n_split, a.n_split, wm, wl, wo, qs,
-                        cm, cl);
+  finish_work_group<GP>(a, b, h, head * a.n_split + s, head * a.n_split, a.n_split, 0, 0, wm, wl,
+                        wo, qs, cm, cl);
 }
 
 }  // namespace

@@ -27,22 +27,48 @@ __device__ __forceinline__ uint32_t float_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
+// Cross-lane moves within 16-lane rows (DPP): QUAD_XOR1/2 exchange lanes
+// i ^ 1 and i ^ 2; ROW_HALF_MIRROR maps lane i of 8 to 7 - i and ROW_MIRROR
+// lane i of 16 to 15 - i.  After the two quad steps every lane of a quad
+// holds the quad's value, so the mirrors then act as butterflies over quads
+// and half rows.
+enum : int { kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xf, 0xf, true));
+}
+
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Reductions over all 64 lanes of a wave (every lane must be active): four
+// DPP butterfly steps give each 16-lane row its total, the four row totals
+// are combined through scalar registers, so every lane gets the same value.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  v = fmaxf(v, dpp_move<kQuadXor1>(v));
+  v = fmaxf(v, dpp_move<kQuadXor2>(v));
+  v = fmaxf(v, dpp_move<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_move<kRowMirror>(v));
+  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
-  return v;
+  v = fminf(v, dpp_move<kQuadXor1>(v));
+  v = fminf(v, dpp_move<kQuadXor2>(v));
+  v = fminf(v, dpp_move<kRowHalfMirror>(v));
+  v = fminf(v, dpp_move<kRowMirror>(v));
+  return fminf(fminf(read_lane(v, 0), read_lane(v, 16)), fminf(read_lane(v, 32), read_lane(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  v += dpp_move<kQuadXor1>(v);
+  v += dpp_move<kQuadXor2>(v);
+  v += dpp_move<kRowHalfMirror>(v);
+  v += dpp_move<kRowMirror>(v);
+  return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 // Device-coherent global accesses for data handed between work-groups of one

@@ -109,7 +109,20 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   // ranges: a work-group leaves one partial per (b, h) it touches, in slot
   // group + b * Hkv + h (unique: the (group, pair) overlaps form a monotone
   // path), so kChainGroups + B * Hkv slots suffice.
-  const size_t slots = own_token_item ? size_t(heads) * p.n_split : size_t(kChainGroups) + heads;
+  if (!own_token_item) {
+    // The token-by-token list of a sequence: the sink, at most 15 INT2
+    // positions before the first whole chunk, at most 16 npt - 1 after the
+    // last whole tile, and the recent window.
+    const int gp = G <= 2 ? 2 : G <= 4 ? 4 : 8;
+    const int npt = 16 / (2 * gp);
+    const int64_t max_list = int64_t(d.n_sink) + 15 + (16 * npt - 1) + d.n_recent;
+    p.n_tok_slices = static_cast<int>((max_list + 63) / 64);
+    p.tok_slot0 = int64_t(kChainGroups) + heads;
+    p.piece_cost = std::max(0, env_int("KVQ_PIECE_COST", kPieceCostChunks)) / npt;
+  }
+  const size_t slots = own_token_item
+                           ? size_t(heads) * p.n_split
+                           : size_t(kChainGroups) + size_t(heads) * (1 + p.n_tok_slices);
   p.partial_bytes = slots * G * kPartialStride * sizeof(float);
   p.total_bytes = p.ticket_bytes + p.qrot_bytes + p.bq_bytes + p.prefix_bytes + p.partial_bytes;
   return p;

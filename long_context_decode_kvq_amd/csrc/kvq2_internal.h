@@ -33,14 +33,22 @@ struct DecodePlan {
   size_t ticket_bytes;
   size_t qrot_bytes;    // rotated queries [B][Hq][kQStride] fp32
   size_t bq_bytes;      // QK MFMA operand per (b, h): [64 lanes][16 dwords] + [64][2] fp32
+  int piece_cost;       // MFMA decode: virtual tiles charged per (b, h) piece start
+  int n_tok_slices;     // MFMA decode: 64-token slices of the token-by-token list
+  int64_t tok_slot0;    // MFMA decode: first partial slot of those slices
   size_t prefix_bytes;   // MFMA decode: per-sequence tile prefix [B + 1] int32
   size_t partial_bytes;
   size_t total_bytes;
 };
 
 // Upper bound of the MFMA decode's work-group count (resident work-groups of
-// the device, 256 CUs x 4); its partial slots number kChainGroups + B * Hkv.
+// the device, 256 CUs x 4); its partial slots number kChainGroups + B * Hkv,
+// followed by B * Hkv * n_tok_slices slots of the token-list slices.
 constexpr int kChainGroups = 1024;
+// Fixed cost of one more piece of the MFMA decode (its prologue, the first
+// tile's latency, the partial store and the combine), in 16-token chunks of
+// streaming: about 15 us at one work-group's share of HBM bandwidth.
+constexpr int kPieceCostChunks = 80;
 
 DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len);
 
