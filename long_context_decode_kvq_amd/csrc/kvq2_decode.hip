@@ -22,9 +22,11 @@ namespace {
 //    run here, before the streaming decode, where their latency is short;
 //  * MFMA decode, work-group (0, 0, 0): the tile prefix of the equal-range
 //    decode.
-// GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.
+// GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.  At most
+// 96 VGPRs (five work-groups per CU) so that the slices of a long batch are
+// resident together.
 template <int GP>
-__global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
   constexpr int KG = GP > 0 ? GP : kMaxGroup;   // query heads per KV head held
   __shared__ float qs[KG][kHeadDim];             // q, then q'
   // rotation half sums [2][KG][128]; then the waves' o' of the token slice

@@ -251,7 +251,12 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
                                                            : gpool);
   uint32_t kpar = *reinterpret_cast<global_u32*>(kind == 2 ? gbase + kKParamsOff + 4 * ts
                                                                   : gpool);
-  uint32_t vword[16], vbyte[16];
+  // Values: one dword per lane and token (bf16: channels 2 lane, 2 lane + 1
+  // of the value row; INT2: the dword holding this lane's code byte), and
+  // for INT2 tokens the (s_V, z_V) pair, the same for every lane, through the
+  // scalar cache.
+  typedef const uint32_t __attribute__((address_space(4))) const_u32;
+  uint32_t vword[16], vpar[16];
   int vkind[16];
   const int cg = lane >> 1;
 #pragma unroll
@@ -259,18 +264,18 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
     vkind[tt] = __builtin_amdgcn_readlane(kind, 4 * tt);
     const int s = __builtin_amdgcn_readlane(ts, 4 * tt);
     global_u8* bp = read_lane_ptr(base, 4 * tt);
-    // bf16: channels 2 lane, 2 lane + 1 of the value row; INT2: (s_V, z_V)
-    const int woff = vkind[tt] == 1 ? 2 * kHeadDim + 4 * lane : kVParamsOff + 4 * s;
-    const int boff = vkind[tt] == 2 ? kVCodesOff + 32 * (cg & 15) + 8 * (s >> 2) + 4 * (cg >> 4) + (s & 3)
-                                    : 0;
+    const int boff = kVCodesOff + 32 * (cg & 15) + 8 * (s >> 2) + 4 * (cg >> 4);   // + (s & 3)
+    const int woff = vkind[tt] == 1 ? 2 * kHeadDim + 4 * lane : boff;
     vword[tt] = *reinterpret_cast<global_u32*>(bp + woff);
-    vbyte[tt] = bp[boff];
+    const uint8_t* pp = vkind[tt] == 2 ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(bp)) + kVParamsOff + 4 * s
+                                       : a.pool;
+    vpar[tt] = *reinterpret_cast<const_u32*>(reinterpret_cast<uintptr_t>(pp));
   }
   // Empty asm statements take the loaded values here: the compiler would
   // otherwise sink each load into the branch that uses it, one wait per load.
   asm volatile("" : "+v"(kb[0]), "+v"(kb[1]), "+v"(kb[2]), "+v"(kb[3]), "+v"(kc), "+v"(kpar));
 #pragma unroll
-  for (int tt = 0; tt < 16; ++tt) asm volatile("" : "+v"(vword[tt]), "+v"(vbyte[tt]));
+  for (int tt = 0; tt < 16; ++tt) asm volatile("" : "+v"(vword[tt]));
   // ---- logits
   float dot[GP];
 #pragma unroll
@@ -332,9 +337,10 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
       v0 = bf16_bits_to_float(vword[tt] & 0xFFFFu);
       v1 = bf16_bits_to_float(vword[tt] >> 16);
     } else {
-      const float sv = f16_bits_to_float(vword[tt] & 0xFFFFu), zv = f16_bits_to_float(vword[tt] >> 16);
-      v0 = fmaf(sv, float((vbyte[tt] >> vsh) & 3u), zv);
-      v1 = fmaf(sv, float((vbyte[tt] >> (vsh + 2)) & 3u), zv);
+      const float sv = f16_bits_to_float(vpar[tt] & 0xFFFFu), zv = f16_bits_to_float(vpar[tt] >> 16);
+      const uint32_t byte = vword[tt] >> (8 * (__builtin_amdgcn_readlane(ts, 4 * tt) & 3));
+      v0 = fmaf(sv, float((byte >> vsh) & 3u), zv);
+      v1 = fmaf(sv, float((byte >> (vsh + 2)) & 3u), zv);
     }
 #pragma unroll
     for (int g = 0; g < GP; ++g) {

@@ -473,8 +473,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       }
     }
     wait_vmcnt<0>();     // drain DMA before the ring memory is reused
-    __builtin_amdgcn_s_setprio(0);
   }
+  // The epilogue, the partial store and the combine are short and end the
+  // piece: they run at the top priority so that streaming waves of other
+  // work-groups do not starve them.
+  __builtin_amdgcn_s_setprio(3);
   __syncthreads();   // the ring is idle from here on
 
   // ---- wave epilogue: per-head l, z and o' into LDS -----------------------
@@ -494,15 +497,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         float v = 0.f;
 #pragma unroll
         for (int r = g; r < 4; r += GP) v += cpv[J][r];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
+        v = xor32_sum(xor16_sum(v));
         if (gq == 0 && g < G) wo[wave][g][ch] = v * sc + z_h[g];
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = cpv[J][r];
-        v += __shfl_xor(v, 32);
+        const float v = xor32_sum(cpv[J][r]);
         const int g = 4 * (gq & 1) + r;
         const float zg = (gq & 1) ? z_h[4 + r] : z_h[r];
         if (gq < 2 && g < G) wo[wave][g][ch] = v * sc + zg;
@@ -522,6 +523,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
                         cmb_m, cmb_l);
 }
 
+// x / y for 0 <= x, 0 < y, in 32-bit arithmetic when both fit.
+__device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t y) {
+  if (((x | y) >> 31) == 0) return static_cast<int>(x) / static_cast<int>(y);
+  return x / y;
+}
+
 // Decode over equal tile ranges: the virtual tiles of all (b, h), in order,
 // W_b = max(1, INT2 tiles of sequence b) + piece_cost per (b, h), are cut
 // into gridDim.x equal contiguous ranges, one per work-group (one round of
@@ -534,28 +541,28 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
   const int i = blockIdx.x, nwg = gridDim.x;
   const int Hkv = a.n_kv_heads, B = a.batch;
   const int32_t* pre = a.tile_prefix;
-  const int total = Hkv * pre[B];
-  const int q = (total + nwg - 1) / nwg;
-  const int g0 = i * q, g1 = min(g0 + q, total);
+  const int64_t total = int64_t(Hkv) * pre[B];
+  const int64_t q = div_nonneg(total + nwg - 1, nwg);   // ranges [i q, i q + q); the last may be empty
+  const int64_t g0 = i * q, g1 = min(g0 + q, total);
   if (g0 >= g1) return;
   // sequence holding tile g0: the largest b with Hkv * pre[b] <= g0
   int lo = 0, hi = B;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (Hkv * pre[mid] <= g0) lo = mid; else hi = mid;
+    if (int64_t(Hkv) * pre[mid] <= g0) lo = mid; else hi = mid;
   }
   int b = lo;
   int wb = pre[b + 1] - pre[b];
-  int h = (g0 - Hkv * pre[b]) / wb;
+  int h = static_cast<int>(div_nonneg(g0 - int64_t(Hkv) * pre[b], wb));
   for (int first = 1;; first = 0) {
-    const int sp = Hkv * pre[b] + h * wb;        // first tile of (b, h)
+    const int64_t sp = int64_t(Hkv) * pre[b] + int64_t(h) * wb;   // first tile of (b, h)
     if (sp >= g1) break;
     if (!first) __syncthreads();   // the previous piece is done with every LDS buffer
     const int p = b * Hkv + h;
-    const int i0 = sp / q, i1 = (sp + wb - 1) / q;
+    const int i0 = static_cast<int>(div_nonneg(sp, q)), i1 = static_cast<int>(div_nonneg(sp + wb - 1, q));
     decode_item<GP>(a, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(h),
-                    max(g0, sp) - sp, min(g1, sp + wb) - sp, i1 - i0 + 1,
-                    int64_t(i) + p, int64_t(i0) + p);
+                    static_cast<int>(max(g0, sp) - sp), static_cast<int>(min(g1, sp + wb) - sp),
+                    i1 - i0 + 1, int64_t(i) + p, int64_t(i0) + p);
     if (++h == Hkv) {
       h = 0;
       if (++b == B) break;

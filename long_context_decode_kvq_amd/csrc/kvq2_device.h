@@ -71,6 +71,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
+// Butterfly sums across 16-lane rows (gfx950 row swaps): v_permlane16_swap
+// exchanges the odd rows of its first operand with the even rows of its
+// second, v_permlane32_swap the upper half of the first with the lower half
+// of the second.  With both operands equal to v the two registers then hold
+// v[i] and v[i ^ 16] (v[i ^ 32]) in row order, so both lanes of a pair add
+// them in the same order.  Written in assembly: the compiler's builtin
+// folded the two results of such a swap into one.  The s_nop covers the
+// wait states between the VALU writes of the operands and the swap.
+__device__ __forceinline__ float xor16_sum(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
+__device__ __forceinline__ float xor32_sum(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
 // Device-coherent global accesses for data handed between work-groups of one
 // launch (split partials, tickets, work counters).  The XCDs of the GPU have
 // separate L2 caches; a generic device-scope fence makes plain stores
