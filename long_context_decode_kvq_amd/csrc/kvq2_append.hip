@@ -102,20 +102,26 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
   const int W = a.n_recent;
   const int ns = a.n_sink;
   const int per_wave = a.tokens_per_block / kWaves;
+  // The token index is wave-uniform: the sequence lookup reads cu_new and
+  // start_pos through the scalar cache (a chain of vector loads would be the
+  // latency of a decode-step append).
+  typedef const int32_t __attribute__((address_space(4))) const_i32;
+  const_i32* cu_new = (const_i32*)a.cu_new;
+  const_i32* start_pos = (const_i32*)a.start_pos;
   for (int it = 0; it < per_wave; ++it) {
-    const int n = blockIdx.x * a.tokens_per_block + wave * per_wave + it;
+    const int n = __builtin_amdgcn_readfirstlane(blockIdx.x * a.tokens_per_block + wave * per_wave + it);
     if (n >= a.total_new) break;
     // Sequence of token n: the largest b with cu_new[b] <= n.
     int lo = 0, hi = a.batch;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (a.cu_new[mid] <= n) lo = mid; else hi = mid;
+      if (cu_new[mid] <= n) lo = mid; else hi = mid;
     }
     const int b = lo;
-    const int start = a.start_pos[b];
+    const int start = start_pos[b];
     if (start < 0) continue;   // invalid length: nothing is written
-    const int pos = start + (n - a.cu_new[b]);
-    const int end = start + (a.cu_new[b + 1] - a.cu_new[b]);
+    const int pos = start + (n - cu_new[b]);
+    const int end = start + (cu_new[b + 1] - cu_new[b]);
     const int64_t seq_head = int64_t(b) * a.n_kv_heads + h;
     const bool to_ring = pos >= ns && pos >= end - W;
 
@@ -193,9 +199,10 @@ int launch_quantize_append(const kvq_dims& d, float /*sm_scale*/, const kvq_laye
   a.total_new = total_new;
   a.x_new[0] = k_new;
   a.x_new[1] = v_new;
-  // Small (decode-step) appends: 16 tokens per work-group for parallelism;
-  // bulk appends: 256 so that each work-group stages R once per 256 vectors.
-  a.tokens_per_block = total_new <= 8192 ? 16 : 256;
+  // Decode-step appends (a few tokens per sequence): one token per wave, for
+  // parallelism; medium ones 16 per work-group; bulk appends 256, so that
+  // each work-group stages R once per 256 vectors.
+  a.tokens_per_block = total_new <= 1024 ? kWaves : total_new <= 8192 ? 16 : 256;
   dim3 grid((total_new + a.tokens_per_block - 1) / a.tokens_per_block, d.n_kv_heads, 2);
   hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
