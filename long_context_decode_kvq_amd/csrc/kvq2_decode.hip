@@ -188,6 +188,52 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
         if (tid == 255) carry += scan[255];
         __syncthreads();
       }
+      // The cut into chain_groups ranges (weighted by dispatch round when
+      // every range keeps at least a few tiles, else equal), then the first
+      // and last range of every (b, h).
+      __shared__ int rs[kChainGroups + 1];
+      const int nwg = a.chain_groups;
+      const int Hkv = a.n_kv_heads;
+      const int64_t total = int64_t(Hkv) * carry;
+      const int rsz = a.round_size, rounds = rsz > 0 ? nwg / rsz : 0;
+      const bool weighted = rsz > 0 && rounds >= 2 && rounds <= 4 && rounds * rsz == nwg &&
+                            total >= 4 * int64_t(nwg);
+      int64_t ctot = 0;
+      for (int r = 0; r < rounds; ++r) ctot += int64_t(a.round_weight[r]) * rsz;
+      const int64_t q = (total + nwg - 1) / nwg;
+      for (int i = tid; i <= nwg; i += blockDim.x) {
+        int64_t v;
+        if (!weighted) {
+          v = min(total, int64_t(i) * q);
+        } else {
+          int64_t c = 0;
+          for (int r = 0; r < rounds; ++r) {
+            const int64_t lo = int64_t(r) * rsz;
+            const int64_t cnt = i <= lo ? 0 : min(int64_t(i), lo + rsz) - lo;
+            c += int64_t(a.round_weight[r]) * cnt;
+          }
+          v = total * c / ctot;
+        }
+        rs[i] = static_cast<int>(v);
+        a.range_start[i] = static_cast<int>(v);
+      }
+      __syncthreads();
+      auto range_of = [&](int x) {   // largest i < nwg with rs[i] <= x
+        int lo = 0, hi = nwg;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (rs[mid] <= x) lo = mid; else hi = mid;
+        }
+        return lo;
+      };
+      for (int pr = tid; pr < a.batch * Hkv; pr += blockDim.x) {
+        const int bb = pr / Hkv, hh = pr % Hkv;
+        const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
+        const int wbb = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
+        // the prefix of bb, recomputed from the scan output in global memory
+        const int sp = Hkv * a.tile_prefix[bb] + hh * wbb;
+        a.pair_range[pr] = range_of(sp) | (range_of(sp + wbb - 1) << 16);
+      }
     }
   }
 }
@@ -195,6 +241,7 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
 }  // namespace
 
 int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
+void set_chain_geometry(DecodeArgs& a, int batch, int max_seq_len);
 int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* stream);
 
 int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
@@ -235,6 +282,13 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.qrot = reinterpret_cast<float*>(ws + plan.ticket_bytes);
   a.bq = reinterpret_cast<uint32_t*>(ws + plan.ticket_bytes + plan.qrot_bytes);
   a.tile_prefix = reinterpret_cast<int32_t*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes);
+  {
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* pre = reinterpret_cast<char*>(a.tile_prefix);
+    a.range_start = reinterpret_cast<int32_t*>(pre + r256((size_t(batch) + 1) * sizeof(int32_t)));
+    a.pair_range = reinterpret_cast<int32_t*>(pre + r256((size_t(batch) + 1) * sizeof(int32_t)) +
+                                              r256((size_t(kChainGroups) + 1) * sizeof(int32_t)));
+  }
   a.partials = reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes +
                                         plan.prefix_bytes);
   const int G = a.group;
@@ -247,6 +301,7 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.n_tok_slices = plan.n_tok_slices;
   a.tok_slot0 = plan.tok_slot0;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
   const dim3 pgrid(d.n_kv_heads, batch, std::max(1, a.n_tok_slices));
   if (a.gp == 2) hipLaunchKernelGGL(prologue_kernel<2>, pgrid, dim3(256), 0, st, a);
   else if (a.gp == 4) hipLaunchKernelGGL(prologue_kernel<4>, pgrid, dim3(256), 0, st, a);

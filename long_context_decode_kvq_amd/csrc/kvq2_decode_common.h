@@ -52,6 +52,17 @@ struct DecodeArgs {
   // tiles.
   int32_t* tile_prefix;
   int piece_cost;
+  // MFMA decode: the cut into chain_groups ranges, written by the pre-pass:
+  // range i is virtual tiles [range_start[i], range_start[i + 1]) (chain_groups
+  // + 1 entries), and pair_range[b Hkv + h] = i0 | i1 << 16, the first and
+  // last range that touch (b, h).  Ranges are sized by round_weight (1/1024
+  // units) of the work-group's dispatch round i / round_size: the work-groups
+  // of one CU stream at different rates by dispatch order.
+  int32_t* range_start;
+  int32_t* pair_range;
+  int chain_groups;
+  int round_size;
+  int round_weight[4];
   // MFMA decode: the token-by-token list of (b, h) is cut into n_tok_slices
   // slices of 64 tokens; the pre-pass leaves the partial of slice z in slot
   // tok_slot0 + (b Hkv + h) n_tok_slices + z, and the combine takes them in.

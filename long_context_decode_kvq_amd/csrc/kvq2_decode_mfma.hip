@@ -28,6 +28,8 @@
 // max is updated lazily: a tile is rescaled only when a logit exceeds the
 // running max by more than 8 (base-2 units), so p <= 256.
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <type_traits>
 
 #include "kvq2_decode_common.h"
@@ -523,12 +525,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
                         cmb_m, cmb_l);
 }
 
-// x / y for 0 <= x, 0 < y, in 32-bit arithmetic when both fit.
-__device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t y) {
-  if (((x | y) >> 31) == 0) return static_cast<int>(x) / static_cast<int>(y);
-  return x / y;
-}
-
 // Decode over equal tile ranges: the virtual tiles of all (b, h), in order,
 // W_b = max(1, INT2 tiles of sequence b) + piece_cost per (b, h), are cut
 // into gridDim.x equal contiguous ranges, one per work-group (one round of
@@ -538,31 +534,30 @@ __device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t y) {
 // so the slots are unique and those of one pair are contiguous.
 template <int GP>
 __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
-  const int i = blockIdx.x, nwg = gridDim.x;
+  const int i = blockIdx.x;
   const int Hkv = a.n_kv_heads, B = a.batch;
   const int32_t* pre = a.tile_prefix;
-  const int64_t total = int64_t(Hkv) * pre[B];
-  const int64_t q = div_nonneg(total + nwg - 1, nwg);   // ranges [i q, i q + q); the last may be empty
-  const int64_t g0 = i * q, g1 = min(g0 + q, total);
+  const int g0 = a.range_start[i], g1 = a.range_start[i + 1];
   if (g0 >= g1) return;
   // sequence holding tile g0: the largest b with Hkv * pre[b] <= g0
   int lo = 0, hi = B;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (int64_t(Hkv) * pre[mid] <= g0) lo = mid; else hi = mid;
+    if (Hkv * pre[mid] <= g0) lo = mid; else hi = mid;
   }
   int b = lo;
   int wb = pre[b + 1] - pre[b];
-  int h = static_cast<int>(div_nonneg(g0 - int64_t(Hkv) * pre[b], wb));
+  int h = (g0 - Hkv * pre[b]) / wb;
   for (int first = 1;; first = 0) {
-    const int64_t sp = int64_t(Hkv) * pre[b] + int64_t(h) * wb;   // first tile of (b, h)
+    const int sp = Hkv * pre[b] + h * wb;   // first tile of (b, h)
     if (sp >= g1) break;
     if (!first) __syncthreads();   // the previous piece is done with every LDS buffer
     const int p = b * Hkv + h;
-    const int i0 = static_cast<int>(div_nonneg(sp, q)), i1 = static_cast<int>(div_nonneg(sp + wb - 1, q));
+    const int pr = a.pair_range[p];
+    const int i0 = pr & 0xFFFF, i1 = pr >> 16;
     decode_item<GP>(a, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(h),
-                    static_cast<int>(max(g0, sp) - sp), static_cast<int>(min(g1, sp + wb) - sp),
-                    i1 - i0 + 1, int64_t(i) + p, int64_t(i0) + p);
+                    max(g0, sp) - sp, min(g1, sp + wb) - sp, i1 - i0 + 1, int64_t(i) + p,
+                    int64_t(i0) + p);
     if (++h == Hkv) {
       h = 0;
       if (++b == B) break;
@@ -603,32 +598,61 @@ int resident_work_groups() {
 // Work-groups of the equal-range decode: one round of resident work-groups,
 // but no more than one per kMinTilesPerGroup tiles (bounded above from
 // max_seq_len), so that short or few sequences are not cut into pieces whose
-// fixed cost (prologue, token tiles, partial, combine) dominates.
+// fixed cost (prologue, partial, combine) dominates.
 constexpr int kMinTilesPerGroup = 128;
 
 template <int GP>
-int launch_chain(const DecodeArgs& a, int batch, int max_seq_len, hipStream_t st) {
+int chain_grid(const DecodeArgs& a, int batch, int max_seq_len) {
   constexpr int NPT = Geo<GP>::NPT;
   const int64_t int2_end = std::max<int64_t>(a.n_sink, int64_t(max_seq_len) - a.n_recent);
   const int64_t tiles = std::max<int64_t>(1, (int2_end / kChunkTokens) / NPT);
   const int64_t est = int64_t(batch) * a.n_kv_heads * tiles;
   const int64_t want = (est + kMinTilesPerGroup - 1) / kMinTilesPerGroup;
-  const int grid = int(std::max<int64_t>(
+  return int(std::max<int64_t>(
       1, std::min<int64_t>(want, std::min(kChainGroups, resident_work_groups<GP>()))));
-  hipLaunchKernelGGL(decode_mfma_kernel<GP>, dim3(grid), dim3(256), 0, st, a);
-  return static_cast<int>(hipGetLastError());
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
 }
 
 }  // namespace
+
+// Grid and range weights of the MFMA decode (before the pre-pass, which
+// writes the cut).  Measured on the 28 x 100000-token batch with four
+// resident work-groups per CU, equal ranges stream at 2.88, 2.68, 2.45 and
+// 2.31 tiles/us from the first to the fourth dispatched; weights a little
+// steeper than those rates gave the shortest launch there (the gap narrows
+// as the ranges shift).  KVQ_ROUND_WEIGHTS="w0,w1,w2,w3" (1/1024 units)
+// overrides them.
+void set_chain_geometry(DecodeArgs& a, int batch, int max_seq_len) {
+  const int G = a.group;
+  a.chain_groups = G <= 2 ? chain_grid<2>(a, batch, max_seq_len)
+                 : G <= 4 ? chain_grid<4>(a, batch, max_seq_len)
+                          : chain_grid<8>(a, batch, max_seq_len);
+  a.round_size = device_cus();
+  int w[4] = {1200, 1090, 950, 860};
+  if (G > 4) { w[0] = w[1] = w[2] = w[3] = 1024; }
+  if (const char* s = std::getenv("KVQ_ROUND_WEIGHTS"))
+    std::sscanf(s, "%d,%d,%d,%d", &w[0], &w[1], &w[2], &w[3]);
+  for (int r = 0; r < 4; ++r) a.round_weight[r] = std::max(1, w[r]);
+}
 
 int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* stream) {
   const int G = a.group;
   if (G > 8) return launch_decode_valu(a, batch, stream);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)batch;
+  (void)max_seq_len;
   // G = 1 runs the two-head kernel with one padding head.
-  if (G <= 2) return launch_chain<2>(a, batch, max_seq_len, st);
-  if (G <= 4) return launch_chain<4>(a, batch, max_seq_len, st);
-  return launch_chain<8>(a, batch, max_seq_len, st);
+  if (G <= 2) hipLaunchKernelGGL(decode_mfma_kernel<2>, dim3(a.chain_groups), dim3(256), 0, st, a);
+  else if (G <= 4) hipLaunchKernelGGL(decode_mfma_kernel<4>, dim3(a.chain_groups), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(decode_mfma_kernel<8>, dim3(a.chain_groups), dim3(256), 0, st, a);
+  return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace kvq

@@ -104,7 +104,11 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   p.ticket_bytes = ((size_t(heads + 2) * sizeof(int32_t) + 255) / 256) * 256;
   p.qrot_bytes = size_t(batch) * d.n_q_heads * kQStride * sizeof(float);
   p.bq_bytes = size_t(heads) * kBqWords * sizeof(uint32_t);
-  p.prefix_bytes = ((size_t(batch) + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  // tile prefix [B + 1], range starts [kChainGroups + 1], pair ranges [B Hkv]
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.prefix_bytes = r256((size_t(batch) + 1) * sizeof(int32_t)) +
+                   r256((size_t(kChainGroups) + 1) * sizeof(int32_t)) +
+                   r256(size_t(heads) * sizeof(int32_t));
   // The MFMA decode cuts all (b, h) tiles into at most kChainGroups equal
   // ranges: a work-group leaves one partial per (b, h) it touches, in slot
   // group + b * Hkv + h (unique: the (group, pair) overlaps form a monotone
@@ -186,6 +190,10 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq
   if (batch < 1 || max_seq_len < 0 || seq_len == nullptr) return KVQ_ERR_ARG;
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
   if (int64_t(max_seq_len) > int64_t(cache->bt_stride) * dims->page_size) return KVQ_ERR_ARG;
+  // The MFMA decode counts virtual tiles of the whole batch in 32 bits.
+  if (int64_t(batch) * dims->n_kv_heads * (int64_t(max_seq_len) / kChunkTokens + kPieceCostChunks + 2) >=
+      (int64_t(1) << 31))
+    return KVQ_ERR_UNSUPPORTED;
   const DecodePlan plan = make_decode_plan(*dims, batch, max_seq_len);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan.total_bytes)
     return KVQ_ERR_WORKSPACE;
