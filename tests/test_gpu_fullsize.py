@@ -1,0 +1,105 @@
+"""GPU parity at the full workload sizes, on sampled (sequence, KV head) pairs.
+
+Each workload's whole cache is built on the GPU by bulk quantize-append from
+its seeded tokens, with the rotations and clip thresholds of the oracle's
+calibration, and decoded once in the launch configuration bench.py times.
+For a few sampled pairs the oracle builds the pair's cache by itself from the
+same seeded tokens (fp64 rotation, its own quantizer and packing), decodes the
+pair's query heads and the outputs are compared row by row (max normwise
+relative error <= 2e-3).  Nothing the GPU produced enters the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import TOL, rel_err, say
+from long_context_decode_kvq_amd import kvq2
+from long_context_decode_kvq_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+HEAD_DIM = 128
+CHUNK = 8192        # tokens per sequence per bulk append call
+
+
+def gpu_cache(w, cal, lens):
+    """The whole workload's cache on the GPU (bulk appends), oracle rotations."""
+    dev = torch.device("cuda")
+    kd = kvq2.dims(w.n_q_heads, w.n_kv_heads, w.page_size, w.n_sink, w.n_recent)
+    bt, n_pages, _ = W.page_assignment(w, lens)
+    dc = kvq2.DeviceCache(kd, w.batch, n_pages, bt, device=dev)
+    keep = (torch.from_numpy(cal.R_K).to(dev), torch.from_numpy(cal.R_V).to(dev))
+    lay = kvq2.layer(keep[0], keep[1], float(cal.clip_K), float(cal.clip_V))
+    done = np.zeros(w.batch, np.int64)
+    while True:
+        todo = np.minimum(lens - done, CHUNK)
+        if todo.sum() == 0:
+            break
+        ks, vs = [], []
+        for b in range(w.batch):
+            if todo[b]:
+                k, v = W.sequence_kv_device(w, b, int(done[b]), int(todo[b]), dev)
+                ks.append(k)
+                vs.append(v)
+        cu = np.zeros(w.batch + 1, np.int32)
+        cu[1:] = np.cumsum(todo)
+        kvq2.quantize_append(kd, lay, dc.handle, w.batch,
+                             torch.from_numpy(done.astype(np.int32)).to(dev),
+                             torch.from_numpy(cu).to(dev), int(cu[-1]), int(todo.max()),
+                             torch.cat(ks), torch.cat(vs))
+        done += todo
+    torch.cuda.synchronize()
+    return kd, dc, lay, keep
+
+
+def oracle_pair(w, cal, b, h, L, q_bits):
+    """Oracle decode of the G query heads of (b, h) from its own cache."""
+    G = w.group
+    od = O.Dims(G, 1, w.page_size, w.n_sink, w.n_recent)
+    npg = math.ceil(L / w.page_size)
+    oc = O.OracleCache(od, 1, npg, np.arange(npg, dtype=np.int32)[None])
+    k, v = W.sequence_kv_device(w, b, 0, L, "cuda")
+    k = k[:, h:h + 1].cpu().numpy().view(np.uint16)
+    v = v[:, h:h + 1].cpu().numpy().view(np.uint16)
+    R_K, R_V = cal.R_K[h:h + 1], cal.R_V[h:h + 1]
+    oc.append(R_K, R_V, cal.clip_K, cal.clip_V, 0, 0, k, v)
+    return oc.decode(R_K, R_V, [L], q_bits[None, h * G:(h + 1) * G])[0]
+
+
+# (workload, sampled pairs); pairs cover the first and last sequence and KV head
+CASES = [
+    ("conc_28x100k", [(0, 0), (27, 7)]),
+    ("b1_131k", [(0, 3)]),
+    ("qwen3_8b_32k", [(0, 5)]),
+    ("qwen3_32b", [(0, 0), (63, 7)]),     # G = 8; sequence 0 shares its prefix pages
+]
+
+
+@pytest.mark.parametrize("name,pairs", CASES, ids=[c[0] for c in CASES])
+def test_fullsize_sampled_pairs(name, pairs):
+    w = W.WORKLOADS[name]
+    say(f"[fullsize] {name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} P={w.page_size}")
+    lens = w.seq_lens().astype(np.int64)
+    q_c, k_c, v_c = W.calibration_tokens(w)
+    cal = O.calibrate(q_c, k_c, v_c, w.n_q_heads, w.n_kv_heads, 1 / math.sqrt(HEAD_DIM), 0.999)
+    kd, dc, lay, keep = gpu_cache(w, cal, lens)
+    max_len = int(lens.max())
+    ws = torch.zeros(kvq2.decode_workspace_bytes(kd, w.batch, max_len), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device="cuda")
+    seq = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = W.decode_queries_device(w, 0)
+    kvq2.decode_attention(kd, lay, dc.handle, w.batch, seq, max_len, q, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    q_bits = q.cpu().numpy().view(np.uint16)
+    G = w.group
+    for b, h in pairs:
+        ref = oracle_pair(w, cal, b, h, int(lens[b]), q_bits[b])
+        e = rel_err(got[b, h * G:(h + 1) * G], ref)
+        say(f"  pair (b={b}, h={h}) len={int(lens[b])}: rel_err={e:.3e}")
+        assert e <= TOL, (name, b, h, e)
