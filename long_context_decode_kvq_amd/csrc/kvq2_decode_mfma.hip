@@ -39,6 +39,7 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));   // cvt_pkrtz result
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -239,6 +240,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   const_i32* bt_row = (const_i32*)(a.block_table + int64_t(b) * a.bt_stride);
   const int cpp_mask = (1 << a.log2_cpp) - 1;
   const int64_t head_off = int64_t(h) * (cpp_mask + 1) * kChunkBytes;
+  // page numbers are int32: a 32-bit bound keeps the check on the scalar unit
+  const int32_t num_pages32 = static_cast<int32_t>(min(a.num_pages, int64_t(INT32_MAX)));
   struct Pages { int32_t pg[NPT]; };
   auto fetch_pages = [&](int tile, Pages& P) {
 #pragma unroll
@@ -255,7 +258,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     for (int p = 0; p < NPT; ++p) {
       const int c = c_begin + tile * NPT + p;
       const int32_t page = P.pg[p];
-      off[p] = (page >= 0 && page < a.num_pages)
+      off[p] = (page >= 0 && page < num_pages32)
                    ? int64_t(page) * a.page_bytes + head_off + int64_t(c & cpp_mask) * kChunkBytes
                    : int64_t(0);
     }
@@ -355,7 +358,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     }
     // lazy running max
     float tmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    if (__any(is_hi && g_ok && tmax > thr)) {
+    if (__builtin_amdgcn_ballot_w64(is_hi && g_ok && tmax > thr) != 0) {
       const float tm = (is_hi && g_ok) ? tmax * qscale : -INFINITY;
       float corr[GP];
 #pragma unroll
@@ -393,12 +396,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       z_lane = fmaf(p, zv[r], z_lane);
       w[r] = p * f16lo(svb[r]);
     }
-    // f16 hi/lo split of w; lo parts move GP lanes up (row_shr) into the lo rows
-    const _Float16 h0 = static_cast<_Float16>(w[0]), h1 = static_cast<_Float16>(w[1]);
-    const _Float16 h2 = static_cast<_Float16>(w[2]), h3 = static_cast<_Float16>(w[3]);
-    const uint32_t hi02 = pack_f16(float(h0), float(h2)), hi13 = pack_f16(float(h1), float(h3));
-    const uint32_t lo02 = pack_f16(w[0] - float(h0), w[2] - float(h2));
-    const uint32_t lo13 = pack_f16(w[1] - float(h1), w[3] - float(h3));
+    // f16 hi/lo split of w (each part packed two per dword, rounded toward
+    // zero: lo = w - hi carries the remainder, so hi + lo is w to ~2^-20);
+    // lo parts move GP lanes up (row_shr) into the lo rows
+    const fp16x2_t h02 = __builtin_amdgcn_cvt_pkrtz(w[0], w[2]);
+    const fp16x2_t h13 = __builtin_amdgcn_cvt_pkrtz(w[1], w[3]);
+    const uint32_t hi02 = __builtin_bit_cast(uint32_t, h02), hi13 = __builtin_bit_cast(uint32_t, h13);
+    const uint32_t lo02 = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0] - float(h02[0]), w[2] - float(h02[1])));
+    const uint32_t lo13 = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_pkrtz(w[1] - float(h13[0]), w[3] - float(h13[1])));
     const uint32_t lo02s = dpp_u<0x110 + GP>(lo02), lo13s = dpp_u<0x110 + GP>(lo13);
     const uint32_t av0 = is_hi ? hi02 : lo02s;
     const uint32_t av1 = is_hi ? hi13 : lo13s;

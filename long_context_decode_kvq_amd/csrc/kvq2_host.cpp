@@ -122,7 +122,8 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
     const int64_t max_list = int64_t(d.n_sink) + 15 + (16 * npt - 1) + d.n_recent;
     p.n_tok_slices = static_cast<int>((max_list + 63) / 64);
     p.tok_slot0 = int64_t(kChainGroups) + heads;
-    p.piece_cost = std::max(0, env_int("KVQ_PIECE_COST", kPieceCostChunks)) / npt;
+    p.piece_cost =
+        std::max(0, env_int("KVQ_PIECE_COST", gp == 8 ? kPieceCostChunksG8 : kPieceCostChunks)) / npt;
   }
   const size_t slots = own_token_item
                            ? size_t(heads) * p.n_split
@@ -191,7 +192,7 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
   if (int64_t(max_seq_len) > int64_t(cache->bt_stride) * dims->page_size) return KVQ_ERR_ARG;
   // The MFMA decode counts virtual tiles of the whole batch in 32 bits.
-  if (int64_t(batch) * dims->n_kv_heads * (int64_t(max_seq_len) / kChunkTokens + kPieceCostChunks + 2) >=
+  if (int64_t(batch) * dims->n_kv_heads * (int64_t(max_seq_len) / kChunkTokens + kPieceCostChunksG8 + 2) >=
       (int64_t(1) << 31))
     return KVQ_ERR_UNSUPPORTED;
   const DecodePlan plan = make_decode_plan(*dims, batch, max_seq_len);

@@ -104,6 +104,15 @@ def test_validation_pointer_and_size_errors():
     assert _decode(d, lay2, cch) == ERR_ARG
 
 
+def test_decode_rejects_batches_beyond_32bit_tile_counts():
+    # 1024 sequences x 8 KV heads x 4M tokens: the batch's tile count does
+    # not fit the decode's 32-bit counters; refused before any launch.
+    L = 1 << 22
+    d, lay, cch = _args(bt_stride=L // 16)
+    assert _decode(d, lay, cch, batch=1024, max_len=L) == ERR_UNSUP
+    assert _decode(d, lay, cch, batch=1024, max_len=L, ws=0) == ERR_UNSUP
+
+
 def test_workspace_bytes_grow_with_batch_and_length():
     d = kvq2.dims(32, 8, 16, 4, 256)
     f = lambda b, n: _lib().kvq_decode_workspace_bytes(C.byref(d), b, n)
