@@ -10,6 +10,86 @@ namespace kvq {
 
 namespace {
 
+// The equal-range plan of the MFMA decode, by one work-group of 256 threads.
+template <int GP>
+__device__ void plan_ranges(const DecodeArgs& a) {
+  constexpr int npt = 16 / (2 * GP);
+  const int tid = threadIdx.x;
+  // W_b = max(1, whole INT2 tiles of sequence b) + piece_cost;
+  // tile_prefix[b] = W_0 + ... + W_{b-1} (inclusive Hillis-Steele scan
+  // over blocks of 256 sequences).
+  __shared__ int scan[256];
+  __shared__ int carry;
+  if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
+  __syncthreads();
+  for (int base = 0; base < a.batch; base += 256) {
+    const int bb = base + tid;
+    int w = 0;
+    if (bb < a.batch) {
+      const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
+      w = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
+    }
+    scan[tid] = w;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int v = tid >= d ? scan[tid - d] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    if (bb < a.batch) a.tile_prefix[bb + 1] = carry + scan[tid];
+    __syncthreads();
+    if (tid == 255) carry += scan[255];
+    __syncthreads();
+  }
+  // The cut into chain_groups ranges (weighted by dispatch round when
+  // every range keeps at least a few tiles, else equal), then the first
+  // and last range of every (b, h).
+  __shared__ int rs[kChainGroups + 1];
+  const int nwg = a.chain_groups;
+  const int Hkv = a.n_kv_heads;
+  const int64_t total = int64_t(Hkv) * carry;
+  const int rsz = a.round_size, rounds = rsz > 0 ? nwg / rsz : 0;
+  const bool weighted = rsz > 0 && rounds >= 2 && rounds <= 4 && rounds * rsz == nwg &&
+                        total >= 4 * int64_t(nwg);
+  int64_t ctot = 0;
+  for (int r = 0; r < rounds; ++r) ctot += int64_t(a.round_weight[r]) * rsz;
+  const int64_t q = (total + nwg - 1) / nwg;
+  for (int i = tid; i <= nwg; i += blockDim.x) {
+    int64_t v;
+    if (!weighted) {
+      v = min(total, int64_t(i) * q);
+    } else {
+      int64_t c = 0;
+      for (int r = 0; r < rounds; ++r) {
+        const int64_t lo = int64_t(r) * rsz;
+        const int64_t cnt = i <= lo ? 0 : min(int64_t(i), lo + rsz) - lo;
+        c += int64_t(a.round_weight[r]) * cnt;
+      }
+      v = total * c / ctot;
+    }
+    rs[i] = static_cast<int>(v);
+    a.range_start[i] = static_cast<int>(v);
+  }
+  __syncthreads();
+  auto range_of = [&](int x) {   // largest i < nwg with rs[i] <= x
+    int lo = 0, hi = nwg;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (rs[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  for (int pr = tid; pr < a.batch * Hkv; pr += blockDim.x) {
+    const int bb = pr / Hkv, hh = pr % Hkv;
+    const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
+    const int wbb = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
+    // the prefix of bb, recomputed from the scan output in global memory
+    const int sp = Hkv * a.tile_prefix[bb] + hh * wbb;
+    a.pair_range[pr] = range_of(sp) | (range_of(sp + wbb - 1) << 16);
+  }
+}
+
 // Pre-pass of the decode, one work-group per (KV head h, sequence b, token
 // slice z):
 //  * q'[g] = alpha R_K[h]^T q[b][hG+g] (OSCAR summary sec. 2.2-B: the query
@@ -20,14 +100,21 @@ namespace {
 //    (b, h), one 16-token tile per wave, merged into one partial in slot
 //    tok_slot0 + (b Hkv + h) n_tok_slices + z.  These scattered small reads
 //    run here, before the streaming decode, where their latency is short;
-//  * MFMA decode, work-group (0, 0, 0): the tile prefix of the equal-range
-//    decode.
+//  * MFMA decode: one more work-group, (Hkv, 0, 0), computes the plan of the
+//    equal-range decode alongside the others (the rest of column Hkv exits
+//    at once).
 // GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.  At most
 // 96 VGPRs (five work-groups per CU) so that the slices of a long batch are
 // resident together.
 template <int GP>
 __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
   constexpr int KG = GP > 0 ? GP : kMaxGroup;   // query heads per KV head held
+  if constexpr (GP > 0) {
+    if (static_cast<int>(blockIdx.x) == a.n_kv_heads) {
+      if (blockIdx.y == 0 && blockIdx.z == 0) plan_ranges<GP>(a);
+      return;
+    }
+  }
   __shared__ float qs[KG][kHeadDim];             // q, then q'
   // rotation half sums [2][KG][128]; then the waves' o' of the token slice
   __shared__ float buf[(GP > 0 ? 4 * GP : 2 * kMaxGroup) * kHeadDim];
@@ -160,81 +247,6 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
       float* out = a.partials + (a.tok_slot0 + head * a.n_tok_slices + z) * G * kPartialStride;
       for (int i = tid; i < G * kPartialStride; i += blockDim.x) out[i] = stage[i];
     }
-    if (h == 0 && b == 0 && z == 0) {
-      // W_b = max(1, whole INT2 tiles of sequence b) + piece_cost;
-      // tile_prefix[b] = W_0 + ... + W_{b-1} (inclusive Hillis-Steele scan
-      // over blocks of 256 sequences).
-      __shared__ int scan[256];
-      __shared__ int carry;
-      if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
-      __syncthreads();
-      for (int base = 0; base < a.batch; base += 256) {
-        const int bb = base + tid;
-        int w = 0;
-        if (bb < a.batch) {
-          const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
-          w = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
-        }
-        scan[tid] = w;
-        __syncthreads();
-        for (int d = 1; d < 256; d <<= 1) {
-          const int v = tid >= d ? scan[tid - d] : 0;
-          __syncthreads();
-          scan[tid] += v;
-          __syncthreads();
-        }
-        if (bb < a.batch) a.tile_prefix[bb + 1] = carry + scan[tid];
-        __syncthreads();
-        if (tid == 255) carry += scan[255];
-        __syncthreads();
-      }
-      // The cut into chain_groups ranges (weighted by dispatch round when
-      // every range keeps at least a few tiles, else equal), then the first
-      // and last range of every (b, h).
-      __shared__ int rs[kChainGroups + 1];
-      const int nwg = a.chain_groups;
-      const int Hkv = a.n_kv_heads;
-      const int64_t total = int64_t(Hkv) * carry;
-      const int rsz = a.round_size, rounds = rsz > 0 ? nwg / rsz : 0;
-      const bool weighted = rsz > 0 && rounds >= 2 && rounds <= 4 && rounds * rsz == nwg &&
-                            total >= 4 * int64_t(nwg);
-      int64_t ctot = 0;
-      for (int r = 0; r < rounds; ++r) ctot += int64_t(a.round_weight[r]) * rsz;
-      const int64_t q = (total + nwg - 1) / nwg;
-      for (int i = tid; i <= nwg; i += blockDim.x) {
-        int64_t v;
-        if (!weighted) {
-          v = min(total, int64_t(i) * q);
-        } else {
-          int64_t c = 0;
-          for (int r = 0; r < rounds; ++r) {
-            const int64_t lo = int64_t(r) * rsz;
-            const int64_t cnt = i <= lo ? 0 : min(int64_t(i), lo + rsz) - lo;
-            c += int64_t(a.round_weight[r]) * cnt;
-          }
-          v = total * c / ctot;
-        }
-        rs[i] = static_cast<int>(v);
-        a.range_start[i] = static_cast<int>(v);
-      }
-      __syncthreads();
-      auto range_of = [&](int x) {   // largest i < nwg with rs[i] <= x
-        int lo = 0, hi = nwg;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (rs[mid] <= x) lo = mid; else hi = mid;
-        }
-        return lo;
-      };
-      for (int pr = tid; pr < a.batch * Hkv; pr += blockDim.x) {
-        const int bb = pr / Hkv, hh = pr % Hkv;
-        const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
-        const int wbb = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
-        // the prefix of bb, recomputed from the scan output in global memory
-        const int sp = Hkv * a.tile_prefix[bb] + hh * wbb;
-        a.pair_range[pr] = range_of(sp) | (range_of(sp + wbb - 1) << 16);
-      }
-    }
   }
 }
 
@@ -302,7 +314,7 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.tok_slot0 = plan.tok_slot0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
-  const dim3 pgrid(d.n_kv_heads, batch, std::max(1, a.n_tok_slices));
+  const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch, std::max(1, a.n_tok_slices));
   if (a.gp == 2) hipLaunchKernelGGL(prologue_kernel<2>, pgrid, dim3(256), 0, st, a);
   else if (a.gp == 4) hipLaunchKernelGGL(prologue_kernel<4>, pgrid, dim3(256), 0, st, a);
   else if (a.gp == 8) hipLaunchKernelGGL(prologue_kernel<8>, pgrid, dim3(256), 0, st, a);

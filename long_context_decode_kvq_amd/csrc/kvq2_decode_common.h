@@ -412,6 +412,147 @@ __device__ void merge_wave_states(int G, const float (*wm)[GP], const float (*wl
   __syncthreads();
 }
 
+// Merge the 4 waves' states (as merge_wave_states) straight into the
+// work-group's partial `part` in the workspace: (M, l, 2 pad, o'[128]) per
+// head, plain stores (read by a later kernel).  The LDS inputs stay intact.
+template <int GP>
+__device__ void store_partial(int G, const float (*wm)[GP], const float (*wl)[GP],
+                              const float (*wo)[GP][kHeadDim], float* part) {
+  const int tid = threadIdx.x;
+  constexpr int K = (GP * kHeadDim + 255) / 256;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int i = tid + 256 * k;
+    if (i < G * kHeadDim) {
+      const int g = i / kHeadDim, c = i % kHeadDim;
+      float M = -INFINITY;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][g]);
+      float o = 0.0f, l = 0.0f;
+      if (M != -INFINITY) {
+        for (int w = 0; w < 4; ++w) {
+          const float f = exp2f(wm[w][g] - M);
+          o += f * wo[w][g][c];
+          l += f * wl[w][g];
+        }
+      }
+      part[g * kPartialStride + 4 + c] = o;
+      if (c == 0) {
+        part[g * kPartialStride + 0] = M;
+        part[g * kPartialStride + 1] = l;
+      }
+    }
+  }
+}
+
+// Split-K combine of one (b, h), by a work-group of 256 threads in a kernel
+// of its own: the partials in slots [base_slot, base_slot + n_parts) and
+// [tok_slot, tok_slot + n_tok), with M = max m_s, f_s = 2^(m_s - M):
+// o' = sum f_s o'_s / sum f_s l_s, then o = R_V o' to `out`.  The slots are
+// taken in slices of kSlice, all loads of a slice in flight together (the
+// running M, l and o' are rescaled between slices); R_V is loaded first.
+template <int GP>
+__device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slot, int n_parts,
+                             int64_t tok_slot, int n_tok) {
+  constexpr int kSlice = 16;
+  constexpr int KO = (GP * kHeadDim + 255) / 256;   // outputs per thread
+  __shared__ float s_ml[kSlice][GP][2];
+  __shared__ float ocomb[GP][kHeadDim];
+  __shared__ float red[2][GP][kHeadDim];
+  const int G = a.group;
+  const int tid = threadIdx.x;
+  const int ri = tid & (kHeadDim - 1), half = tid >> 7;
+  float4 r[16];
+  {
+    const float4* row = reinterpret_cast<const float4*>(
+        a.R_V + int64_t(h) * kHeadDim * kHeadDim + ri * kHeadDim + 64 * half);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = row[j];
+  }
+  auto slot_ptr = [&](int i) -> const float* {
+    const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    return a.partials + s * G * kPartialStride;
+  };
+  int gk[KO], ck[KO];
+  float M[KO], den[KO], acc[KO];
+#pragma unroll
+  for (int k = 0; k < KO; ++k) {
+    const int o = tid + 256 * k;
+    gk[k] = min(o / kHeadDim, G - 1);   // rows past G load head G - 1 and are not stored
+    ck[k] = o % kHeadDim;
+    M[k] = -INFINITY;
+    den[k] = 0.f;
+    acc[k] = 0.f;
+  }
+  const int n_all = n_parts + n_tok;
+  for (int s0 = 0; s0 < n_all; s0 += kSlice) {
+    const int ns = min(kSlice, n_all - s0);
+    if (tid < ns * G) {
+      const float* p = slot_ptr(s0 + tid / G) + (tid % G) * kPartialStride;
+      s_ml[tid / G][tid % G][0] = p[0];
+      s_ml[tid / G][tid % G][1] = p[1];
+    }
+    float ov[kSlice][KO];
+#pragma unroll
+    for (int i = 0; i < kSlice; ++i) {
+      const float* p = slot_ptr(s0 + min(i, ns - 1));   // past the slice: re-read, unused
+#pragma unroll
+      for (int k = 0; k < KO; ++k) ov[i][k] = p[gk[k] * kPartialStride + 4 + ck[k]];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KO; ++k) {
+      const int g = gk[k];
+      float mx = -INFINITY;
+      for (int i = 0; i < ns; ++i) mx = fmaxf(mx, s_ml[i][g][0]);
+      const float nM = fmaxf(M[k], mx);
+      if (nM != -INFINITY) {
+        const float sc = M[k] == -INFINITY ? 0.f : exp2f(M[k] - nM);
+        acc[k] *= sc;
+        den[k] *= sc;
+#pragma unroll
+        for (int i = 0; i < kSlice; ++i) {
+          if (i < ns) {
+            const float mi = s_ml[i][g][0];
+            const float f = mi == -INFINITY ? 0.f : exp2f(mi - nM);
+            acc[k] = fmaf(f, ov[i][k], acc[k]);
+            den[k] = fmaf(f, s_ml[i][g][1], den[k]);
+          }
+        }
+        M[k] = nM;
+      }
+    }
+    __syncthreads();   // s_ml is refilled by the next slice
+  }
+#pragma unroll
+  for (int k = 0; k < KO; ++k) {
+    const int o = tid + 256 * k;
+    if (o < G * kHeadDim) ocomb[gk[k]][ck[k]] = den[k] > 0.f ? acc[k] / den[k] : 0.f;
+  }
+  __syncthreads();
+  // o = R_V o' (row-major R_V: o_i = sum_j R_V[i][j] o'_j); thread (half, i)
+  // holds half of row i and applies it to every head; the halves meet in LDS.
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (g < G) {
+      const float* oc = &ocomb[g][64 * half];
+      float o = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        o = fmaf(r[j].x, oc[4 * j + 0], o);
+        o = fmaf(r[j].y, oc[4 * j + 1], o);
+        o = fmaf(r[j].z, oc[4 * j + 2], o);
+        o = fmaf(r[j].w, oc[4 * j + 3], o);
+      }
+      red[half][g][ri] = o;
+    }
+  }
+  __syncthreads();
+  for (int k = tid; k < G * kHeadDim; k += blockDim.x) {
+    const int g = k / kHeadDim, c = k % kHeadDim;
+    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] = red[0][g][c] + red[1][g][c];
+  }
+}
+
 // Merge the 4 waves' states (see merge_wave_states) and store the
 // work-group's partial in slot `part_slot` of the workspace.  Then take an
 // arrival ticket of (b, h); the last of its n_parts work-groups combines the

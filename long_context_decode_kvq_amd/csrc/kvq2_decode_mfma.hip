@@ -57,6 +57,14 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
       __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, true));
 }
 
+// a if sel (all ones) else b, as bit operations: the compiler turns a
+// lane-dependent choice between two array elements into an indexed private
+// array otherwise.
+__device__ __forceinline__ float select_bits(uint32_t sel, float a, float b) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, a) & sel) |
+                                       (__builtin_bit_cast(uint32_t, b) & ~sel));
+}
+
 __device__ __forceinline__ float f16lo(uint32_t v) { return f16_bits_to_float(v & 0xFFFFu); }
 __device__ __forceinline__ float f16hi(uint32_t v) { return f16_bits_to_float(v >> 16); }
 
@@ -142,28 +150,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // One piece of (b, h): the INT2 tiles [t_lo, t_hi) of its range of W_b
 // virtual tiles (the first piece_cost of them stand for no tile; the rest
 // are clipped to the tiles the sequence has).  Leaves its partial in slot
-// part_slot; the last of the n_pieces pieces of (b, h) to finish combines
-// slots [base_slot, base_slot + n_pieces) and the token-list slices that the
-// pre-pass left, and writes `out`.
+// part_slot for the combine kernel.
 template <int GP>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, const int h,
-                                            const int t_lo, const int t_hi, const int n_pieces,
-                                            const int64_t part_slot,
-                                            const int64_t base_slot) {
+                                            const int t_lo, const int t_hi,
+                                            const int64_t part_slot) {
   constexpr int NPT = Geo<GP>::NPT;    // 16-token chunks per tile
   constexpr int RING = Geo<GP>::RING;
   constexpr int TILE = Geo<GP>::TILE;
   __shared__ float wm[4][GP], wl[4][GP];
-  // The combine's o' and split weights are only used after the tile loop:
-  // they live in ring position 1 when it is large enough (the LDS then holds
-  // four work-groups with a four-tile ring per wave).
-  constexpr int kAuxBytes = GP * (kHeadDim * 4 + 2 * kCombineSlice * 4);
-  constexpr bool kAuxInRing = RING > 1 && 4 * TILE >= kAuxBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t aux_own[kAuxInRing ? 16 : kAuxBytes];
-  uint8_t* aux = kAuxInRing ? ring_slot<GP, 1>(0) : aux_own;
-  float (*ocomb)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(aux);
-  float (*cmb_m)[GP] = reinterpret_cast<float (*)[GP]>(aux + GP * kHeadDim * 4);
-  float (*cmb_l)[GP] = reinterpret_cast<float (*)[GP]>(aux + GP * (kHeadDim * 4 + kCombineSlice * 4));
   // Per-wave o' staging of the epilogue; it reuses ring position 0 when that
   // is large enough (the ring is idle by then).
   constexpr bool kWoInRing = 4 * TILE >= int(4 * GP * kHeadDim * sizeof(float));
@@ -373,15 +368,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       for (int r = 0; r < 4; ++r) {
         // head of PV row 4gq + r is (4gq + r) % GP
         float cr = corr[r % GP];
-        if constexpr (GP == 8) cr = (gq & 1) ? corr[4 + r] : corr[r];
+        if constexpr (GP == 8) cr = select_bits(0u - uint32_t(gq & 1), corr[4 + r], corr[r]);
 #pragma unroll
         for (int J = 0; J < 8; ++J) cpv[J][r] *= cr;
       }
       float cl = corr[0], ml = m_h[0];
 #pragma unroll
       for (int g = 1; g < GP; ++g) {
-        cl = (g_col == g) ? corr[g] : cl;
-        ml = (g_col == g) ? m_h[g] : ml;
+        const uint32_t sel = 0u - uint32_t(g_col == g);
+        cl = select_bits(sel, corr[g], cl);
+        ml = select_bits(sel, m_h[g], ml);
       }
       l_lane *= cl;
       z_lane *= cl;
@@ -483,9 +479,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     }
     wait_vmcnt<0>();     // drain DMA before the ring memory is reused
   }
-  // The epilogue, the partial store and the combine are short and end the
-  // piece: they run at the top priority so that streaming waves of other
-  // work-groups do not starve them.
+  // The epilogue and the partial store are short and end the piece: they
+  // run at the top priority so that streaming waves of other work-groups do
+  // not starve them.
   __builtin_amdgcn_s_setprio(3);
   __syncthreads();   // the ring is idle from here on
 
@@ -514,7 +510,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       for (int r = 0; r < 4; ++r) {
         const float v = xor32_sum(cpv[J][r]);
         const int g = 4 * (gq & 1) + r;
-        const float zg = (gq & 1) ? z_h[4 + r] : z_h[r];
+        const float zg = select_bits(0u - uint32_t(gq & 1), z_h[4 + r], z_h[r]);
         if (gq < 2 && g < G) wo[wave][g][ch] = v * sc + zg;
       }
     }
@@ -526,10 +522,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   }
 
   __syncthreads();
-  const int64_t head = int64_t(b) * a.n_kv_heads + h;
-  finish_work_group<GP>(a, b, h, part_slot, base_slot, n_pieces,
-                        a.tok_slot0 + head * a.n_tok_slices, a.n_tok_slices, wm, wl, wo, ocomb,
-                        cmb_m, cmb_l);
+  store_partial<GP>(G, wm, wl, wo, a.partials + part_slot * G * kPartialStride);
 }
 
 // Decode over equal tile ranges: the virtual tiles of all (b, h), in order,
@@ -560,17 +553,29 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
     if (sp >= g1) break;
     if (!first) __syncthreads();   // the previous piece is done with every LDS buffer
     const int p = b * Hkv + h;
-    const int pr = a.pair_range[p];
-    const int i0 = pr & 0xFFFF, i1 = pr >> 16;
     decode_item<GP>(a, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(h),
-                    max(g0, sp) - sp, min(g1, sp + wb) - sp, i1 - i0 + 1, int64_t(i) + p,
-                    int64_t(i0) + p);
+                    max(g0, sp) - sp, min(g1, sp + wb) - sp, int64_t(i) + p);
     if (++h == Hkv) {
       h = 0;
       if (++b == B) break;
       wb = pre[b + 1] - pre[b];
     }
   }
+}
+
+// Split-K combine, one work-group per (KV head h, sequence b): the pieces'
+// partials of (b, h) (slots i0 + p .. i1 + p, p = b Hkv + h, with i0, i1 the
+// first and last range touching it) and its token-list slices from the
+// pre-pass.  A kernel of its own: it starts once every partial is written,
+// with HBM idle, so its few dependent loads are short.
+template <int GP>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int p = b * a.n_kv_heads + h;
+  const int pr = a.pair_range[p];
+  const int i0 = pr & 0xFFFF, i1 = pr >> 16;
+  combine_pair<GP>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, a.tok_slot0 + int64_t(p) * a.n_tok_slices,
+                   a.n_tok_slices);
 }
 
 }  // namespace
@@ -656,9 +661,17 @@ int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* st
   (void)batch;
   (void)max_seq_len;
   // G = 1 runs the two-head kernel with one padding head.
-  if (G <= 2) hipLaunchKernelGGL(decode_mfma_kernel<2>, dim3(a.chain_groups), dim3(256), 0, st, a);
-  else if (G <= 4) hipLaunchKernelGGL(decode_mfma_kernel<4>, dim3(a.chain_groups), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(decode_mfma_kernel<8>, dim3(a.chain_groups), dim3(256), 0, st, a);
+  const dim3 grid(a.chain_groups), cgrid(a.n_kv_heads, a.batch);
+  if (G <= 2) {
+    hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel<2>, cgrid, dim3(256), 0, st, a);
+  } else if (G <= 4) {
+    hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel<4>, cgrid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(decode_mfma_kernel<8>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(256), 0, st, a);
+  }
   return static_cast<int>(hipGetLastError());
 }
 
