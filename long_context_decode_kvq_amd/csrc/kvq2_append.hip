@@ -172,6 +172,115 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
   }
 }
 
+// Decode-step appends (a few tokens in all): one (token, KV head, K|V)
+// vector per wave, four waves per work-group sharing (KV head, K|V).  Same
+// arithmetic and destinations as quantize_append_kernel; what differs is the
+// order of the memory accesses, since at this size the kernel is a chain of
+// dependent loads: the sequence lookup reads cu_new and start_pos with one
+// vector load per lane (a ballot finds the sequence) instead of a binary
+// search, and the new vector, that lookup and the R staging are all issued
+// before the first wait; the ring slot and block-table reads that depend on
+// the position follow as one more round.
+__global__ __launch_bounds__(256) void append_step_kernel(AppendArgs a) {
+  __shared__ float Rs[kHeadDim * kHeadDim];
+  __shared__ double xs[kWaves][kHeadDim];
+  const int h = blockIdx.y;
+  const int kind = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
+  const bool active = n < a.total_new;
+  const int nn = active ? n : 0;
+  // the new vector (depends on the token index only)
+  const uint16_t* x = a.x_new[kind] + (int64_t(nn) * a.n_kv_heads + h) * kHeadDim;
+  const uint32_t xr0 = x[lane], xr1 = x[lane + 64];
+  // Sequence of token n: the first b with cu_new[b + 1] > n (cu_new is
+  // non-decreasing, so the sequences that end at or before n are a prefix).
+  int b = a.batch, first = 0, last = 0, start = -1;
+  for (int base = 0; base < a.batch; base += 64) {
+    const int i = base + lane;
+    const bool in = i < a.batch;
+    const int hi = in ? a.cu_new[i + 1] : INT32_MAX;
+    const int lo = in ? a.cu_new[i] : 0;
+    const int sp = in ? a.start_pos[i] : -1;
+    const int cnt = __builtin_amdgcn_readfirstlane(
+        static_cast<int>(__popcll(__builtin_amdgcn_ballot_w64(hi <= nn))));
+    if (cnt < 64) {
+      b = base + cnt;
+      first = __builtin_amdgcn_readlane(lo, cnt);
+      last = __builtin_amdgcn_readlane(hi, cnt);
+      start = __builtin_amdgcn_readlane(sp, cnt);
+      break;
+    }
+  }
+  // R rows into registers; stored to LDS once the dependent reads are issued
+  float4 rr[kHeadDim * kHeadDim / 4 / 256];
+  {
+    const float4* src = reinterpret_cast<const float4*>(a.R[kind] + int64_t(h) * kHeadDim * kHeadDim);
+#pragma unroll
+    for (int k = 0; k < kHeadDim * kHeadDim / 4 / 256; ++k) rr[k] = src[threadIdx.x + 256 * k];
+  }
+  const bool ok = active && b < a.batch && start >= 0;
+  const int W = a.n_recent;
+  const int ns = a.n_sink;
+  const int pos = start + (n - first);
+  const int end = start + (last - first);
+  const int64_t seq_head = int64_t(ok ? b : 0) * a.n_kv_heads + h;
+  const bool to_ring = pos >= ns && pos >= end - W;
+  // the ring slot's occupant from before this append, if it leaves the window
+  const int pold = pos - ((pos - start) / W + 1) * W;
+  const bool evict = ok && to_ring && pold >= ns;
+  float e0 = 0.f, e1 = 0.f;
+  int64_t evict_off = -1;
+  if (evict) {
+    const uint16_t* src = a.recent + (seq_head * W + (pold - ns) % W) * 2 * kHeadDim + kind * kHeadDim;
+    e0 = bf16_bits_to_float(src[lane]);
+    e1 = bf16_bits_to_float(src[lane + 64]);
+    evict_off = chunk_offset_uniform(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
+                                     a.page_size, b, h, pold);
+  }
+  int64_t int2_off = -1;
+  if (ok && pos >= ns && !to_ring)
+    int2_off = chunk_offset_uniform(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
+                                    a.page_size, b, h, pos);
+  {
+    float4* dst = reinterpret_cast<float4*>(Rs);
+#pragma unroll
+    for (int k = 0; k < kHeadDim * kHeadDim / 4 / 256; ++k) dst[threadIdx.x + 256 * k] = rr[k];
+  }
+  xs[wave][lane] = double(bf16_bits_to_float(xr0));
+  xs[wave][lane + 64] = double(bf16_bits_to_float(xr1));
+  __syncthreads();
+  if (!ok) return;
+  const float clip = a.clip[kind];
+  if (evict_off >= 0) quantize_store(a.pool + evict_off, pold % kChunkTokens, kind, e0, e1, clip, lane);
+
+  // Pinned rotation of the new vector.
+  double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll 8
+  for (int j = 0; j < kHeadDim; ++j) {
+    const double xj = xs[wave][j];
+    acc0 = __fma_rn(xj, double(Rs[j * kHeadDim + lane]), acc0);
+    acc1 = __fma_rn(xj, double(Rs[j * kHeadDim + lane + 64]), acc1);
+  }
+  const uint32_t rb0 = float_to_bf16_bits(__double2float_rn(acc0));
+  const uint32_t rb1 = float_to_bf16_bits(__double2float_rn(acc1));
+
+  if (pos < ns) {
+    uint16_t* dst = a.sink + (seq_head * ns + pos) * 2 * kHeadDim + kind * kHeadDim;
+    dst[lane] = static_cast<uint16_t>(rb0);
+    dst[lane + 64] = static_cast<uint16_t>(rb1);
+  } else if (!to_ring) {
+    if (int2_off >= 0)
+      quantize_store(a.pool + int2_off, pos % kChunkTokens, kind, bf16_bits_to_float(rb0),
+                     bf16_bits_to_float(rb1), clip, lane);
+  } else {
+    uint16_t* dst = a.recent + (seq_head * W + (pos - ns) % W) * 2 * kHeadDim + kind * kHeadDim;
+    dst[lane] = static_cast<uint16_t>(rb0);
+    dst[lane + 64] = static_cast<uint16_t>(rb1);
+  }
+}
+
 }  // namespace
 
 int launch_quantize_append(const kvq_dims& d, float /*sm_scale*/, const kvq_layer& layer,
@@ -204,8 +313,11 @@ int launch_quantize_append(const kvq_dims& d, float /*sm_scale*/, const kvq_laye
   // each work-group stages R once per 256 vectors.
   a.tokens_per_block = total_new <= 1024 ? kWaves : total_new <= 8192 ? 16 : 256;
   dim3 grid((total_new + a.tokens_per_block - 1) / a.tokens_per_block, d.n_kv_heads, 2);
-  hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  if (a.tokens_per_block == kWaves)
+    hipLaunchKernelGGL(append_step_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
 
