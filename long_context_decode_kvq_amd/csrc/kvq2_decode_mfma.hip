@@ -270,11 +270,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   constexpr int kDmaPerTile = NPT + (NPT + 1) / 2;
   // One tile from its LDS slot: QK on the matrix cores, lazy online softmax
   // on the hi lanes, PV on the matrix cores.  `after_reads` runs once the
-  // tile's LDS reads have completed: the next block-table lookup is issued
-  // there, so that no lgkmcnt wait of this tile covers it and its latency
-  // overlaps the tile's arithmetic.
+  // tile's LDS reads have completed: the slot is refilled there, and the
+  // next block-table lookup is issued there, so that no lgkmcnt wait of this
+  // tile covers it and its latency overlaps the tile's arithmetic.
   auto compute_tile = [&](const uint8_t* slot, auto&& after_reads) {
-    // this tile's DMA is complete once at most (RING-1) tiles of DMA remain
+    // RING tiles of DMA are outstanding (this one and the RING - 1 after
+    // it); this tile's is complete once at most RING - 1 tiles' remain
     wait_vmcnt<(RING - 1) * kDmaPerTile>();
     uint2 kc[NPT], vc[NPT];
     uint4 kp, vp;
@@ -443,26 +444,28 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     }
   };
 
-  // ---- tile loop: a ring of RING LDS tile slots per wave, DMA RING-1 tiles
-  // ahead.  Every step issues its DMA unconditionally (tiles past the end
-  // read chunk 0 and are never computed), so the number of loads in flight
-  // is the same on every path; page lookups run one step ahead of the DMA.
+  // ---- tile loop: a ring of RING LDS tile slots per wave.  A slot is
+  // refilled with the tile RING steps ahead as soon as its LDS reads have
+  // completed (inside compute_tile), so RING tiles are in flight while one
+  // is computed.  Every computed step issues its DMA unconditionally (tiles
+  // past the end read chunk 0 and are never computed), so the number of
+  // loads in flight at each wait is the same on every path; page lookups
+  // run one step ahead of the DMA.
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;     // tiles wave, wave+4, ...
   if (my_tiles > 0) {
     Pages pn;
 #pragma unroll
-    for (int k = 0; k < RING - 1; ++k) {
+    for (int k = 0; k < RING; ++k) {
       fetch_pages(wave + 4 * k, pn);
       issue_tile(wave + 4 * k, pn, ring_slot_k<GP>(k, wave));
     }
-    fetch_pages(wave + 4 * (RING - 1), pn);
+    fetch_pages(wave + 4 * RING, pn);
     for (int k0 = 0; k0 < my_tiles; k0 += RING) {
 #pragma unroll
       for (int k = 0; k < RING; ++k) {
-        const int kn = (k + RING - 1) % RING;
-        const int ahead = wave + 4 * (k0 + k + RING - 1);
-        issue_tile(ahead, pn, ring_slot_k<GP>(kn, wave));
         if (k0 + k < my_tiles) {
+          const int ahead = wave + 4 * (k0 + k + RING);
+          uint8_t* slot = ring_slot_k<GP>(k, wave);
           // Rotating wave priority: the arbiter otherwise serves the oldest
           // resident waves first, and the work-groups of one CU, which all
           // carry equal work, would finish far apart.
@@ -471,9 +474,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           else if (pr == 1) __builtin_amdgcn_s_setprio(1);
           else if (pr == 2) __builtin_amdgcn_s_setprio(2);
           else __builtin_amdgcn_s_setprio(3);
-          compute_tile(ring_slot_k<GP>(k, wave), [&] { fetch_pages(ahead + 4, pn); });
-        } else {
-          fetch_pages(ahead + 4, pn);
+          compute_tile(slot, [&] {
+            issue_tile(ahead, pn, slot);
+            fetch_pages(ahead + 4, pn);
+          });
         }
       }
     }
