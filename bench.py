@@ -206,8 +206,12 @@ def cpu_baseline(w, W, seconds_budget=10.0, max_steps=100):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # Sustained decode: the first ~100 back-to-back calls after an idle GPU
+    # run through a clock/power transient (calls 6-30 up to 30 % slower, then
+    # back to steady state), so the default warm-up is long enough to time
+    # the steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="conc_28x100k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",

@@ -48,10 +48,11 @@ constexpr int kChainGroups = 1024;
 // Fixed cost of one more piece of the MFMA decode (its prologue, the first
 // tile's latency, the partial store and the combine), in 16-token chunks of
 // streaming: about 15 us of one work-group's stream.  A work-group of the
-// eight-head kernel streams about twice as many chunks per us and its combine
-// is larger (measured best near 300 chunks on the 64-sequence G = 8 batch).
+// eight-head kernel streams about twice as many chunks per us; on the
+// 64-sequence G = 8 batch with a shared prefix, 150 chunks measured best in
+// sustained decode (395 us against 398 at 200 and 406 at 300).
 constexpr int kPieceCostChunks = 80;
-constexpr int kPieceCostChunksG8 = 300;
+constexpr int kPieceCostChunksG8 = 150;
 
 DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len);
 
