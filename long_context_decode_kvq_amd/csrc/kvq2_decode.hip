@@ -50,10 +50,20 @@ __device__ void plan_ranges(const DecodeArgs& a) {
   const int Hkv = a.n_kv_heads;
   const int64_t total = int64_t(Hkv) * carry;
   const int rsz = a.round_size, rounds = rsz > 0 ? nwg / rsz : 0;
-  const bool weighted = rsz > 0 && rounds >= 2 && rounds <= 4 && rounds * rsz == nwg &&
-                        total >= 4 * int64_t(nwg);
+  const bool weighted = rsz > 0 && rsz % 8 == 0 && rounds >= 2 && rounds <= 4 &&
+                        rounds * rsz == nwg && total >= 4 * int64_t(nwg);
+  // Work-group j weighs round_weight[j / rsz] * xcd_weight[j % 8]; range i
+  // starts at total * (weight of work-groups < i) / (weight of all).  A round
+  // (rsz, a multiple of 8 when weighted) holds every XCD rsz / 8 times.
+  int64_t xsum = 0;
+  for (int x = 0; x < 8; ++x) xsum += a.xcd_weight[x];
+  auto xcd_prefix = [&](int64_t k) {   // sum of xcd_weight[j % 8] over j < k
+    int64_t c = (k / 8) * xsum;
+    for (int x = 0; x < int(k % 8); ++x) c += a.xcd_weight[x];
+    return c;
+  };
   int64_t ctot = 0;
-  for (int r = 0; r < rounds; ++r) ctot += int64_t(a.round_weight[r]) * rsz;
+  for (int r = 0; r < rounds; ++r) ctot += int64_t(a.round_weight[r]) * xcd_prefix(rsz);
   const int64_t q = (total + nwg - 1) / nwg;
   for (int i = tid; i <= nwg; i += blockDim.x) {
     int64_t v;
@@ -64,7 +74,7 @@ __device__ void plan_ranges(const DecodeArgs& a) {
       for (int r = 0; r < rounds; ++r) {
         const int64_t lo = int64_t(r) * rsz;
         const int64_t cnt = i <= lo ? 0 : min(int64_t(i), lo + rsz) - lo;
-        c += int64_t(a.round_weight[r]) * cnt;
+        c += int64_t(a.round_weight[r]) * xcd_prefix(cnt);
       }
       v = total * c / ctot;
     }

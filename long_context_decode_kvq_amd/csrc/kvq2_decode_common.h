@@ -63,6 +63,9 @@ struct DecodeArgs {
   int chain_groups;
   int round_size;
   int round_weight[4];
+  // Weight of a work-group's range by the XCD it runs on (work-group i is
+  // dispatched to XCD i mod 8), 1/1024 units.
+  int xcd_weight[8];
   // MFMA decode: the token-by-token list of (b, h) is cut into n_tok_slices
   // slices of 64 tokens; the pre-pass leaves the partial of slice z in slot
   // tok_slot0 + (b Hkv + h) n_tok_slices + z, and the combine takes them in.

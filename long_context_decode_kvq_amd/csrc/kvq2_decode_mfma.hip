@@ -639,23 +639,35 @@ int device_cus() {
 }  // namespace
 
 // Grid and range weights of the MFMA decode (before the pre-pass, which
-// writes the cut).  Measured on the 28 x 100000-token batch with four
-// resident work-groups per CU, equal ranges stream at 2.88, 2.68, 2.45 and
-// 2.31 tiles/us from the first to the fourth dispatched; weights a little
-// steeper than those rates gave the shortest launch there (the gap narrows
-// as the ranges shift).  KVQ_ROUND_WEIGHTS="w0,w1,w2,w3" (1/1024 units)
-// overrides them.
+// writes the cut).  The resident work-groups do not stream at one rate:
+//  * by dispatch round: on the 28 x 100000-token batch (four work-groups per
+//    CU) equal ranges stream at 2.88, 2.68, 2.45 and 2.31 tiles/us from the
+//    first to the fourth dispatched; on the 64-sequence G = 8 batch (three
+//    per CU) the third round ends ~29 us after the first;
+//  * by XCD: work-groups on odd XCDs (i mod 8 odd) end 10-15 us after those
+//    on even XCDs (per-work-group timestamps, stable from call to call).
+// The weights below, a little steeper than the measured rates, gave the
+// shortest sustained decode in A/B runs on one MI355X (28 x 100000: 334 ->
+// 328 us per step; 64-sequence G = 8: 403 -> 392 us).
+// KVQ_ROUND_WEIGHTS="w0,w1,w2,w3" and KVQ_XCD_WEIGHTS="even,odd" (1/1024
+// units) override them.
 void set_chain_geometry(DecodeArgs& a, int batch, int max_seq_len) {
   const int G = a.group;
   a.chain_groups = G <= 2 ? chain_grid<2>(a, batch, max_seq_len)
                  : G <= 4 ? chain_grid<4>(a, batch, max_seq_len)
                           : chain_grid<8>(a, batch, max_seq_len);
   a.round_size = device_cus();
-  int w[4] = {1200, 1090, 950, 860};
-  if (G > 4) { w[0] = w[1] = w[2] = w[3] = 1024; }
+  int w[4] = {1230, 1100, 940, 830};
+  int xw[2] = {1060, 988};
+  if (G > 4) {
+    w[0] = 1120; w[1] = 1024; w[2] = 930; w[3] = 1024;
+    xw[0] = 1036; xw[1] = 1012;
+  }
   if (const char* s = std::getenv("KVQ_ROUND_WEIGHTS"))
     std::sscanf(s, "%d,%d,%d,%d", &w[0], &w[1], &w[2], &w[3]);
-  for (int r = 0; r < 4; ++r) a.round_weight[r] = std::max(1, w[r]);
+  if (const char* s = std::getenv("KVQ_XCD_WEIGHTS")) std::sscanf(s, "%d,%d", &xw[0], &xw[1]);
+  for (int r = 0; r < 4; ++r) a.round_weight[r] = std::min(std::max(1, w[r]), 4096);
+  for (int x = 0; x < 8; ++x) a.xcd_weight[x] = std::min(std::max(1, xw[x & 1]), 4096);
 }
 
 int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* stream) {
