@@ -100,37 +100,29 @@ __device__ void plan_ranges(const DecodeArgs& a) {
   }
 }
 
-// Pre-pass of the decode, one work-group per (KV head h, sequence b, token
-// slice z):
+// Pre-pass of the decode, one work-group per (KV head h, sequence b):
 //  * q'[g] = alpha R_K[h]^T q[b][hG+g] (OSCAR summary sec. 2.2-B: the query
 //    is rotated once instead of un-rotating every cached key), sum(q'[g])
-//    and the exponent e with 2^-e max|q'[g]| < 1; slice 0 stores them and,
-//    for the MFMA decode, its QK operand block;
-//  * MFMA decode: tokens [64 z, 64 z + 64) of the token-by-token list of
-//    (b, h), one 16-token tile per wave, merged into one partial in slot
-//    tok_slot0 + (b Hkv + h) n_tok_slices + z.  These scattered small reads
-//    run here, before the streaming decode, where their latency is short;
-//  * MFMA decode: one more work-group, (Hkv, 0, 0), computes the plan of the
+//    and the exponent e with 2^-e max|q'[g]| < 1, stored for the later
+//    kernels and, for the MFMA decode, its QK operand block;
+//  * MFMA decode: one more work-group, (Hkv, 0), computes the plan of the
 //    equal-range decode alongside the others (the rest of column Hkv exits
 //    at once).
-// GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.  At most
-// 96 VGPRs (five work-groups per CU) so that the slices of a long batch are
-// resident together.
+// GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.
 template <int GP>
 __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
   constexpr int KG = GP > 0 ? GP : kMaxGroup;   // query heads per KV head held
   if constexpr (GP > 0) {
     if (static_cast<int>(blockIdx.x) == a.n_kv_heads) {
-      if (blockIdx.y == 0 && blockIdx.z == 0) plan_ranges<GP>(a);
+      if (blockIdx.y == 0) plan_ranges<GP>(a);
       return;
     }
   }
   __shared__ float qs[KG][kHeadDim];             // q, then q'
-  // rotation half sums [2][KG][128]; then the waves' o' of the token slice
-  __shared__ float buf[(GP > 0 ? 4 * GP : 2 * kMaxGroup) * kHeadDim];
+  __shared__ float buf[2 * KG * kHeadDim];   // rotation half sums [2][KG][128]
   __shared__ float qsum[KG];
   __shared__ int qexp[KG];
-  const int h = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
+  const int h = blockIdx.x, b = blockIdx.y;
   const int G = a.group;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float (*part)[KG][kHeadDim] = reinterpret_cast<float (*)[KG][kHeadDim]>(buf);
@@ -181,7 +173,7 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
     const int g = i / kHeadDim, c = i % kHeadDim;
     const float v = (part[0][g][c] + part[1][g][c]) * a.alpha;
     qs[g][c] = v;
-    if (z == 0) dst[g * kQStride + c] = v;
+    dst[g * kQStride + c] = v;
   }
   __syncthreads();
   for (int g = wave; g < G; g += blockDim.x / 64) {
@@ -190,17 +182,15 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
     const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
     if (lane == 0) {
       const int e = mx > 0.f ? ilogbf(mx) + 1 : 0;
-      if (z == 0) {
-        dst[g * kQStride + kHeadDim] = sum;
-        dst[g * kQStride + kHeadDim + 1] = float(e);
-      }
+      dst[g * kQStride + kHeadDim] = sum;
+      dst[g * kQStride + kHeadDim + 1] = float(e);
       qsum[g] = sum;
       qexp[g] = e;
     }
   }
   __syncthreads();
   if constexpr (GP > 0) {
-    if (z == 0) {
+    {
       // QK operand of the MFMA kernel in its per-lane layout: lane (gq, n)
       // holds column n = 2GP p + GP t + g (t = 0: f16 hi part, 1: lo part of
       // q'[g] scaled by 2^-e_g 2^(8 - 2s)) for the 32 k-slots of its lane group.
@@ -228,34 +218,6 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
         reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane] = qscale;
         reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane + 1] = ok ? qsum[g] / qscale : 0.f;
       }
-    }
-    constexpr int npt = 16 / (2 * GP);
-    if (a.n_tok_slices > 0) {
-      __shared__ float pbuf[4][16][GP];
-      __shared__ float wm[4][GP], wl[4][GP];
-      float (*wo)[GP][kHeadDim] = reinterpret_cast<float (*)[GP][kHeadDim]>(buf);
-      const int L = a.seq_len[b];
-      const Int2Range rg = int2_range(a, L, npt);
-      const TokenList tl = token_list(a, L, rg);
-      float m[GP], l[GP], acc0[GP], acc1[GP];
-#pragma unroll
-      for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
-      token_tile<GP>(a, b, h, tl, rg, 4 * z + wave, qs, qsum, pbuf[wave], m, l, acc0, acc1);
-      // the rotation's half sums in buf are dead since the barrier above
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        if (g < G) {
-          wo[wave][g][2 * lane] = acc0[g];
-          wo[wave][g][2 * lane + 1] = acc1[g];
-          if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
-        }
-      }
-      __syncthreads();
-      float* stage = &wo[0][0][0];
-      merge_wave_states<GP>(G, wm, wl, wo, stage);
-      const int64_t head = int64_t(b) * a.n_kv_heads + h;
-      float* out = a.partials + (a.tok_slot0 + head * a.n_tok_slices + z) * G * kPartialStride;
-      for (int i = tid; i < G * kPartialStride; i += blockDim.x) out[i] = stage[i];
     }
   }
 }
@@ -324,7 +286,7 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.tok_slot0 = plan.tok_slot0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
-  const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch, std::max(1, a.n_tok_slices));
+  const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch);
   if (a.gp == 2) hipLaunchKernelGGL(prologue_kernel<2>, pgrid, dim3(256), 0, st, a);
   else if (a.gp == 4) hipLaunchKernelGGL(prologue_kernel<4>, pgrid, dim3(256), 0, st, a);
   else if (a.gp == 8) hipLaunchKernelGGL(prologue_kernel<8>, pgrid, dim3(256), 0, st, a);

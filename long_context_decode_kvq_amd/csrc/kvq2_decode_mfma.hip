@@ -102,6 +102,24 @@ __device__ __forceinline__ uint8_t* ring_slot(int wave) {
   return slot[wave];
 }
 
+// Per-work-group LDS outside the ring: the waves' softmax (m, l) and, when
+// ring position 0 is too small for it, the waves' o' staging.
+template <int GP>
+struct WaveStage {
+  static constexpr bool kWoInRing =
+      4 * Geo<GP>::TILE >= int(4 * GP * kHeadDim * sizeof(float));
+};
+template <int GP>
+__device__ __forceinline__ float (*wave_m())[GP] {
+  __shared__ float m[4][GP];
+  return m;
+}
+template <int GP>
+__device__ __forceinline__ float (*wave_l())[GP] {
+  __shared__ float l[4][GP];
+  return l;
+}
+
 template <int GP>
 __device__ __forceinline__ uint8_t* ring_slot_k(int k, int wave) {
   // k is a compile-time constant after unrolling
@@ -111,6 +129,14 @@ __device__ __forceinline__ uint8_t* ring_slot_k(int k, int wave) {
   if (k == 3) return ring_slot<GP, 3>(wave);
   if (k == 4) return ring_slot<GP, 4>(wave);
   return ring_slot<GP, 5>(wave);
+}
+
+template <int GP>
+__device__ __forceinline__ float (*wave_o())[GP][kHeadDim] {
+  constexpr bool in_ring = WaveStage<GP>::kWoInRing;
+  __shared__ float own[in_ring ? 1 : 4][in_ring ? 1 : GP][kHeadDim];
+  return in_ring ? reinterpret_cast<float (*)[GP][kHeadDim]>(ring_slot<GP, 0>(0))
+                 : reinterpret_cast<float (*)[GP][kHeadDim]>(&own[0][0][0]);
 }
 
 // Direct HBM -> LDS loads and the LDS reads of a tile are written in
@@ -158,14 +184,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   constexpr int NPT = Geo<GP>::NPT;    // 16-token chunks per tile
   constexpr int RING = Geo<GP>::RING;
   constexpr int TILE = Geo<GP>::TILE;
-  __shared__ float wm[4][GP], wl[4][GP];
+  float (*wm)[GP] = wave_m<GP>();
+  float (*wl)[GP] = wave_l<GP>();
   // Per-wave o' staging of the epilogue; it reuses ring position 0 when that
   // is large enough (the ring is idle by then).
-  constexpr bool kWoInRing = 4 * TILE >= int(4 * GP * kHeadDim * sizeof(float));
-  __shared__ float wo_own[kWoInRing ? 1 : 4][kWoInRing ? 1 : GP][kHeadDim];
-  float (*wo)[GP][kHeadDim] =
-      kWoInRing ? reinterpret_cast<float (*)[GP][kHeadDim]>(ring_slot<GP, 0>(0))
-                : reinterpret_cast<float (*)[GP][kHeadDim]>(&wo_own[0][0][0]);
+  float (*wo)[GP][kHeadDim] = wave_o<GP>();
   const int G = a.group;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // The lane id passes through an empty asm statement so that the per-lane
@@ -536,8 +559,60 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
 // work-group takes every (b, h) its range touches.  Partial slot of
 // (work-group i, pair p) is i + p: the (i, p) overlaps form a monotone path,
 // so the slots are unique and those of one pair are contiguous.
+// Token-by-token list of (b, h), slice z: tokens [64 z, 64 z + 64) of the
+// list (the bf16 sink, the INT2 positions outside whole tiles, the bf16
+// recent window), one 16-token tile per wave, plain fp32, merged into one
+// partial in slot tok_slot0 + (b Hkv + h) n_tok_slices + z for the combine.
+// Run by the work-groups after the streaming ones: they are dispatched as
+// the streaming work-groups retire, into the CUs that the end of the stream
+// leaves idle.  q' comes from the pre-pass; the LDS buffers are carved from
+// the (idle) ring.
+template <int GP>
+__device__ void token_slice_item(const DecodeArgs& a, int idx) {
+  constexpr int NPT = Geo<GP>::NPT;
+  constexpr int RING = Geo<GP>::RING;
+  __shared__ float qsum[GP];
+  __shared__ int qexp[GP];
+  const int S = a.n_tok_slices;
+  const int z = idx % S, pair = idx / S;
+  const int b = pair / a.n_kv_heads, h = pair % a.n_kv_heads;
+  const int G = a.group;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float (*qs)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(ring_slot<GP, 1>(0));
+  float (*pbuf)[16][GP] = reinterpret_cast<float (*)[16][GP]>(
+      RING >= 3 ? ring_slot_k<GP>(2, 0) : ring_slot<GP, 1>(0) + 4096);
+  float (*wm)[GP] = wave_m<GP>();
+  float (*wl)[GP] = wave_l<GP>();
+  float (*wo)[GP][kHeadDim] = wave_o<GP>();
+  load_queries<GP>(a, b, h, qs, qsum, qexp);
+  const int L = a.seq_len[b];
+  const Int2Range rg = int2_range(a, L, NPT);
+  const TokenList tl = token_list(a, L, rg);
+  float m[GP], l[GP], acc0[GP], acc1[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
+  token_tile<GP>(a, b, h, tl, rg, 4 * z + wave, qs, qsum, pbuf[wave], m, l, acc0, acc1);
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (g < G) {
+      wo[wave][g][2 * lane] = acc0[g];
+      wo[wave][g][2 * lane + 1] = acc1[g];
+      if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
+    }
+  }
+  __syncthreads();
+  float* stage = &wo[0][0][0];
+  merge_wave_states<GP>(G, wm, wl, wo, stage);
+  float* out = a.partials + (a.tok_slot0 + int64_t(pair) * S + z) * G * kPartialStride;
+  for (int i = tid; i < G * kPartialStride; i += blockDim.x) out[i] = stage[i];
+}
+
 template <int GP>
 __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
+  if (static_cast<int>(blockIdx.x) >= a.chain_groups) {
+    token_slice_item<GP>(a, static_cast<int>(blockIdx.x) - a.chain_groups);
+    return;
+  }
   const int i = blockIdx.x;
   const int Hkv = a.n_kv_heads, B = a.batch;
   const int32_t* pre = a.tile_prefix;
@@ -677,7 +752,9 @@ int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* st
   (void)batch;
   (void)max_seq_len;
   // G = 1 runs the two-head kernel with one padding head.
-  const dim3 grid(a.chain_groups), cgrid(a.n_kv_heads, a.batch);
+  // the streaming work-groups, then one per token-list slice of every (b, h)
+  const dim3 grid(a.chain_groups + a.batch * a.n_kv_heads * a.n_tok_slices),
+      cgrid(a.n_kv_heads, a.batch);
   if (G <= 2) {
     hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(combine_kernel<2>, cgrid, dim3(256), 0, st, a);
