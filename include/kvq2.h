@@ -178,6 +178,28 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * One decode step: kvq_quantize_append of the new tokens, then
+ * kvq_decode_attention over the cache that includes them (OSCAR summary sec.
+ * 2.2-B: quantize on eviction from the recent window, fused INT2 attention).
+ * The arguments mean what they mean for those two calls, with the same
+ * validation (every error is reported before any launch); the results are
+ * identical to theirs, call for call.  Decode-size appends (total_new <=
+ * 1024, at most 8 query heads per KV head) run the append inside the decode's
+ * q-rotation pre-pass launch, which takes one launch and the pre-pass off
+ * the step's critical path; other shapes run the two calls in stream order.
+ * seq_len must hold the lengths after the append (start_pos + new tokens).
+ */
+int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer,
+                    const kvq_cache* cache, int32_t batch,
+                    const int32_t* start_pos, const int32_t* cu_new,
+                    int32_t total_new, int32_t max_new,
+                    const uint16_t* k_new, const uint16_t* v_new,
+                    const int32_t* seq_len, int32_t max_seq_len,
+                    const uint16_t* q, float* out,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Human-readable name of a kvq_status value (static storage). */
 const char* kvq_status_string(int status);
 

@@ -4,22 +4,37 @@
 #include <algorithm>
 #include <cmath>
 
+#include "kvq2_append_common.h"
 #include "kvq2_decode_common.h"
 
 namespace kvq {
 
 namespace {
 
+// LDS of the range plan and of the q-rotation pre-pass.
+struct PlanLds {
+  int scan[256];
+  int carry;
+  int rs[kChainGroups + 1];
+};
+template <int KG>
+struct PrologueLds {
+  float qs[KG][kHeadDim];           // q, then q'
+  float buf[2 * KG * kHeadDim];     // rotation half sums [2][KG][128]
+  float qsum[KG];
+  int qexp[KG];
+};
+
 // The equal-range plan of the MFMA decode, by one work-group of 256 threads.
 template <int GP>
-__device__ void plan_ranges(const DecodeArgs& a) {
+__device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   constexpr int npt = 16 / (2 * GP);
   const int tid = threadIdx.x;
   // W_b = max(1, whole INT2 tiles of sequence b) + piece_cost;
   // tile_prefix[b] = W_0 + ... + W_{b-1} (inclusive Hillis-Steele scan
   // over blocks of 256 sequences).
-  __shared__ int scan[256];
-  __shared__ int carry;
+  int* scan = P.scan;
+  int& carry = P.carry;
   if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
   __syncthreads();
   for (int base = 0; base < a.batch; base += 256) {
@@ -45,7 +60,7 @@ __device__ void plan_ranges(const DecodeArgs& a) {
   // The cut into chain_groups ranges (weighted by dispatch round when
   // every range keeps at least a few tiles, else equal), then the first
   // and last range of every (b, h).
-  __shared__ int rs[kChainGroups + 1];
+  int* rs = P.rs;
   const int nwg = a.chain_groups;
   const int Hkv = a.n_kv_heads;
   const int64_t total = int64_t(Hkv) * carry;
@@ -109,20 +124,24 @@ __device__ void plan_ranges(const DecodeArgs& a) {
 //    equal-range decode alongside the others (the rest of column Hkv exits
 //    at once).
 // GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.
+// Work-group (hx, b) of the pre-pass grid (Hkv + 1, B) (Hkv, B for the
+// VALU decode), with its LDS.
 template <int GP>
-__global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
+__device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int b,
+                                               PrologueLds<(GP > 0 ? GP : kMaxGroup)>& Lq,
+                                               PlanLds& P) {
   constexpr int KG = GP > 0 ? GP : kMaxGroup;   // query heads per KV head held
   if constexpr (GP > 0) {
-    if (static_cast<int>(blockIdx.x) == a.n_kv_heads) {
-      if (blockIdx.y == 0) plan_ranges<GP>(a);
+    if (hx == a.n_kv_heads) {
+      if (b == 0) plan_ranges<GP>(a, P);
       return;
     }
   }
-  __shared__ float qs[KG][kHeadDim];             // q, then q'
-  __shared__ float buf[2 * KG * kHeadDim];   // rotation half sums [2][KG][128]
-  __shared__ float qsum[KG];
-  __shared__ int qexp[KG];
-  const int h = blockIdx.x, b = blockIdx.y;
+  float (*qs)[kHeadDim] = Lq.qs;
+  float* buf = Lq.buf;
+  float* qsum = Lq.qsum;
+  int* qexp = Lq.qexp;
+  const int h = hx;
   const int G = a.group;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float (*part)[KG][kHeadDim] = reinterpret_cast<float (*)[KG][kHeadDim]>(buf);
@@ -222,16 +241,53 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
   }
 }
 
+template <int GP>
+__global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
+  __shared__ PrologueLds<(GP > 0 ? GP : kMaxGroup)> Lq;
+  __shared__ PlanLds P;
+  prologue_block<GP>(a, blockIdx.x, blockIdx.y, Lq, P);
+}
+
+// The pre-pass of a fused decode step: the work-groups of the decode-step
+// append (grid (n_app_x, Hkv, 2), first) and those of the q-rotation
+// pre-pass (grid (Hkv + 1, B)) in one launch.  They are independent: the
+// append writes the cache, the pre-pass reads only q, R_K and the lengths.
+// One LDS arena serves either role.
+template <int GP>
+__global__ __launch_bounds__(256) void step_prologue_kernel(AppendArgs aa, DecodeArgs a,
+                                                            int n_app_x) {
+  constexpr size_t kAppendLds =
+      sizeof(float) * kHeadDim * kHeadDim + sizeof(double) * kWaves * kHeadDim;
+  constexpr size_t kPreLds = sizeof(PrologueLds<GP>) + sizeof(PlanLds);
+  __shared__ __attribute__((aligned(16))) unsigned char arena[kAppendLds > kPreLds ? kAppendLds
+                                                                                     : kPreLds];
+  const int x = blockIdx.x;
+  const int n_app = n_app_x * a.n_kv_heads * 2;
+  if (x < n_app) {
+    const int bx = x % n_app_x, h = (x / n_app_x) % a.n_kv_heads;
+    const int kind = x / (n_app_x * a.n_kv_heads);
+    append_step_block(aa, bx, h, kind, reinterpret_cast<float*>(arena),
+                      reinterpret_cast<double (*)[kHeadDim]>(
+                          arena + sizeof(float) * kHeadDim * kHeadDim));
+    return;
+  }
+  const int y = x - n_app, H1 = a.n_kv_heads + 1;
+  prologue_block<GP>(a, y % H1, y / H1, *reinterpret_cast<PrologueLds<GP>*>(arena),
+                     *reinterpret_cast<PlanLds*>(arena + sizeof(PrologueLds<GP>)));
+}
+
 }  // namespace
 
 int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
 void set_chain_geometry(DecodeArgs& a, int batch, int max_seq_len);
 int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* stream);
 
-int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
-                  const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
-                  int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
-                  const DecodePlan& plan, DecodeKernel which, void* stream) {
+namespace {
+
+DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
+                            const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
+                            const uint16_t* q, float* out, void* workspace,
+                            const DecodePlan& plan, DecodeKernel which) {
   DecodeArgs a{};
   a.R_K = layer.R_K;
   a.R_V = layer.R_V;
@@ -284,6 +340,17 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   a.piece_cost = plan.piece_cost;
   a.n_tok_slices = plan.n_tok_slices;
   a.tok_slot0 = plan.tok_slot0;
+  return a;
+}
+
+}  // namespace
+
+int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
+                  const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
+                  int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
+                  const DecodePlan& plan, DecodeKernel which, void* stream) {
+  DecodeArgs a = make_decode_args(d, sm_scale, layer, cache, batch, seq_len, q, out, workspace,
+                                  plan, which);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
   const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch);
@@ -294,6 +361,30 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   const int err = static_cast<int>(hipGetLastError());
   if (err != 0) return err;
   if (a.gp == 0) return launch_decode_valu(a, batch, stream);
+  return launch_decode_mfma(a, batch, max_seq_len, stream);
+}
+
+
+int launch_decode_step(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
+                       const kvq_cache& cache, int32_t batch, const int32_t* start_pos,
+                       const int32_t* cu_new, int32_t total_new, const uint16_t* k_new,
+                       const uint16_t* v_new, const int32_t* seq_len, int32_t max_seq_len,
+                       const uint16_t* q, float* out, void* workspace, const DecodePlan& plan,
+                       void* stream) {
+  DecodeArgs a = make_decode_args(d, sm_scale, layer, cache, batch, seq_len, q, out, workspace,
+                                  plan, kDecodeMfma);
+  const AppendArgs aa = make_append_args(d, layer, cache, batch, start_pos, cu_new, total_new,
+                                         k_new, v_new);
+  if (a.gp == 0 || aa.tokens_per_block != kWaves) return -1;   // not a fused-step shape
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  set_chain_geometry(a, batch, max_seq_len);
+  const int n_app_x = (total_new + kWaves - 1) / kWaves;
+  const dim3 grid(n_app_x * d.n_kv_heads * 2 + (d.n_kv_heads + 1) * batch);
+  if (a.gp == 2) hipLaunchKernelGGL(step_prologue_kernel<2>, grid, dim3(256), 0, st, aa, a, n_app_x);
+  else if (a.gp == 4) hipLaunchKernelGGL(step_prologue_kernel<4>, grid, dim3(256), 0, st, aa, a, n_app_x);
+  else hipLaunchKernelGGL(step_prologue_kernel<8>, grid, dim3(256), 0, st, aa, a, n_app_x);
+  const int err = static_cast<int>(hipGetLastError());
+  if (err != 0) return err;
   return launch_decode_mfma(a, batch, max_seq_len, stream);
 }
 

@@ -137,6 +137,56 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
 
 using namespace kvq;
 
+namespace {
+
+// Argument checks of an append (before any HIP call); KVQ_OK with
+// *nothing = true when there is nothing to append.
+int check_append(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
+                 int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
+                 int32_t total_new, int32_t max_new, const uint16_t* k_new,
+                 const uint16_t* v_new, bool* nothing) {
+  int rc = check_dims(dims);
+  if (rc != KVQ_OK) return rc;
+  if ((rc = check_layer(layer)) != KVQ_OK) return rc;
+  if ((rc = check_cache(dims, cache)) != KVQ_OK) return rc;
+  if (batch < 1 || total_new < 0 || max_new < 0 || max_new > total_new) return KVQ_ERR_ARG;
+  if (start_pos == nullptr || cu_new == nullptr) return KVQ_ERR_ARG;
+  *nothing = total_new == 0;
+  if (*nothing) return KVQ_OK;
+  if (k_new == nullptr || v_new == nullptr || !aligned16(k_new) || !aligned16(v_new))
+    return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+// Argument checks of a decode (before any HIP call); fills the plan.
+int check_decode(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
+                 int32_t batch, const int32_t* seq_len, int32_t max_seq_len, const uint16_t* q,
+                 float* out, void* workspace, size_t workspace_bytes, DecodePlan* plan) {
+  int rc = check_dims(dims);
+  if (rc != KVQ_OK) return rc;
+  if ((rc = check_layer(layer)) != KVQ_OK) return rc;
+  if ((rc = check_cache(dims, cache)) != KVQ_OK) return rc;
+  if (batch < 1 || max_seq_len < 0 || seq_len == nullptr) return KVQ_ERR_ARG;
+  if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
+  if (int64_t(max_seq_len) > int64_t(cache->bt_stride) * dims->page_size) return KVQ_ERR_ARG;
+  // The MFMA decode counts virtual tiles of the whole batch in 32 bits.
+  if (int64_t(batch) * dims->n_kv_heads * (int64_t(max_seq_len) / kChunkTokens + kPieceCostChunksG8 + 2) >=
+      (int64_t(1) << 31))
+    return KVQ_ERR_UNSUPPORTED;
+  *plan = make_decode_plan(*dims, batch, max_seq_len);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan->total_bytes)
+    return KVQ_ERR_WORKSPACE;
+  return KVQ_OK;
+}
+
+int hip_status(int err) {
+  if (err == 0) return KVQ_OK;
+  set_last_error(hip_error_name(err));
+  return KVQ_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* kvq_status_string(int status) {
@@ -157,22 +207,12 @@ int kvq_quantize_append(const kvq_dims* dims, const kvq_layer* layer, const kvq_
                         int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
                         int32_t total_new, int32_t max_new, const uint16_t* k_new,
                         const uint16_t* v_new, void* stream) {
-  int rc = check_dims(dims);
-  if (rc != KVQ_OK) return rc;
-  if ((rc = check_layer(layer)) != KVQ_OK) return rc;
-  if ((rc = check_cache(dims, cache)) != KVQ_OK) return rc;
-  if (batch < 1 || total_new < 0 || max_new < 0 || max_new > total_new) return KVQ_ERR_ARG;
-  if (start_pos == nullptr || cu_new == nullptr) return KVQ_ERR_ARG;
-  if (total_new == 0) return KVQ_OK;
-  if (k_new == nullptr || v_new == nullptr || !aligned16(k_new) || !aligned16(v_new))
-    return KVQ_ERR_ARG;
-  int err = launch_quantize_append(*dims, resolved_scale(dims), *layer, *cache, batch, start_pos,
-                                   cu_new, total_new, k_new, v_new, stream);
-  if (err != 0) {
-    set_last_error(hip_error_name(err));
-    return KVQ_ERR_HIP;
-  }
-  return KVQ_OK;
+  bool nothing = false;
+  const int rc = check_append(dims, layer, cache, batch, start_pos, cu_new, total_new, max_new,
+                              k_new, v_new, &nothing);
+  if (rc != KVQ_OK || nothing) return rc;
+  return hip_status(launch_quantize_append(*dims, resolved_scale(dims), *layer, *cache, batch,
+                                           start_pos, cu_new, total_new, k_new, v_new, stream));
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_dims* dims, int32_t batch, int32_t max_seq_len) {
@@ -184,27 +224,45 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq
                          int32_t batch, const int32_t* seq_len, int32_t max_seq_len,
                          const uint16_t* q, float* out, void* workspace, size_t workspace_bytes,
                          void* stream) {
-  int rc = check_dims(dims);
+  DecodePlan plan;
+  const int rc = check_decode(dims, layer, cache, batch, seq_len, max_seq_len, q, out, workspace,
+                              workspace_bytes, &plan);
   if (rc != KVQ_OK) return rc;
-  if ((rc = check_layer(layer)) != KVQ_OK) return rc;
-  if ((rc = check_cache(dims, cache)) != KVQ_OK) return rc;
-  if (batch < 1 || max_seq_len < 0 || seq_len == nullptr) return KVQ_ERR_ARG;
-  if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
-  if (int64_t(max_seq_len) > int64_t(cache->bt_stride) * dims->page_size) return KVQ_ERR_ARG;
-  // The MFMA decode counts virtual tiles of the whole batch in 32 bits.
-  if (int64_t(batch) * dims->n_kv_heads * (int64_t(max_seq_len) / kChunkTokens + kPieceCostChunksG8 + 2) >=
-      (int64_t(1) << 31))
-    return KVQ_ERR_UNSUPPORTED;
-  const DecodePlan plan = make_decode_plan(*dims, batch, max_seq_len);
-  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan.total_bytes)
-    return KVQ_ERR_WORKSPACE;
-  int err = launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
-                          max_seq_len, q, out, workspace, plan, selected_decode_kernel(), stream);
-  if (err != 0) {
-    set_last_error(hip_error_name(err));
-    return KVQ_ERR_HIP;
+  return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
+                                  max_seq_len, q, out, workspace, plan, selected_decode_kernel(),
+                                  stream));
+}
+
+int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
+                    int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
+                    int32_t total_new, int32_t max_new, const uint16_t* k_new,
+                    const uint16_t* v_new, const int32_t* seq_len, int32_t max_seq_len,
+                    const uint16_t* q, float* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  bool nothing = false;
+  int rc = check_append(dims, layer, cache, batch, start_pos, cu_new, total_new, max_new, k_new,
+                        v_new, &nothing);
+  if (rc != KVQ_OK) return rc;
+  DecodePlan plan;
+  rc = check_decode(dims, layer, cache, batch, seq_len, max_seq_len, q, out, workspace,
+                    workspace_bytes, &plan);
+  if (rc != KVQ_OK) return rc;
+  const float scale = resolved_scale(dims);
+  const int G = dims->n_q_heads / dims->n_kv_heads;
+  if (!nothing && total_new <= kStepAppendMax && G <= 8 &&
+      selected_decode_kernel() == kDecodeMfma) {
+    return hip_status(launch_decode_step(*dims, scale, *layer, *cache, batch, start_pos, cu_new,
+                                         total_new, k_new, v_new, seq_len, max_seq_len, q, out,
+                                         workspace, plan, stream));
   }
-  return KVQ_OK;
+  // Other shapes: the append, then the decode, in stream order.
+  if (!nothing) {
+    rc = hip_status(launch_quantize_append(*dims, scale, *layer, *cache, batch, start_pos, cu_new,
+                                           total_new, k_new, v_new, stream));
+    if (rc != KVQ_OK) return rc;
+  }
+  return hip_status(launch_decode(*dims, scale, *layer, *cache, batch, seq_len, max_seq_len, q,
+                                  out, workspace, plan, selected_decode_kernel(), stream));
 }
 
 }  // extern "C"

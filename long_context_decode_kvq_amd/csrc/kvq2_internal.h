@@ -67,6 +67,20 @@ int launch_quantize_append(const kvq_dims& d, float sm_scale, const kvq_layer& l
                            const int32_t* cu_new, int32_t total_new, const uint16_t* k_new,
                            const uint16_t* v_new, void* stream);
 
+// Appends of at most this many new tokens in all run the one-token-per-wave
+// step kernel (decode steps), and can be fused with the decode pre-pass.
+constexpr int kStepAppendMax = 1024;
+
+// Fused decode step (append work-groups in the decode pre-pass launch); the
+// MFMA decode and 0 < total_new <= kStepAppendMax only (returns -1 otherwise,
+// before any launch).
+int launch_decode_step(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
+                       const kvq_cache& cache, int32_t batch, const int32_t* start_pos,
+                       const int32_t* cu_new, int32_t total_new, const uint16_t* k_new,
+                       const uint16_t* v_new, const int32_t* seq_len, int32_t max_seq_len,
+                       const uint16_t* q, float* out, void* workspace, const DecodePlan& plan,
+                       void* stream);
+
 int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                   const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
                   int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,

@@ -43,7 +43,7 @@ class KvqCache(C.Structure):
 
 
 EXPORTS = ("kvq_calibrate", "kvq_quantize_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attention", "kvq_status_string", "kvq_last_error")
+           "kvq_decode_attention", "kvq_decode_step", "kvq_status_string", "kvq_last_error")
 
 
 def lib():
@@ -65,6 +65,10 @@ def lib():
         L.kvq_decode_attention.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
                                            C.POINTER(KvqCache), I32, P, I32, P, P, P, SZ, P]
         L.kvq_decode_attention.restype = C.c_int
+        L.kvq_decode_step.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
+                                      C.POINTER(KvqCache), I32, P, P, I32, I32, P, P, P, I32,
+                                      P, P, P, SZ, P]
+        L.kvq_decode_step.restype = C.c_int
         L.kvq_status_string.argtypes = [C.c_int]
         L.kvq_status_string.restype = C.c_char_p
         L.kvq_last_error.argtypes = []
@@ -154,6 +158,17 @@ def decode_attention(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, seq_l
                                     max_seq_len, _ptr(q), _ptr(out), _ptr(workspace), nbytes,
                                     _stream_handle(stream))
     _check(rc, "kvq_decode_attention")
+
+
+def decode_step(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, start_pos, cu_new,
+                total_new: int, max_new: int, k_new, v_new, seq_len, max_seq_len: int, q, out,
+                workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kvq_decode_step(C.byref(d), C.byref(lay), C.byref(cch), batch, _ptr(start_pos),
+                               _ptr(cu_new), total_new, max_new, _ptr(k_new), _ptr(v_new),
+                               _ptr(seq_len), max_seq_len, _ptr(q), _ptr(out), _ptr(workspace),
+                               nbytes, _stream_handle(stream))
+    _check(rc, "kvq_decode_step")
 
 
 # ------------------------------------------------------------------ device cache holder

@@ -115,6 +115,37 @@ class Scenario:
         ok_rec = np.array_equal(rec, self.oc.recent)
         return ok_pool, ok_sink, ok_rec
 
+    def step(self, counts, q_seed=99):
+        """append(counts) and decode(q_seed) in one kvq_decode_step call."""
+        B = self.B
+        start = np.array(self.cur, np.int32)
+        cu = np.zeros(B + 1, np.int32)
+        cu[1:] = np.cumsum(counts)
+        total = int(cu[-1])
+        k_dev = v_dev = None
+        if total:
+            ks = np.concatenate([self.k_all[b][self.cur[b]:self.cur[b] + counts[b]] for b in range(B)])
+            vs = np.concatenate([self.v_all[b][self.cur[b]:self.cur[b] + counts[b]] for b in range(B)])
+            k_dev, v_dev = dev_u16(ks), dev_u16(vs)
+        for b in range(B):
+            if counts[b]:
+                self.oc.append(self.R_K, self.R_V, self.clip_K, self.clip_V, b, self.cur[b],
+                               self.k_all[b][self.cur[b]:self.cur[b] + counts[b]],
+                               self.v_all[b][self.cur[b]:self.cur[b] + counts[b]])
+            self.cur[b] += counts[b]
+        q = normal_bits(self.seed * 31 + q_seed, (B, self.od.n_q_heads, 128))
+        seq = torch.tensor(self.cur, dtype=torch.int32, device="cuda")
+        maxL = max(self.cur)
+        ws = torch.zeros(kvq2.decode_workspace_bytes(self.kd, B, maxL), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty((B, self.od.n_q_heads, 128), dtype=torch.float32, device="cuda")
+        kvq2.decode_step(self.kd, self.layer, self.dc.handle, B, torch.from_numpy(start).cuda(),
+                         torch.from_numpy(cu).cuda(), total, int(max(counts)), k_dev, v_dev, seq,
+                         maxL, dev_u16(q), out, ws)
+        torch.cuda.synchronize()
+        ref = self.oc.decode(self.R_K, self.R_V, self.cur, q)
+        return out.cpu().numpy(), ref
+
     def decode(self, q_seed=99):
         q = normal_bits(self.seed * 31 + q_seed, (self.B, self.od.n_q_heads, 128))
         seq = torch.tensor(self.cur, dtype=torch.int32, device="cuda")

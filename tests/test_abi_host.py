@@ -62,6 +62,12 @@ def _append(d, lay, cch, batch=2, sp=FAKE, cu=FAKE, total=4, mx=2, k=FAKE, v=FAK
                                       mx, k, v, None)
 
 
+def _step(d, lay, cch, batch=2, sp=FAKE, cu=FAKE, total=4, mx=2, k=FAKE, v=FAKE, seq=FAKE,
+          max_len=100, q=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30):
+    return _lib().kvq_decode_step(C.byref(d), C.byref(lay), C.byref(cch), batch, sp, cu, total, mx,
+                                  k, v, seq, max_len, q, out, ws, wsb, None)
+
+
 @pytest.mark.parametrize("over,rc", [
     (dict(head_dim=64), ERR_UNSUP),
     (dict(P=8), ERR_UNSUP),
@@ -80,6 +86,8 @@ def test_validation_rejects_before_launch(over, rc):
     assert _decode(d, lay, cch) == rc
     d, lay, cch = _args(**dict(over))
     assert _append(d, lay, cch) == rc
+    d, lay, cch = _args(**dict(over))
+    assert _step(d, lay, cch) == rc
 
 
 def test_validation_pointer_and_size_errors():
@@ -102,6 +110,22 @@ def test_validation_pointer_and_size_errors():
     lay2 = kvq2.KvqLayer(FAKE + 4, FAKE, 4.0, 4.0)
     d, _, cch = _args()
     assert _decode(d, lay2, cch) == ERR_ARG
+
+
+def test_decode_step_validates_both_halves_before_launch():
+    d, lay, cch = _args()
+    need = _lib().kvq_decode_workspace_bytes(C.byref(d), 2, 100)
+    # append half
+    assert _step(d, lay, cch, mx=5) == ERR_ARG
+    assert _step(d, lay, cch, k=FAKE + 8) == ERR_ARG
+    assert _step(d, lay, cch, sp=0) == ERR_ARG
+    # decode half (also when there is nothing to append)
+    assert _step(d, lay, cch, q=FAKE + 2) == ERR_ARG
+    assert _step(d, lay, cch, seq=0) == ERR_ARG
+    assert _step(d, lay, cch, max_len=8 * 16 + 1) == ERR_ARG
+    assert _step(d, lay, cch, wsb=need - 1) == ERR_WS
+    assert _step(d, lay, cch, total=0, mx=0, ws=0) == ERR_WS
+    assert _step(d, lay, cch, batch=0) == ERR_ARG
 
 
 def test_decode_rejects_batches_beyond_32bit_tile_counts():
