@@ -7,6 +7,10 @@ For a few sampled pairs the oracle builds the pair's cache by itself from the
 same seeded tokens (fp64 rotation, its own quantizer and packing), decodes the
 pair's query heads and the outputs are compared row by row (max normwise
 relative error <= 2e-3).  Nothing the GPU produced enters the oracle.
+The decode-step cases build the cache to L - 1 tokens and append the last
+token of every sequence in the kvq_decode_step call that decodes (the call
+bench.py times), so that step's eviction, ring write and fused pre-pass are
+part of what is compared.
 """
 import math
 
@@ -25,7 +29,7 @@ HEAD_DIM = 128
 CHUNK = 8192        # tokens per sequence per bulk append call
 
 
-def gpu_cache(w, cal, lens):
+def gpu_cache(w, cal, lens, until=None):
     """The whole workload's cache on the GPU (bulk appends), oracle rotations."""
     dev = torch.device("cuda")
     kd = kvq2.dims(w.n_q_heads, w.n_kv_heads, w.page_size, w.n_sink, w.n_recent)
@@ -34,8 +38,9 @@ def gpu_cache(w, cal, lens):
     keep = (torch.from_numpy(cal.R_K).to(dev), torch.from_numpy(cal.R_V).to(dev))
     lay = kvq2.layer(keep[0], keep[1], float(cal.clip_K), float(cal.clip_V))
     done = np.zeros(w.batch, np.int64)
+    fill = lens if until is None else until
     while True:
-        todo = np.minimum(lens - done, CHUNK)
+        todo = np.minimum(fill - done, CHUNK)
         if todo.sum() == 0:
             break
         ks, vs = [], []
@@ -93,6 +98,47 @@ def test_fullsize_sampled_pairs(name, pairs):
     seq = torch.from_numpy(lens.astype(np.int32)).cuda()
     q = W.decode_queries_device(w, 0)
     kvq2.decode_attention(kd, lay, dc.handle, w.batch, seq, max_len, q, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    q_bits = q.cpu().numpy().view(np.uint16)
+    G = w.group
+    for b, h in pairs:
+        ref = oracle_pair(w, cal, b, h, int(lens[b]), q_bits[b])
+        e = rel_err(got[b, h * G:(h + 1) * G], ref)
+        say(f"  pair (b={b}, h={h}) len={int(lens[b])}: rel_err={e:.3e}")
+        assert e <= TOL, (name, b, h, e)
+
+
+STEP_CASES = [
+    ("conc_28x100k", [(13, 2)]),
+    ("qwen3_32b", [(1, 6), (40, 1)]),
+]
+
+
+@pytest.mark.parametrize("name,pairs", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_fullsize_decode_step_sampled_pairs(name, pairs):
+    w = W.WORKLOADS[name]
+    say(f"[fullsize step] {name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads}")
+    lens = w.seq_lens().astype(np.int64)
+    q_c, k_c, v_c = W.calibration_tokens(w)
+    cal = O.calibrate(q_c, k_c, v_c, w.n_q_heads, w.n_kv_heads, 1 / math.sqrt(HEAD_DIM), 0.999)
+    kd, dc, lay, keep = gpu_cache(w, cal, lens, until=lens - 1)
+    dev = torch.device("cuda")
+    # the last token of every sequence, appended by the decode step itself
+    new = [W.sequence_kv_device(w, b, int(lens[b]) - 1, 1, dev) for b in range(w.batch)]
+    k_new = torch.cat([kv[0] for kv in new]).contiguous()
+    v_new = torch.cat([kv[1] for kv in new]).contiguous()
+    start = torch.from_numpy((lens - 1).astype(np.int32)).to(dev)
+    cu = torch.arange(w.batch + 1, dtype=torch.int32, device=dev)
+    max_len = int(lens.max())
+    ws = torch.zeros(kvq2.decode_workspace_bytes(kd, w.batch, max_len), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=dev)
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    q = W.decode_queries_device(w, 0)
+    kvq2.decode_step(kd, lay, dc.handle, w.batch, start, cu, w.batch, 1, k_new, v_new, seq,
+                     max_len, q, out, ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
