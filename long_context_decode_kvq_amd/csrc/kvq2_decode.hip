@@ -28,7 +28,7 @@ struct PrologueLds {
 // The equal-range plan of the MFMA decode, by one work-group of 256 threads.
 template <int GP>
 __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
-  constexpr int npt = 16 / (2 * GP);
+  constexpr int npt = chunks_per_tile(GP);
   const int tid = threadIdx.x;
   // W_b = max(1, whole INT2 tiles of sequence b) + piece_cost;
   // tile_prefix[b] = W_0 + ... + W_{b-1} (inclusive Hillis-Steele scan

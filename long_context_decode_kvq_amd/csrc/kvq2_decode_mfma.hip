@@ -83,23 +83,39 @@ __device__ __forceinline__ void k_operands(uint32_t w, half8_t& even, half8_t& o
   odd = __builtin_bit_cast(half8_t, o);
 }
 
-// Tile geometry: 16 / (2 GP) chunks per tile.  In LDS a tile is stored as
-// [codes of chunk 0..NPT-1 (1024 B each)][scale/zero params (128 B each)];
-// at least 256 B of params space so one 64-lane dword DMA always fits.
+// Tile geometry: NPT = chunks_per_tile(GP) chunks per tile.  In LDS a tile
+// is stored as [codes of chunk 0..NPT-1 (1024 B each)][scale/zero params
+// (128 B each)]; at least 256 B of params space so one 64-lane dword DMA
+// always fits.  SHARED: the eight-head layout, whose QK columns are the same
+// for both chunks of a tile (every lane takes logits of both chunks).
 template <int GP>
 struct Geo {
-  static constexpr int NPT = 16 / (2 * GP);
+  static constexpr int NPT = chunks_per_tile(GP);
+  static constexpr bool SHARED = 2 * GP * NPT > 16;
   static constexpr int PARAM_BYTES = NPT >= 2 ? NPT * 128 : 256;
   static constexpr int TILE = NPT * 1024 + PARAM_BYTES;
   static constexpr int RING = NPT >= 4 ? 2 : (NPT == 2 ? 4 : 6);   // tiles per wave ring
 };
 
+// The eight-head kernel keeps its ring in one array, so that the epilogue's
+// o' staging (16 KiB) fits in ring positions 0 and 1 and three work-groups
+// fit a CU's LDS.
+template <int GP>
+__device__ __forceinline__ uint8_t* shared_ring() {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[Geo<GP>::RING][4][Geo<GP>::TILE];
+  return &ring[0][0][0];
+}
+
 // One LDS array per ring position (all waves' slots for that position), so
 // that the wait before reading a slot covers only that slot's DMA loads.
 template <int GP, int K>
 __device__ __forceinline__ uint8_t* ring_slot(int wave) {
-  __shared__ __attribute__((aligned(16))) uint8_t slot[4][Geo<GP>::TILE];
-  return slot[wave];
+  if constexpr (Geo<GP>::SHARED) {
+    return shared_ring<GP>() + (K * 4 + wave) * Geo<GP>::TILE;
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t slot[4][Geo<GP>::TILE];
+    return slot[wave];
+  }
 }
 
 // Per-work-group LDS outside the ring: the waves' softmax (m, l) and, when
@@ -107,7 +123,13 @@ __device__ __forceinline__ uint8_t* ring_slot(int wave) {
 template <int GP>
 struct WaveStage {
   static constexpr bool kWoInRing =
-      4 * Geo<GP>::TILE >= int(4 * GP * kHeadDim * sizeof(float));
+      (Geo<GP>::SHARED ? Geo<GP>::RING : 1) * 4 * Geo<GP>::TILE >=
+      int(4 * GP * kHeadDim * sizeof(float));
+  // ring positions holding the token-slice role's q' and softmax weights
+  // (clear of the o' staging)
+  static constexpr int kQsPos = Geo<GP>::SHARED ? 2 : 1;
+  static constexpr int kPbPos = Geo<GP>::SHARED ? 3 : (Geo<GP>::RING >= 3 ? 2 : 1);
+  static constexpr int kPbOff = Geo<GP>::SHARED || Geo<GP>::RING >= 3 ? 0 : 4096;
 };
 template <int GP>
 __device__ __forceinline__ float (*wave_m())[GP] {
@@ -300,6 +322,134 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     // RING tiles of DMA are outstanding (this one and the RING - 1 after
     // it); this tile's is complete once at most RING - 1 tiles' remain
     wait_vmcnt<(RING - 1) * kDmaPerTile>();
+    if constexpr (Geo<GP>::SHARED) {
+      // Eight heads: the 16 QK columns (head, hi/lo) serve both chunks of
+      // the tile.  Every lane takes the logits of its four tokens of each
+      // chunk, and one 16x16x32 PV product per channel tile covers both
+      // chunks (k-slots 0-3 chunk 0, 4-7 chunk 1).
+      uint2 kc0, vc0, kc1, vc1;
+      uint4 kp0, vp0, kp1, vp1;
+      const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot));
+      const uint32_t acode = lds + 32u * n + 8u * gq;
+      const uint32_t aprm = lds + 2048u + 16u * gq;
+      asm volatile(
+          "ds_read_b64 %0, %8\n\t"
+          "ds_read_b64 %1, %8 offset:512\n\t"
+          "ds_read_b64 %2, %8 offset:1024\n\t"
+          "ds_read_b64 %3, %8 offset:1536\n\t"
+          "ds_read_b128 %4, %9\n\t"
+          "ds_read_b128 %5, %9 offset:64\n\t"
+          "ds_read_b128 %6, %9 offset:128\n\t"
+          "ds_read_b128 %7, %9 offset:192\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(kc0), "=v"(vc0), "=v"(kc1), "=v"(vc1), "=v"(kp0), "=v"(vp0), "=v"(kp1),
+            "=v"(vp1)
+          : "v"(acode), "v"(aprm)
+          : "memory");
+      after_reads();
+      float4_t cq[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint2 kcp = p == 0 ? kc0 : kc1;
+        half8_t a0, a1, a2, a3;
+        k_operands(kcp.x, a0, a1);
+        k_operands(kcp.y, a2, a3);
+        float4_t c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bq[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[3], c, 0, 0, 0);
+        cq[p] = c;
+      }
+      float lg[8], zv[8];
+      uint32_t svb[8];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint4 kp = p == 0 ? kp0 : kp1;
+        const uint4 vp = p == 0 ? vp0 : vp1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float d = cq[p][r] + dpp_f<0x100 + GP>(cq[p][r]);   // hi + lo columns
+          const uint32_t kpr = r == 0 ? kp.x : r == 1 ? kp.y : r == 2 ? kp.z : kp.w;
+          const uint32_t vpr = r == 0 ? vp.x : r == 1 ? vp.y : r == 2 ? vp.z : vp.w;
+          lg[4 * p + r] = fmaf(f16lo(kpr), d, f16hi(kpr) * qbar_s);
+          svb[4 * p + r] = vpr;
+          zv[4 * p + r] = f16hi(vpr);
+        }
+      }
+      float tmax = lg[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, lg[i]);
+      if (__builtin_amdgcn_ballot_w64(is_hi && g_ok && tmax > thr) != 0) {
+        const float tm = (is_hi && g_ok) ? tmax * qscale : -INFINITY;
+        float corr[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          const float mg = wave_max(g_col == g ? tm : -INFINITY);
+          const float mo = m_h[g];
+          const float mn = fmaxf(mo, mg);
+          corr[g] = (mn == -INFINITY) ? 1.f : exp2f(mo - mn);
+          m_h[g] = mn;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // head of PV row 4gq + r is (4gq + r) % 8
+          const float cr = select_bits(0u - uint32_t(gq & 1), corr[4 + r], corr[r]);
+#pragma unroll
+          for (int J = 0; J < 8; ++J) cpv[J][r] *= cr;
+        }
+        float cl = corr[0], ml = m_h[0];
+#pragma unroll
+        for (int g = 1; g < GP; ++g) {
+          const uint32_t sel = 0u - uint32_t(g_col == g);
+          cl = select_bits(sel, corr[g], cl);
+          ml = select_bits(sel, m_h[g], ml);
+        }
+        l_lane *= cl;
+        z_lane *= cl;
+        m_eff = g_ok ? ml - log2_sigma : INFINITY;
+        thr = g_ok ? (ml + kTau) / qscale : INFINITY;
+      }
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], qscale, -m_eff));
+        l_lane += p;                     // lo lanes accumulate garbage, masked at the end
+        z_lane = fmaf(p, zv[i], z_lane);
+        w[i] = p * f16lo(svb[i]);
+      }
+      // f16 hi/lo split per chunk as in the other layouts; lo parts move GP
+      // lanes up (row_shr) into the lo rows
+      uint32_t av[4];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const fp16x2_t h02 = __builtin_amdgcn_cvt_pkrtz(w[4 * p + 0], w[4 * p + 2]);
+        const fp16x2_t h13 = __builtin_amdgcn_cvt_pkrtz(w[4 * p + 1], w[4 * p + 3]);
+        const uint32_t lo02 = __builtin_bit_cast(
+            uint32_t,
+            __builtin_amdgcn_cvt_pkrtz(w[4 * p + 0] - float(h02[0]), w[4 * p + 2] - float(h02[1])));
+        const uint32_t lo13 = __builtin_bit_cast(
+            uint32_t,
+            __builtin_amdgcn_cvt_pkrtz(w[4 * p + 1] - float(h13[0]), w[4 * p + 3] - float(h13[1])));
+        const uint32_t lo02s = dpp_u<0x110 + GP>(lo02), lo13s = dpp_u<0x110 + GP>(lo13);
+        av[2 * p] = is_hi ? __builtin_bit_cast(uint32_t, h02) : lo02s;
+        av[2 * p + 1] = is_hi ? __builtin_bit_cast(uint32_t, h13) : lo13s;
+      }
+      const u32x4_t ap = {av[0], av[1], av[2], av[3]};
+      const half8_t A = __builtin_bit_cast(half8_t, ap);
+      const uint32_t e0 = vc0.x, e1 = vc0.y, f0 = vc1.x, f1 = vc1.y;
+      const uint32_t e0s = e0 >> 8, e1s = e1 >> 8, f0s = f0 >> 8, f1s = f1 >> 8;
+#pragma unroll
+      for (int J = 0; J < 8; ++J) {
+        const uint32_t mask = 0x00030003u << (2 * (J & 3));
+        const uint32_t d = J < 4 ? e0 : e1, ds = J < 4 ? e0s : e1s;
+        const uint32_t f = J < 4 ? f0 : f1, fs = J < 4 ? f0s : f1s;
+        const u32x4_t bv = {d & mask, ds & mask, f & mask, fs & mask};
+        cpv[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bv),
+                                                        cpv[J], 0, 0, 0);
+      }
+      return;
+    }
     uint2 kc[NPT], vc[NPT];
     uint4 kp, vp;
     const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot));
@@ -578,9 +728,10 @@ __device__ void token_slice_item(const DecodeArgs& a, int idx) {
   const int b = pair / a.n_kv_heads, h = pair % a.n_kv_heads;
   const int G = a.group;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  float (*qs)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(ring_slot<GP, 1>(0));
+  float (*qs)[kHeadDim] =
+      reinterpret_cast<float (*)[kHeadDim]>(ring_slot<GP, WaveStage<GP>::kQsPos>(0));
   float (*pbuf)[16][GP] = reinterpret_cast<float (*)[16][GP]>(
-      RING >= 3 ? ring_slot_k<GP>(2, 0) : ring_slot<GP, 1>(0) + 4096);
+      ring_slot<GP, WaveStage<GP>::kPbPos>(0) + WaveStage<GP>::kPbOff);
   float (*wm)[GP] = wave_m<GP>();
   float (*wl)[GP] = wave_l<GP>();
   float (*wo)[GP][kHeadDim] = wave_o<GP>();

@@ -118,7 +118,7 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
     // positions before the first whole chunk, at most 16 npt - 1 after the
     // last whole tile, and the recent window.
     const int gp = G <= 2 ? 2 : G <= 4 ? 4 : 8;
-    const int npt = 16 / (2 * gp);
+    const int npt = chunks_per_tile(gp);
     const int64_t max_list = int64_t(d.n_sink) + 15 + (16 * npt - 1) + d.n_recent;
     p.n_tok_slices = static_cast<int>((max_list + 63) / 64);
     p.tok_slot0 = int64_t(kChainGroups) + heads;

@@ -24,6 +24,13 @@ constexpr int kQStride = 132;          // floats per rotated query: q'[128], sum
                                        // f16 scaling exponent, 2 pad
 constexpr int kBqWords = 64 * 16 + 64 * 2;   // u32 words per (b, h) of the QK operand block
 
+// 16-token chunks per tile of the MFMA decode for head-group width gp (2, 4
+// or 8): the QK tile's 16 columns hold (chunk, f16 hi/lo, head), so a tile
+// spans 16 / (2 gp) chunks; the eight-head tile fills all 16 columns with
+// one chunk and takes two chunks per tile (two QK products, one PV product
+// over both).
+constexpr int chunks_per_tile(int gp) { return gp >= 8 ? 2 : 16 / (2 * gp); }
+
 // Resolved decode geometry shared by the workspace query and the launch.
 struct DecodePlan {
   int n_split_int2;   // work items per (sequence, KV head) over INT2 chunk tiles
