@@ -324,26 +324,26 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     wait_vmcnt<(RING - 1) * kDmaPerTile>();
     if constexpr (Geo<GP>::SHARED) {
       // Eight heads: the 16 QK columns (head, hi/lo) serve both chunks of
-      // the tile.  Every lane takes the logits of its four tokens of each
-      // chunk, and one 16x16x32 PV product per channel tile covers both
-      // chunks (k-slots 0-3 chunk 0, 4-7 chunk 1).
+      // the tile.  After the hi + lo column sums, the hi lanes (n < 8) keep
+      // the logits of chunk 0 and the lo lanes (n >= 8) take those of chunk
+      // 1 (lane n - 8's sums), so every lane runs the softmax of four tokens
+      // of one chunk.  One 16x16x32 PV product per channel tile covers both
+      // chunks (k-slots 0-3 chunk 0, 4-7 chunk 1): row n < 8 takes the hi
+      // parts of head n's weights, row n + 8 the lo parts.
       uint2 kc0, vc0, kc1, vc1;
-      uint4 kp0, vp0, kp1, vp1;
+      uint4 kp, vp;
       const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot));
       const uint32_t acode = lds + 32u * n + 8u * gq;
-      const uint32_t aprm = lds + 2048u + 16u * gq;
+      const uint32_t aprm = lds + 2048u + (is_hi ? 0u : 128u) + 16u * gq;   // own chunk
       asm volatile(
-          "ds_read_b64 %0, %8\n\t"
-          "ds_read_b64 %1, %8 offset:512\n\t"
-          "ds_read_b64 %2, %8 offset:1024\n\t"
-          "ds_read_b64 %3, %8 offset:1536\n\t"
-          "ds_read_b128 %4, %9\n\t"
-          "ds_read_b128 %5, %9 offset:64\n\t"
-          "ds_read_b128 %6, %9 offset:128\n\t"
-          "ds_read_b128 %7, %9 offset:192\n\t"
+          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %1, %6 offset:512\n\t"
+          "ds_read_b64 %2, %6 offset:1024\n\t"
+          "ds_read_b64 %3, %6 offset:1536\n\t"
+          "ds_read_b128 %4, %7\n\t"
+          "ds_read_b128 %5, %7 offset:64\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(kc0), "=v"(vc0), "=v"(kc1), "=v"(vc1), "=v"(kp0), "=v"(vp0), "=v"(kp1),
-            "=v"(vp1)
+          : "=v"(kc0), "=v"(vc0), "=v"(kc1), "=v"(vc1), "=v"(kp), "=v"(vp)
           : "v"(acode), "v"(aprm)
           : "memory");
       after_reads();
@@ -361,27 +361,27 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[3], c, 0, 0, 0);
         cq[p] = c;
       }
-      float lg[8], zv[8];
-      uint32_t svb[8];
+      // Every lane move below runs with all 64 lanes active and its result
+      // is chosen with bit operations (a conditional expression around a
+      // lane move can become a branch whose moves read inactive lanes).
+      const uint32_t hi_sel = 0u - uint32_t(is_hi);
+      float lg[4], zv[4];
+      uint32_t svb[4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const uint4 kp = p == 0 ? kp0 : kp1;
-        const uint4 vp = p == 0 ? vp0 : vp1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float d = cq[p][r] + dpp_f<0x100 + GP>(cq[p][r]);   // hi + lo columns
-          const uint32_t kpr = r == 0 ? kp.x : r == 1 ? kp.y : r == 2 ? kp.z : kp.w;
-          const uint32_t vpr = r == 0 ? vp.x : r == 1 ? vp.y : r == 2 ? vp.z : vp.w;
-          lg[4 * p + r] = fmaf(f16lo(kpr), d, f16hi(kpr) * qbar_s);
-          svb[4 * p + r] = vpr;
-          zv[4 * p + r] = f16hi(vpr);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float d0 = cq[0][r] + dpp_f<0x100 + GP>(cq[0][r]);   // valid on hi lanes
+        const float d1 = cq[1][r] + dpp_f<0x100 + GP>(cq[1][r]);
+        const float d1m = dpp_f<0x110 + GP>(d1);                   // lo lanes: chunk 1
+        const float d = select_bits(hi_sel, d0, d1m);
+        const uint32_t kpr = r == 0 ? kp.x : r == 1 ? kp.y : r == 2 ? kp.z : kp.w;
+        const uint32_t vpr = r == 0 ? vp.x : r == 1 ? vp.y : r == 2 ? vp.z : vp.w;
+        lg[r] = fmaf(f16lo(kpr), d, f16hi(kpr) * qbar_s);
+        svb[r] = vpr;
+        zv[r] = f16hi(vpr);
       }
-      float tmax = lg[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, lg[i]);
-      if (__builtin_amdgcn_ballot_w64(is_hi && g_ok && tmax > thr) != 0) {
-        const float tm = (is_hi && g_ok) ? tmax * qscale : -INFINITY;
+      const float tmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+      if (__builtin_amdgcn_ballot_w64(g_ok && tmax > thr) != 0) {
+        const float tm = g_ok ? tmax * qscale : -INFINITY;
         float corr[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
@@ -410,32 +410,28 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         m_eff = g_ok ? ml - log2_sigma : INFINITY;
         thr = g_ok ? (ml + kTau) / qscale : INFINITY;
       }
-      float w[8];
+      float w[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(lg[i], qscale, -m_eff));
-        l_lane += p;                     // lo lanes accumulate garbage, masked at the end
-        z_lane = fmaf(p, zv[i], z_lane);
-        w[i] = p * f16lo(svb[i]);
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(lg[r], qscale, -m_eff));
+        l_lane += p;
+        z_lane = fmaf(p, zv[r], z_lane);
+        w[r] = p * f16lo(svb[r]);
       }
-      // f16 hi/lo split per chunk as in the other layouts; lo parts move GP
-      // lanes up (row_shr) into the lo rows
-      uint32_t av[4];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const fp16x2_t h02 = __builtin_amdgcn_cvt_pkrtz(w[4 * p + 0], w[4 * p + 2]);
-        const fp16x2_t h13 = __builtin_amdgcn_cvt_pkrtz(w[4 * p + 1], w[4 * p + 3]);
-        const uint32_t lo02 = __builtin_bit_cast(
-            uint32_t,
-            __builtin_amdgcn_cvt_pkrtz(w[4 * p + 0] - float(h02[0]), w[4 * p + 2] - float(h02[1])));
-        const uint32_t lo13 = __builtin_bit_cast(
-            uint32_t,
-            __builtin_amdgcn_cvt_pkrtz(w[4 * p + 1] - float(h13[0]), w[4 * p + 3] - float(h13[1])));
-        const uint32_t lo02s = dpp_u<0x110 + GP>(lo02), lo13s = dpp_u<0x110 + GP>(lo13);
-        av[2 * p] = is_hi ? __builtin_bit_cast(uint32_t, h02) : lo02s;
-        av[2 * p + 1] = is_hi ? __builtin_bit_cast(uint32_t, h13) : lo13s;
-      }
-      const u32x4_t ap = {av[0], av[1], av[2], av[3]};
+      const fp16x2_t h02 = __builtin_amdgcn_cvt_pkrtz(w[0], w[2]);
+      const fp16x2_t h13 = __builtin_amdgcn_cvt_pkrtz(w[1], w[3]);
+      const uint32_t hi02 = __builtin_bit_cast(uint32_t, h02), hi13 = __builtin_bit_cast(uint32_t, h13);
+      const uint32_t lo02 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0] - float(h02[0]), w[2] - float(h02[1])));
+      const uint32_t lo13 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_pkrtz(w[1] - float(h13[0]), w[3] - float(h13[1])));
+      // row n < 8: hi parts of chunk 0 (own) and chunk 1 (lane n + 8);
+      // row n + 8: lo parts of chunk 0 (lane n) and chunk 1 (own)
+      const uint32_t hi02u = dpp_u<0x100 + GP>(hi02), hi13u = dpp_u<0x100 + GP>(hi13);
+      const uint32_t lo02d = dpp_u<0x110 + GP>(lo02), lo13d = dpp_u<0x110 + GP>(lo13);
+      auto pick = [&](uint32_t a, uint32_t b) { return (a & hi_sel) | (b & ~hi_sel); };
+      const u32x4_t ap = {pick(hi02, lo02d), pick(hi13, lo13d), pick(hi02u, lo02),
+                          pick(hi13u, lo13)};
       const half8_t A = __builtin_bit_cast(half8_t, ap);
       const uint32_t e0 = vc0.x, e1 = vc0.y, f0 = vc1.x, f1 = vc1.y;
       const uint32_t e0s = e0 >> 8, e1s = e1 >> 8, f0s = f0 >> 8, f1s = f1 >> 8;
@@ -664,10 +660,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
 
   // ---- wave epilogue: per-head l, z and o' into LDS -----------------------
   float l_h[GP], z_h[GP];
+  // (in the eight-head layout the lo lanes hold the sums of the tiles'
+  // second chunks, for the same heads)
+  constexpr bool kAllLanes = Geo<GP>::SHARED;
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
-    l_h[g] = wave_sum((is_hi && g_col == g) ? l_lane : 0.f);
-    z_h[g] = wave_sum((is_hi && g_col == g) ? z_lane : 0.f);
+    l_h[g] = wave_sum(((kAllLanes || is_hi) && g_col == g) ? l_lane : 0.f);
+    z_h[g] = wave_sum(((kAllLanes || is_hi) && g_col == g) ? z_lane : 0.f);
   }
 #pragma unroll
   for (int J = 0; J < 8; ++J) {
@@ -720,7 +719,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
 template <int GP>
 __device__ void token_slice_item(const DecodeArgs& a, int idx) {
   constexpr int NPT = Geo<GP>::NPT;
-  constexpr int RING = Geo<GP>::RING;
   __shared__ float qsum[GP];
   __shared__ int qexp[GP];
   const int S = a.n_tok_slices;
