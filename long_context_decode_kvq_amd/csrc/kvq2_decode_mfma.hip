@@ -838,8 +838,14 @@ int resident_work_groups() {
 // Work-groups of the equal-range decode: one round of resident work-groups,
 // but no more than one per kMinTilesPerGroup tiles (bounded above from
 // max_seq_len), so that short or few sequences are not cut into pieces whose
-// fixed cost (prologue, partial, combine) dominates.
+// fixed cost (prologue, partial, combine) dominates -- yet one per CU while
+// each still gets kMinTilesPerCuGroup tiles, so that small batches fill the
+// GPU (measured at batch 1: 32768 tokens 46.8 -> 37.4 us per step with 256
+// work-groups instead of 64; more than one round of small ranges was slower).
 constexpr int kMinTilesPerGroup = 128;
+constexpr int kMinTilesPerCuGroup = 32;
+
+int device_cus();
 
 template <int GP>
 int chain_grid(const DecodeArgs& a, int batch, int max_seq_len) {
@@ -847,7 +853,10 @@ int chain_grid(const DecodeArgs& a, int batch, int max_seq_len) {
   const int64_t int2_end = std::max<int64_t>(a.n_sink, int64_t(max_seq_len) - a.n_recent);
   const int64_t tiles = std::max<int64_t>(1, (int2_end / kChunkTokens) / NPT);
   const int64_t est = int64_t(batch) * a.n_kv_heads * tiles;
-  const int64_t want = (est + kMinTilesPerGroup - 1) / kMinTilesPerGroup;
+  const int64_t cus = std::max(1, device_cus());
+  const int64_t want = std::max<int64_t>(
+      (est + kMinTilesPerGroup - 1) / kMinTilesPerGroup,
+      std::min<int64_t>(cus, est / kMinTilesPerCuGroup));
   return int(std::max<int64_t>(
       1, std::min<int64_t>(want, std::min(kChainGroups, resident_work_groups<GP>()))));
 }
