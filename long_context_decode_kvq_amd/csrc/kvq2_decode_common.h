@@ -556,6 +556,113 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   }
 }
 
+// Split-K combine of one query head g of (b, h), by a work-group of 256
+// threads in a kernel of its own (one work-group per query head, so that a
+// small batch still spreads its combines over many CUs): the partials in
+// slots [base_slot, base_slot + n_parts) and [tok_slot, tok_slot + n_tok),
+// with M = max m_s, f_s = 2^(m_s - M): o' = sum f_s o'_s / sum f_s l_s, then
+// o = R_V o' to `out`.  Thread (half, c) takes channel c of the slots of its
+// half of each round (kRound slots per half, all loads in flight together;
+// the (m, l) of a round are staged in LDS once), the halves merge in LDS;
+// R_V row c is loaded first.
+template <int GP>
+__device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t base_slot,
+                             int n_parts, int64_t tok_slot, int n_tok) {
+  constexpr int kRound = 16;   // slots per half per round
+  __shared__ float s_ml[2 * kRound][2];
+  __shared__ float s_part[2][3][kHeadDim];   // per half: M, den, acc
+  __shared__ float ocomb[kHeadDim];
+  __shared__ float red[2][kHeadDim];
+  const int G = a.group;
+  const int tid = threadIdx.x;
+  const int c = tid & (kHeadDim - 1), half = tid >> 7;
+  float4 r[16];
+  {
+    const float4* row = reinterpret_cast<const float4*>(
+        a.R_V + int64_t(h) * kHeadDim * kHeadDim + c * kHeadDim + 64 * half);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = row[j];
+  }
+  auto slot_ptr = [&](int i) -> const float* {
+    const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    return a.partials + (s * G + g) * kPartialStride;
+  };
+  const int n_all = n_parts + n_tok;
+  float M = -INFINITY, den = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < n_all; s0 += 2 * kRound) {
+    const int ns = min(2 * kRound, n_all - s0);
+    if (tid < 2 * ns) {
+      const float* p = slot_ptr(s0 + (tid >> 1));
+      s_ml[tid >> 1][tid & 1] = p[tid & 1];
+    }
+    float ov[kRound];
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+      const int i = half * kRound + k;
+      ov[k] = slot_ptr(s0 + min(i, ns - 1))[4 + c];   // past the round: re-read, unused
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+      const int i = half * kRound + k;
+      if (i < ns) mx = fmaxf(mx, s_ml[i][0]);
+    }
+    const float nM = fmaxf(M, mx);
+    if (nM != -INFINITY) {
+      const float sc = M == -INFINITY ? 0.f : exp2f(M - nM);
+      acc *= sc;
+      den *= sc;
+#pragma unroll
+      for (int k = 0; k < kRound; ++k) {
+        const int i = half * kRound + k;
+        if (i < ns) {
+          const float mi = s_ml[i][0];
+          const float f = mi == -INFINITY ? 0.f : exp2f(mi - nM);
+          acc = fmaf(f, ov[k], acc);
+          den = fmaf(f, s_ml[i][1], den);
+        }
+      }
+      M = nM;
+    }
+    __syncthreads();   // s_ml is refilled by the next round
+  }
+  s_part[half][0][c] = M;
+  s_part[half][1][c] = den;
+  s_part[half][2][c] = acc;
+  __syncthreads();
+  if (half == 0) {
+    const float M1 = s_part[1][0][c], d1 = s_part[1][1][c], a1 = s_part[1][2][c];
+    const float nM = fmaxf(M, M1);
+    float o = 0.f;
+    if (nM != -INFINITY) {
+      const float f0 = M == -INFINITY ? 0.f : exp2f(M - nM);
+      const float f1 = M1 == -INFINITY ? 0.f : exp2f(M1 - nM);
+      const float dd = f0 * den + f1 * d1;
+      o = dd > 0.f ? (f0 * acc + f1 * a1) / dd : 0.f;
+    }
+    ocomb[c] = o;
+  }
+  __syncthreads();
+  // o = R_V o' (row-major R_V: o_c = sum_j R_V[c][j] o'_j); thread (half, c)
+  // sums half of row c, the halves meet in LDS.
+  {
+    const float* oc = &ocomb[64 * half];
+    float o = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      o = fmaf(r[j].x, oc[4 * j + 0], o);
+      o = fmaf(r[j].y, oc[4 * j + 1], o);
+      o = fmaf(r[j].z, oc[4 * j + 2], o);
+      o = fmaf(r[j].w, oc[4 * j + 3], o);
+    }
+    red[half][c] = o;
+  }
+  __syncthreads();
+  if (tid < kHeadDim)
+    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + tid] = red[0][tid] + red[1][tid];
+}
+
 // Merge the 4 waves' states (see merge_wave_states) and store the
 // work-group's partial in slot `part_slot` of the workspace.  Then take an
 // arrival ticket of (b, h); the last of its n_parts work-groups combines the

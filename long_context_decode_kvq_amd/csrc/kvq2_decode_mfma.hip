@@ -791,19 +791,24 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
   }
 }
 
-// Split-K combine, one work-group per (KV head h, sequence b): the pieces'
-// partials of (b, h) (slots i0 + p .. i1 + p, p = b Hkv + h, with i0, i1 the
-// first and last range touching it) and its token-list slices from the
-// pre-pass.  A kernel of its own: it starts once every partial is written,
-// with HBM idle, so its few dependent loads are short.
+// Split-K combine of (b, h): the pieces' partials (slots i0 + p .. i1 + p,
+// p = b Hkv + h, with i0, i1 the first and last range touching it) and its
+// token-list slices.  A kernel of its own: it starts once every partial is
+// written, with HBM idle, so its few dependent loads are short.  One
+// work-group per (KV head, sequence) for large batches; per (KV head,
+// sequence, query head) when there are few (sequence, KV head) pairs, so
+// that a small batch's combine spreads over more CUs (grid z = 1 or G).
 template <int GP>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int p = b * a.n_kv_heads + h;
   const int pr = a.pair_range[p];
   const int i0 = pr & 0xFFFF, i1 = pr >> 16;
-  combine_pair<GP>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, a.tok_slot0 + int64_t(p) * a.n_tok_slices,
-                   a.n_tok_slices);
+  const int64_t tok = a.tok_slot0 + int64_t(p) * a.n_tok_slices;
+  if (gridDim.z == 1)
+    combine_pair<GP>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices);
+  else
+    combine_head<GP>(a, b, h, blockIdx.z, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices);
 }
 
 }  // namespace
@@ -912,7 +917,8 @@ int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* st
   // G = 1 runs the two-head kernel with one padding head.
   // the streaming work-groups, then one per token-list slice of every (b, h)
   const dim3 grid(a.chain_groups + a.batch * a.n_kv_heads * a.n_tok_slices),
-      cgrid(a.n_kv_heads, a.batch);
+      cgrid(a.n_kv_heads, a.batch,
+            2 * a.batch * a.n_kv_heads < std::max(1, device_cus()) ? a.group : 1);
   if (G <= 2) {
     hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(combine_kernel<2>, cgrid, dim3(256), 0, st, a);
