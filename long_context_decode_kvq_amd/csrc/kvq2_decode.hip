@@ -1,6 +1,8 @@
-// Decode dispatch: fills the kernel arguments from the validated ABI
-// structures, carves the caller's workspace into arrival counters and
-// split-K partials, and launches the selected decode kernel.
+// Decode dispatch and pre-pass: fills the kernel arguments from the
+// validated ABI structures, carves the caller's workspace (arrival counters,
+// rotated queries, QK operands, range plan, split-K partials), launches the
+// q-rotation / range-plan pre-pass (fused with the decode-step append for
+// kvq_decode_step) and then the selected decode kernel.
 #include <algorithm>
 #include <cmath>
 

@@ -1,6 +1,8 @@
-// Pieces shared by the decode kernels: the query-rotation prologue, the
-// work-group merge of per-wave softmax states, the split-K partial store and
-// the last-arrival combine with the output inverse rotation.
+// Pieces shared by the decode kernels: the kernel arguments, the INT2
+// range and token-list geometry, the token-by-token tile, the work-group
+// merge of per-wave softmax states, the split-K partial store and the
+// combines with the output inverse rotation (per (b, h) or per query head
+// for the MFMA decode, last-arrival for the VALU decode).
 //
 // OSCAR technical summary, sec. 2.2-B: the fused kernel undoes the rotation;
 // here that is done exactly once per query head on each side: q' = R_K^T q
