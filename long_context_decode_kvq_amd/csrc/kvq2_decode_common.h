@@ -558,32 +558,35 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   }
 }
 
-// Split-K combine of one query head g of (b, h), by a work-group of 256
+// Split-K combine of one query head g of (b, h), by a work-group of NQ x 128
 // threads in a kernel of its own (one work-group per query head, so that a
 // small batch still spreads its combines over many CUs): the partials in
 // slots [base_slot, base_slot + n_parts) and [tok_slot, tok_slot + n_tok),
 // with M = max m_s, f_s = 2^(m_s - M): o' = sum f_s o'_s / sum f_s l_s, then
-// o = R_V o' to `out`.  Thread (half, c) takes channel c of the slots of its
-// half of each round (kRound slots per half, all loads in flight together;
-// the (m, l) of a round are staged in LDS once), the halves merge in LDS;
-// R_V row c is loaded first.
-template <int GP>
+// o = R_V o' to `out`.  Thread (part, c) takes channel c of the slots of its
+// part of each round (kRound slots per part, all loads in flight together;
+// the (m, l) of a round are staged in LDS once), and the NQ parts merge in
+// LDS; R_V row c is loaded first, 128 / NQ columns per thread.  With NQ = 8
+// a round covers 128 slots: the split count of a batch-1 decode (about 70)
+// takes one round of dependent loads instead of three.
+template <int GP, int NQ>
 __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t base_slot,
                              int n_parts, int64_t tok_slot, int n_tok) {
-  constexpr int kRound = 16;   // slots per half per round
-  __shared__ float s_ml[2 * kRound][2];
-  __shared__ float s_part[2][3][kHeadDim];   // per half: M, den, acc
+  constexpr int kRound = 16;              // slots per part per round
+  constexpr int kCols = kHeadDim / NQ;    // R_V columns per thread
+  __shared__ float s_ml[NQ * kRound][2];
+  __shared__ float s_part[NQ][3][kHeadDim];   // per part: M, den, acc
   __shared__ float ocomb[kHeadDim];
-  __shared__ float red[2][kHeadDim];
+  __shared__ float red[NQ][kHeadDim];
   const int G = a.group;
   const int tid = threadIdx.x;
-  const int c = tid & (kHeadDim - 1), half = tid >> 7;
-  float4 r[16];
+  const int c = tid & (kHeadDim - 1), part = tid >> 7;
+  float4 r[kCols / 4];
   {
     const float4* row = reinterpret_cast<const float4*>(
-        a.R_V + int64_t(h) * kHeadDim * kHeadDim + c * kHeadDim + 64 * half);
+        a.R_V + int64_t(h) * kHeadDim * kHeadDim + c * kHeadDim + kCols * part);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) r[j] = row[j];
+    for (int j = 0; j < kCols / 4; ++j) r[j] = row[j];
   }
   auto slot_ptr = [&](int i) -> const float* {
     const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
@@ -591,8 +594,8 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
   };
   const int n_all = n_parts + n_tok;
   float M = -INFINITY, den = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < n_all; s0 += 2 * kRound) {
-    const int ns = min(2 * kRound, n_all - s0);
+  for (int s0 = 0; s0 < n_all; s0 += NQ * kRound) {
+    const int ns = min(NQ * kRound, n_all - s0);
     if (tid < 2 * ns) {
       const float* p = slot_ptr(s0 + (tid >> 1));
       s_ml[tid >> 1][tid & 1] = p[tid & 1];
@@ -600,14 +603,14 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
     float ov[kRound];
 #pragma unroll
     for (int k = 0; k < kRound; ++k) {
-      const int i = half * kRound + k;
+      const int i = part * kRound + k;
       ov[k] = slot_ptr(s0 + min(i, ns - 1))[4 + c];   // past the round: re-read, unused
     }
     __syncthreads();
     float mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kRound; ++k) {
-      const int i = half * kRound + k;
+      const int i = part * kRound + k;
       if (i < ns) mx = fmaxf(mx, s_ml[i][0]);
     }
     const float nM = fmaxf(M, mx);
@@ -617,7 +620,7 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
       den *= sc;
 #pragma unroll
       for (int k = 0; k < kRound; ++k) {
-        const int i = half * kRound + k;
+        const int i = part * kRound + k;
         if (i < ns) {
           const float mi = s_ml[i][0];
           const float f = mi == -INFINITY ? 0.f : exp2f(mi - nM);
@@ -629,40 +632,50 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
     }
     __syncthreads();   // s_ml is refilled by the next round
   }
-  s_part[half][0][c] = M;
-  s_part[half][1][c] = den;
-  s_part[half][2][c] = acc;
+  s_part[part][0][c] = M;
+  s_part[part][1][c] = den;
+  s_part[part][2][c] = acc;
   __syncthreads();
-  if (half == 0) {
-    const float M1 = s_part[1][0][c], d1 = s_part[1][1][c], a1 = s_part[1][2][c];
-    const float nM = fmaxf(M, M1);
+  if (part == 0) {
+    float nM = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) nM = fmaxf(nM, s_part[q][0][c]);
     float o = 0.f;
     if (nM != -INFINITY) {
-      const float f0 = M == -INFINITY ? 0.f : exp2f(M - nM);
-      const float f1 = M1 == -INFINITY ? 0.f : exp2f(M1 - nM);
-      const float dd = f0 * den + f1 * d1;
-      o = dd > 0.f ? (f0 * acc + f1 * a1) / dd : 0.f;
+      float dd = 0.f, oo = 0.f;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float Mq = s_part[q][0][c];
+        const float f = Mq == -INFINITY ? 0.f : exp2f(Mq - nM);
+        dd = fmaf(f, s_part[q][1][c], dd);
+        oo = fmaf(f, s_part[q][2][c], oo);
+      }
+      o = dd > 0.f ? oo / dd : 0.f;
     }
     ocomb[c] = o;
   }
   __syncthreads();
-  // o = R_V o' (row-major R_V: o_c = sum_j R_V[c][j] o'_j); thread (half, c)
-  // sums half of row c, the halves meet in LDS.
+  // o = R_V o' (row-major R_V: o_c = sum_j R_V[c][j] o'_j); thread (part, c)
+  // sums its columns of row c, the parts meet in LDS.
   {
-    const float* oc = &ocomb[64 * half];
+    const float* oc = &ocomb[kCols * part];
     float o = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kCols / 4; ++j) {
       o = fmaf(r[j].x, oc[4 * j + 0], o);
       o = fmaf(r[j].y, oc[4 * j + 1], o);
       o = fmaf(r[j].z, oc[4 * j + 2], o);
       o = fmaf(r[j].w, oc[4 * j + 3], o);
     }
-    red[half][c] = o;
+    red[part][c] = o;
   }
   __syncthreads();
-  if (tid < kHeadDim)
-    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + tid] = red[0][tid] + red[1][tid];
+  if (tid < kHeadDim) {
+    float o = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) o += red[q][tid];
+    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + tid] = o;
+  }
 }
 
 // Merge the 4 waves' states (see merge_wave_states) and store the

@@ -795,9 +795,11 @@ __global__ __launch_bounds__(256, GP <= 4 ? 4 : 2) void decode_mfma_kernel(Decod
 // p = b Hkv + h, with i0, i1 the first and last range touching it) and its
 // token-list slices.  A kernel of its own: it starts once every partial is
 // written, with HBM idle, so its few dependent loads are short.  One
-// work-group per (KV head, sequence) for large batches; per (KV head,
-// sequence, query head) when there are few (sequence, KV head) pairs, so
-// that a small batch's combine spreads over more CUs (grid z = 1 or G).
+// 256-thread work-group per (KV head, sequence) for large batches
+// (combine_kernel); one 1024-thread work-group per (KV head, sequence, query
+// head) when there are few (sequence, KV head) pairs, so that a small
+// batch's combine spreads over more CUs and takes its many splits in one
+// round (combine_head_kernel).
 template <int GP>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
@@ -805,10 +807,20 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int pr = a.pair_range[p];
   const int i0 = pr & 0xFFFF, i1 = pr >> 16;
   const int64_t tok = a.tok_slot0 + int64_t(p) * a.n_tok_slices;
-  if (gridDim.z == 1)
-    combine_pair<GP>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices);
-  else
-    combine_head<GP>(a, b, h, blockIdx.z, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices);
+  combine_pair<GP>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices);
+}
+
+constexpr int kHeadCombineParts = 8;   // 128-thread parts of a combine_head_kernel work-group
+
+template <int GP>
+__global__ __launch_bounds__(128 * kHeadCombineParts) void combine_head_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int p = b * a.n_kv_heads + h;
+  const int pr = a.pair_range[p];
+  const int i0 = pr & 0xFFFF, i1 = pr >> 16;
+  const int64_t tok = a.tok_slot0 + int64_t(p) * a.n_tok_slices;
+  combine_head<GP, kHeadCombineParts>(a, b, h, blockIdx.z, int64_t(i0) + p, i1 - i0 + 1, tok,
+                                      a.n_tok_slices);
 }
 
 }  // namespace
@@ -916,18 +928,22 @@ int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* st
   (void)max_seq_len;
   // G = 1 runs the two-head kernel with one padding head.
   // the streaming work-groups, then one per token-list slice of every (b, h)
-  const dim3 grid(a.chain_groups + a.batch * a.n_kv_heads * a.n_tok_slices),
-      cgrid(a.n_kv_heads, a.batch,
-            2 * a.batch * a.n_kv_heads < std::max(1, device_cus()) ? a.group : 1);
+  const dim3 grid(a.chain_groups + a.batch * a.n_kv_heads * a.n_tok_slices);
+  const bool per_head = 2 * a.batch * a.n_kv_heads < std::max(1, device_cus());
+  const dim3 cgrid(a.n_kv_heads, a.batch, per_head ? a.group : 1);
+  const dim3 cblock(per_head ? 128 * kHeadCombineParts : 256);
   if (G <= 2) {
     hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(combine_kernel<2>, cgrid, dim3(256), 0, st, a);
+    if (per_head) hipLaunchKernelGGL(combine_head_kernel<2>, cgrid, cblock, 0, st, a);
+    else hipLaunchKernelGGL(combine_kernel<2>, cgrid, cblock, 0, st, a);
   } else if (G <= 4) {
     hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(combine_kernel<4>, cgrid, dim3(256), 0, st, a);
+    if (per_head) hipLaunchKernelGGL(combine_head_kernel<4>, cgrid, cblock, 0, st, a);
+    else hipLaunchKernelGGL(combine_kernel<4>, cgrid, cblock, 0, st, a);
   } else {
     hipLaunchKernelGGL(decode_mfma_kernel<8>, grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(256), 0, st, a);
+    if (per_head) hipLaunchKernelGGL(combine_head_kernel<8>, cgrid, cblock, 0, st, a);
+    else hipLaunchKernelGGL(combine_kernel<8>, cgrid, cblock, 0, st, a);
   }
   return static_cast<int>(hipGetLastError());
 }
