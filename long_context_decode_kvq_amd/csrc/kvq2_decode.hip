@@ -72,15 +72,28 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   // Work-group j weighs round_weight[j / rsz] * xcd_weight[j % 8]; range i
   // starts at total * (weight of work-groups < i) / (weight of all).  A round
   // (rsz, a multiple of 8 when weighted) holds every XCD rsz / 8 times.
+  // The weights are held in registers and the loops have fixed trip counts:
+  // read from the argument block term by term, the dependent loads made this
+  // cut the longest part of the pre-pass.
+  int xw[8], rw[4];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) xw[x] = a.xcd_weight[x];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rw[r] = a.round_weight[r];
   int64_t xsum = 0;
-  for (int x = 0; x < 8; ++x) xsum += a.xcd_weight[x];
-  auto xcd_prefix = [&](int64_t k) {   // sum of xcd_weight[j % 8] over j < k
-    int64_t c = (k / 8) * xsum;
-    for (int x = 0; x < int(k % 8); ++x) c += a.xcd_weight[x];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) xsum += xw[x];
+  auto xcd_prefix = [&](int64_t k) {   // sum of xcd_weight[j % 8] over j < k (k >= 0)
+    int64_t c = (k >> 3) * xsum;
+    const int m = static_cast<int>(k & 7);
+#pragma unroll
+    for (int x = 0; x < 7; ++x) c += x < m ? xw[x] : 0;
     return c;
   };
   int64_t ctot = 0;
-  for (int r = 0; r < rounds; ++r) ctot += int64_t(a.round_weight[r]) * xcd_prefix(rsz);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (r < rounds) ctot += int64_t(rw[r]) * xcd_prefix(rsz);
   const int64_t q = (total + nwg - 1) / nwg;
   for (int i = tid; i <= nwg; i += blockDim.x) {
     int64_t v;
@@ -88,10 +101,13 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
       v = min(total, int64_t(i) * q);
     } else {
       int64_t c = 0;
-      for (int r = 0; r < rounds; ++r) {
-        const int64_t lo = int64_t(r) * rsz;
-        const int64_t cnt = i <= lo ? 0 : min(int64_t(i), lo + rsz) - lo;
-        c += int64_t(a.round_weight[r]) * xcd_prefix(cnt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < rounds) {
+          const int64_t lo = int64_t(r) * rsz;
+          const int64_t cnt = i <= lo ? 0 : min(int64_t(i), lo + rsz) - lo;
+          c += int64_t(rw[r]) * xcd_prefix(cnt);
+        }
       }
       v = total * c / ctot;
     }
