@@ -135,3 +135,15 @@ def test_workspace_reuse_keeps_counters_at_zero(kernel):
     assert np.array_equal(out.cpu().numpy(), out1)
     n_heads = sc.B * 2
     assert int(ws[: 4 * n_heads].view(torch.int32).abs().sum()) == 0
+
+
+def test_small_batch_combine_over_two_rounds(kernel):
+    """A batch-1 decode whose split count exceeds one round of the per-query-
+    head combine (8 parts x 16 slots = 128): an 8192-token recent window
+    makes 129 token-list slices besides the INT2 piece, so the combine takes
+    its slots in two rounds."""
+    sc = Scenario(4, 1, 16, 4, 8192, [10000], seed=12)
+    sc.fill_to(pieces=2)
+    out, ref, _ = sc.decode()
+    assert np.isfinite(out).all()
+    assert rel_err(out, ref) <= TOL
