@@ -31,6 +31,7 @@ CASES = [
     (2, 2, 64, 20, 5, [400, 26, 130]),                 # G = 1, page 64, sink > 16
     (16, 1, 16, 4, 1, [97, 5]),                        # G = 16, W = 1
     (6, 2, 16, 3, 32, [333, 64]),                      # G = 3 (padded group)
+    (8, 2, 32, 4, 8, [70, 45, 0, 1, 4, 12, 13, 300]),  # ragged batch incl. empty, G = 4, page 32
 ]
 
 
