@@ -23,6 +23,7 @@ STEP_CASES = [
     (8, 1, 32, 0, 16, [120, 50], [100, 20]),            # G = 8, no sink
     (6, 2, 16, 3, 32, [333, 64], [300, 30]),            # G = 3 (padded group)
     (16, 1, 16, 4, 1, [40, 8], [30, 2]),                # G = 16 (VALU decode), W = 1
+    (8, 2, 32, 4, 8, [40, 0, 13, 20], [30, 0, 9, 19]),  # an empty sequence; one that stops growing
 ]
 
 
