@@ -148,3 +148,26 @@ def test_small_batch_combine_over_two_rounds(kernel):
     out, ref, _ = sc.decode()
     assert np.isfinite(out).all()
     assert rel_err(out, ref) <= TOL
+
+
+def test_max_seq_len_above_the_lengths(kernel):
+    """max_seq_len is a bound that sizes the launch and the workspace; a
+    caller may pass its capacity rather than the longest length.  With a
+    bound four times the longest sequence the outputs still match the oracle."""
+    import long_context_decode_kvq_amd.kvq2 as K
+    from gpu_helpers import dev_u16
+    from long_context_decode_kvq_amd.workloads import normal_bits
+    cap = 2800
+    sc = Scenario(4, 2, 16, 4, 16, [cap, 90, 3], seed=17)   # block table for `cap` tokens
+    sc.append([700, 90, 3])
+    _, ref, _ = sc.decode()
+    assert cap == 4 * max(sc.cur)
+    ws = torch.zeros(K.decode_workspace_bytes(sc.kd, sc.B, cap), dtype=torch.uint8, device="cuda")
+    seq = torch.tensor(sc.cur, dtype=torch.int32, device="cuda")
+    q = normal_bits(sc.seed * 31 + 99, (sc.B, 4, 128))
+    out = torch.empty((sc.B, 4, 128), dtype=torch.float32, device="cuda")
+    K.decode_attention(sc.kd, sc.layer, sc.dc.handle, sc.B, seq, cap, dev_u16(q), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= TOL
