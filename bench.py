@@ -338,7 +338,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # products on the f16 matrix cores (INT2 codes exact, q' and the
+        # softmax weights as f16 hi + lo pairs), fp32 accumulation, softmax
+        # and combine
+        "dtype": "f16/f32",
         "data": "synthetic",
         "config": {
             "workload": w.name,
