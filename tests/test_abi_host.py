@@ -178,6 +178,21 @@ def test_calibrate_matches_oracle_on_separated_spectrum():
     assert abs(cV - cal.clip_V) <= ulp(cal.clip_V)
 
 
+def test_calibrate_closed_form_wiring():
+    """kvq_calibrate on data whose eigenbases are known in closed form
+    (tests/calib_fixture.py): R_K[h] = U_Q(h) H P and R_V[h] = U_S(h) H P
+    for KV head h's own query heads, one clip per tensor."""
+    from calib_fixture import ClosedFormCalibration
+    for Hq, Hkv, seed in ((4, 2, 2024), (12, 3, 7)):
+        fx = ClosedFormCalibration(n_q_heads=Hq, n_kv_heads=Hkv, seed=seed)
+        d = kvq2.dims(Hq, Hkv, 16, 4, 128)
+        R_K, R_V, cK, cV = kvq2.calibrate(d, fx.q, fx.k, fx.v, 1.0)
+        for h in range(Hkv):
+            assert np.abs(R_K[h] - fx.R_K[h]).max() <= 1e-6, f"R_K[{h}]"
+            assert np.abs(R_V[h] - fx.R_V[h]).max() <= 1e-6, f"R_V[{h}]"
+        assert (cK, cV) == (fx.clip_K, fx.clip_V)
+
+
 def test_calibrate_invariants_on_isotropic_data():
     """iid queries: C_Q ~ I and the eigenbasis is noise; check invariants only."""
     rng = np.random.default_rng(3)

@@ -178,6 +178,38 @@ def test_calibrate_clip_p1_is_max_and_R_orthogonal():
     assert np.all(np.diff(cal.eig_Q, axis=1) <= 0)
 
 
+def test_calibrate_wiring_closed_form():
+    """R_K[h] = U_Q(h) H P and R_V[h] = U_S(h) H P, with U_Q from the pooled
+    queries of KV head h's own query heads (h G .. h G + G - 1), U_S from the
+    attention outputs of those queries over head h's keys and values, and
+    one clip per tensor (p = 1: the largest |rotated value|), on data whose
+    eigenbases are known in closed form (tests/calib_fixture.py)."""
+    from calib_fixture import ClosedFormCalibration
+    fx = ClosedFormCalibration(n_q_heads=4, n_kv_heads=2)
+    cal = O.calibrate(fx.q, fx.k, fx.v, 4, 2, 1 / math.sqrt(128), clip_quantile=1.0)
+    for h in range(2):
+        assert np.abs(cal.R_K[h] - fx.R_K[h].astype(np.float32)).max() <= 1e-7, f"R_K[{h}]"
+        assert np.abs(cal.R_V[h] - fx.R_V[h].astype(np.float32)).max() <= 1e-7, f"R_V[{h}]"
+        assert np.allclose(cal.eig_Q[h], fx.eig_Q[h], rtol=1e-12, atol=0)
+        assert np.allclose(cal.eig_S[h], fx.eig_S[h], rtol=1e-9, atol=0)
+    assert cal.clip_K == fx.clip_K
+    assert cal.clip_V == fx.clip_V
+    assert fx.clip_K != fx.clip_V
+
+
+def test_calibrate_wiring_eight_heads_per_kv_head():
+    """The same closed form with G = 4 and three KV heads (query heads
+    4h .. 4h + 3 belong to KV head h)."""
+    from calib_fixture import ClosedFormCalibration
+    fx = ClosedFormCalibration(n_q_heads=12, n_kv_heads=3, seed=7)
+    cal = O.calibrate(fx.q, fx.k, fx.v, 12, 3, 1 / math.sqrt(128), clip_quantile=1.0)
+    for h in range(3):
+        assert np.abs(cal.R_K[h] - fx.R_K[h].astype(np.float32)).max() <= 1e-7, f"R_K[{h}]"
+        assert np.abs(cal.R_V[h] - fx.R_V[h].astype(np.float32)).max() <= 1e-7, f"R_V[{h}]"
+        assert np.allclose(cal.eig_Q[h], fx.eig_Q[h], rtol=1e-12, atol=0)
+    assert (cal.clip_K, cal.clip_V) == (fx.clip_K, fx.clip_V)
+
+
 # ---------------------------------------------------------------- pinned rotation
 
 def test_rotate_identity_permutation_and_hadamard():
