@@ -334,7 +334,6 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
   a.q = q;
   a.out = out;
   a.tickets = static_cast<int32_t*>(workspace);
-  a.work_counter = a.tickets + int64_t(batch) * d.n_kv_heads;
   a.batch = batch;
   char* ws = static_cast<char*>(workspace);
   a.qrot = reinterpret_cast<float*>(ws + plan.ticket_bytes);
@@ -352,8 +351,6 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
   const int G = a.group;
   a.gp = (which == kDecodeValu || G > 8) ? 0 : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
   a.n_split_int2 = plan.n_split_int2;
-  a.n_split_big = plan.n_split_big;
-  a.n_split_small = plan.n_split_small;
   a.n_split = plan.n_split;
   a.piece_cost = plan.piece_cost;
   a.n_tok_slices = plan.n_tok_slices;

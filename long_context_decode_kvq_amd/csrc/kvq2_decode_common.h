@@ -34,17 +34,15 @@ struct DecodeArgs {
   const int32_t* seq_len;
   const uint16_t* q;
   float* out;
-  int32_t* tickets;            // [B * Hkv]
-  int32_t* work_counter;       // [2]: next work item, work-groups finished
+  int32_t* tickets;            // [B * Hkv] (VALU decode)
   int batch;
   float* qrot;                 // [B][Hq][kQStride]: alpha R_K^T q, its sum, f16 exponent
   uint32_t* bq;                // [B * Hkv][kBqWords]: QK MFMA operand and lane constants
   int gp;                      // MFMA head-group width (2, 4 or 8)
-  float* partials;             // [B][Hkv][n_split][G][kPartialStride]
-  int n_split_int2;            // INT2 splits per (b, h) = n_split_big + n_split_small
-  int n_split_big;             // splits over the first 3/4 of the tiles (scheduled first)
-  int n_split_small;           // splits over the last 1/4 (scheduled after every big one)
-  int n_split;
+  float* partials;             // MFMA: slots [range + pair], then token-list slices;
+                               // VALU: [B][Hkv][n_split]; each slot [G][kPartialStride]
+  int n_split_int2;            // VALU decode: even INT2 splits per (b, h)
+  int n_split;                 // VALU decode: n_split_int2 + the bf16 work-group
   // MFMA decode: tile_prefix[b] = sum over b' < b of W_b' (B + 1 entries,
   // written by the pre-pass), W_b = max(1, INT2 tiles of sequence b) +
   // piece_cost; the launch cuts the concatenated W_b of all (b, h) into equal
@@ -76,11 +74,11 @@ struct DecodeArgs {
 };
 
 // INT2 work of a sequence of length L is split in two parts:
-//  * whole tiles of `npt` fully valid 16-token chunks [cf, cl), cut into
-//    n_split_int2 contiguous tile ranges (one per split work-group);
+//  * whole tiles of `npt` fully valid 16-token chunks [cf, cl), streamed in
+//    contiguous tile ranges;
 //  * the few INT2 positions outside them (the partial chunk after the sink,
 //    the partial chunk before the recent window and a sub-tile remainder),
-//    which the work-group of the bf16 segments handles token by token.
+//    which are handled token by token with the bf16 segments.
 struct Int2Range {
   int int2_end;   // INT2 positions are [n_sink, int2_end)
   int cf, cl;     // tiled chunks [cf, cl), cl - cf a multiple of npt
@@ -95,23 +93,12 @@ __device__ __forceinline__ Int2Range int2_range(const DecodeArgs& a, int L, int 
   return r;
 }
 
-// Tile range [t_begin, t_end) of INT2 split s.  Splits s < n_split_big
-// share the first 3/4 of the n tiles evenly, the n_split_small others the
-// rest: the work queue hands out every big split before any small one, so
-// the launch ends on short items (with n_split_small = 0, one even split).
+// Tile range [t_begin, t_end) of INT2 split s of n_split_int2 even splits.
 __device__ __forceinline__ void split_tiles(const DecodeArgs& a, const Int2Range& r, int npt, int s,
                                             int& t_begin, int& t_end) {
   const int n = (r.cl - r.cf) / npt;
-  const int nb = a.n_split_big, nsm = a.n_split_small;
-  const int n_big = nsm > 0 ? (3 * n) / 4 : n;   // tiles of the big splits
-  if (s < nb) {
-    t_begin = int(int64_t(n_big) * s / nb);
-    t_end = int(int64_t(n_big) * (s + 1) / nb);
-  } else {
-    const int j = s - nb;
-    t_begin = n_big + int(int64_t(n - n_big) * j / nsm);
-    t_end = n_big + int(int64_t(n - n_big) * (j + 1) / nsm);
-  }
+  t_begin = int(int64_t(n) * s / a.n_split_int2);
+  t_end = int(int64_t(n) * (s + 1) / a.n_split_int2);
 }
 
 // QK k-slot -> channel map of the MFMA decode kernel: k-slot i (pair q = i/2,
@@ -694,23 +681,23 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
   const int64_t head = int64_t(b) * a.n_kv_heads + h;
   float* part = a.partials + part_slot * G * kPartialStride;
   // Merged partial -> LDS (wo[0] is free once every thread has read its
-  // inputs), then one wave stores it, makes it visible device-wide (one
-  // agent-scope release per work-group) and takes the arrival ticket.
+  // inputs), then one wave stores it and takes the arrival ticket with an
+  // agent-scope release (one per work-group).
   float* stage = &wo[0][0][0];
   merge_wave_states<GP>(G, wm, wl, wo, stage);
   __shared__ int is_last;
-  if (tid < 64) {
+  if (tid < 64)
     for (int i = tid; i < G * kPartialStride; i += 64) store_agent(part + i, stage[i]);
-    wait_global_stores();   // the partial is complete before the ticket is taken
-    if (tid == 0) {
-      const int prev = fetch_add_agent(&a.tickets[head], 1);
-      is_last = (prev == n_parts - 1);
-    }
+  // (the barrier orders the other lanes' stores before thread 0's release)
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = fetch_add_acq_rel_agent(&a.tickets[head], 1);
+    is_last = (prev == n_parts - 1);
   }
   __syncthreads();
   if (!is_last) return;
-  // Every other partial of (b, h) is complete; they are read with
-  // device-coherent loads below.
+  // The last arriver's ticket acquired every other partial of (b, h); they
+  // are read with agent-scope loads below.
 
   // Split weights f_i = 2^(m_i - M) / sum_k 2^(m_k - M) l_k, staged in LDS
   // in slices of kCombineSlice partials so that all loads of a slice are in

@@ -28,8 +28,7 @@
 // max is updated lazily: a tile is rescaled only when a logit exceeds the
 // running max by more than 8 (base-2 units), so p <= 256.
 #include <algorithm>
-#include <cstdio>
-#include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "kvq2_decode_common.h"
@@ -214,8 +213,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   const int G = a.group;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // The lane id passes through an empty asm statement so that the per-lane
-  // constants derived from it are recomputed per item rather than hoisted out
-  // of the persistent item loop (which would keep them live throughout).
+  // constants derived from it are recomputed per piece rather than hoisted
+  // out of the work-group's piece loop (which would keep them live
+  // throughout).
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
   const int gq = lane >> 4, n = lane & 15;
@@ -831,25 +831,49 @@ int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
 // (two MFMA row blocks of hi/lo would not fit 16 rows) use the VALU kernel.
 namespace {
 
-// Work-groups of `kernel` the current device holds at once (cached per
-// device and kernel).
+// Per-device launch geometry, queried once per device: compute units and
+// the work-groups of each decode kernel one CU holds at once.
+struct DeviceGeometry {
+  int cus;
+  int per_cu[3];   // decode_mfma_kernel<2>, <4>, <8>
+};
+
+template <int GP>
+int kernel_per_cu() {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<GP>, 256, 0) !=
+          hipSuccess || per_cu <= 0)
+    return 1;
+  return per_cu;
+}
+
+const DeviceGeometry& device_geometry() {
+  constexpr int kMaxDevices = 64;
+  static DeviceGeometry cached[kMaxDevices];
+  static std::once_flag once[kMaxDevices];
+  static const DeviceGeometry fallback = {256, {1, 1, 1}};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fallback;
+  std::call_once(once[dev], [dev] {
+    DeviceGeometry g = fallback;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      g.cus = cus;
+    g.per_cu[0] = kernel_per_cu<2>();
+    g.per_cu[1] = kernel_per_cu<4>();
+    g.per_cu[2] = kernel_per_cu<8>();
+    cached[dev] = g;
+  });
+  return cached[dev];
+}
+
+int device_cus() { return device_geometry().cus; }
+
 template <int GP>
 int resident_work_groups() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<GP>, 256, 0) !=
-            hipSuccess ||
-        cus <= 0 || per_cu <= 0) {
-      cus = 256;
-      per_cu = 1;
-    }
-    cached[dev] = cus * per_cu;
-  }
-  return cached[dev];
+  const DeviceGeometry& g = device_geometry();
+  return g.cus * g.per_cu[GP == 2 ? 0 : GP == 4 ? 1 : 2];
 }
 
 // Work-groups of the equal-range decode: one round of resident work-groups,
@@ -861,8 +885,6 @@ int resident_work_groups() {
 // work-groups instead of 64; more than one round of small ranges was slower).
 constexpr int kMinTilesPerGroup = 128;
 constexpr int kMinTilesPerCuGroup = 32;
-
-int device_cus();
 
 template <int GP>
 int chain_grid(const DecodeArgs& a, int batch, int max_seq_len) {
@@ -878,46 +900,21 @@ int chain_grid(const DecodeArgs& a, int batch, int max_seq_len) {
       1, std::min<int64_t>(want, std::min(kChainGroups, resident_work_groups<GP>()))));
 }
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return cus;
-}
-
 }  // namespace
 
 // Grid and range weights of the MFMA decode (before the pre-pass, which
-// writes the cut).  The resident work-groups do not stream at one rate:
-//  * by dispatch round: on the 28 x 100000-token batch (four work-groups per
-//    CU) equal ranges stream at 2.88, 2.68, 2.45 and 2.31 tiles/us from the
-//    first to the fourth dispatched; on the 64-sequence G = 8 batch (three
-//    per CU) the third round ends ~29 us after the first;
-//  * by XCD: work-groups on odd XCDs (i mod 8 odd) end 10-15 us after those
-//    on even XCDs (per-work-group timestamps, stable from call to call).
-// The weights below, a little steeper than the measured rates, gave the
-// shortest sustained decode in A/B runs on one MI355X (28 x 100000: 334 ->
-// 328 us per step; 64-sequence G = 8: 403 -> 392 us).
-// KVQ_ROUND_WEIGHTS="w0,w1,w2,w3" and KVQ_XCD_WEIGHTS="even,odd" (1/1024
-// units) override them.
+// writes the cut): one round of resident work-groups, each range weighted by
+// its work-group's dispatch round and XCD (decode_tuning()).
 void set_chain_geometry(DecodeArgs& a, int batch, int max_seq_len) {
   const int G = a.group;
   a.chain_groups = G <= 2 ? chain_grid<2>(a, batch, max_seq_len)
                  : G <= 4 ? chain_grid<4>(a, batch, max_seq_len)
                           : chain_grid<8>(a, batch, max_seq_len);
   a.round_size = device_cus();
-  int w[4] = {1230, 1100, 940, 830};
-  int xw[2] = {1060, 988};
-  if (G > 4) {
-    w[0] = 1120; w[1] = 1024; w[2] = 930; w[3] = 1024;
-    xw[0] = 1036; xw[1] = 1012;
-  }
-  if (const char* s = std::getenv("KVQ_ROUND_WEIGHTS"))
-    std::sscanf(s, "%d,%d,%d,%d", &w[0], &w[1], &w[2], &w[3]);
-  if (const char* s = std::getenv("KVQ_XCD_WEIGHTS")) std::sscanf(s, "%d,%d", &xw[0], &xw[1]);
-  for (int r = 0; r < 4; ++r) a.round_weight[r] = std::min(std::max(1, w[r]), 4096);
-  for (int x = 0; x < 8; ++x) a.xcd_weight[x] = std::min(std::max(1, xw[x & 1]), 4096);
+  const DecodeTuning& t = decode_tuning();
+  const int k = G > 4 ? 1 : 0;
+  for (int r = 0; r < 4; ++r) a.round_weight[r] = t.round_weight[k][r];
+  for (int x = 0; x < 8; ++x) a.xcd_weight[x] = t.xcd_weight[k][x & 1];
 }
 
 int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* stream) {

@@ -92,13 +92,14 @@ __device__ __forceinline__ float xor32_sum(float v) {
 }
 
 // Device-coherent global accesses for data handed between work-groups of one
-// launch (split partials, tickets, work counters).  The XCDs of the GPU have
-// separate L2 caches; a generic device-scope fence makes plain stores
-// visible by writing back (and, for acquire, invalidating) the issuing XCD's
-// L2, which is expensive when many work-groups do it.  Agent-scope atomic
-// loads and stores are coherent across the XCDs by themselves, so data
-// published only through them needs just completion ordering: the writer
-// waits for its stores (vmcnt) before it takes the arrival ticket.
+// launch (the VALU decode's split partials and arrival tickets).  The XCDs of
+// the GPU have separate L2 caches; agent-scope atomic loads and stores are
+// coherent across them.  The hand-off follows the HIP memory model: the
+// writer stores its partial with agent-scope atomic stores and takes the
+// arrival ticket with an agent-scope acquire-release read-modify-write; the
+// last arriver's ticket operation is then an acquire of every earlier
+// writer's release, and it reads the partials with agent-scope loads after a
+// work-group barrier.
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -108,12 +109,10 @@ __device__ __forceinline__ void store_agent(int* p, int v) {
 __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int fetch_add_agent(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until every global store issued so far by this wave has completed.
-__device__ __forceinline__ void wait_global_stores() {
-  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+// Arrival ticket: releases this wave's earlier stores, acquires those of the
+// waves that took the ticket before.
+__device__ __forceinline__ int fetch_add_acq_rel_agent(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Byte offset of the 1152-byte chunk holding position `pos` of sequence b,

@@ -3,6 +3,7 @@
 // that every error is reported without touching the device.
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -62,6 +63,51 @@ int env_int(const char* name, int fallback) {
 
 void set_last_error(const char* msg) { g_last_error = msg ? msg : ""; }
 
+namespace {
+
+// Range weights of the MFMA decode's cut.  The resident work-groups do not
+// stream at one rate:
+//  * by dispatch round: on the 28 x 100000-token batch (four work-groups per
+//    CU) equal ranges stream at 2.88, 2.68, 2.45 and 2.31 tiles/us from the
+//    first to the fourth dispatched; on the 64-sequence G = 8 batch (three
+//    per CU) the third round ends ~29 us after the first;
+//  * by XCD: work-groups on odd XCDs (i mod 8 odd) end 10-15 us after those
+//    on even XCDs (per-work-group timestamps, stable from call to call on
+//    the MI355X they were taken on).
+// The defaults, a little steeper than the measured rates, gave the shortest
+// sustained decode in A/B runs (28 x 100000: 334 -> 328 us per step;
+// 64-sequence G = 8: 403 -> 392 us).
+DecodeTuning read_tuning() {
+  DecodeTuning t = {{kPieceCostChunks, kPieceCostChunksG8},
+                    {{1230, 1100, 940, 830}, {1120, 1024, 930, 1024}},
+                    {{1060, 988}, {1036, 1012}}};
+  const int pc = env_int("KVQ_PIECE_COST", -1);
+  if (pc >= 0) t.piece_cost[0] = t.piece_cost[1] = std::min(pc, 4096);
+  for (int k = 0; k < 2; ++k) {
+    if (const char* s = std::getenv("KVQ_ROUND_WEIGHTS"))
+      std::sscanf(s, "%d,%d,%d,%d", &t.round_weight[k][0], &t.round_weight[k][1],
+                  &t.round_weight[k][2], &t.round_weight[k][3]);
+    if (const char* s = std::getenv("KVQ_XCD_WEIGHTS"))
+      std::sscanf(s, "%d,%d", &t.xcd_weight[k][0], &t.xcd_weight[k][1]);
+    // round x XCD products within a factor of four of each other
+    int rmax = 1, xmax = 1;
+    for (int r = 0; r < 4; ++r) rmax = std::max(rmax, std::min(t.round_weight[k][r], 4096));
+    for (int x = 0; x < 2; ++x) xmax = std::max(xmax, std::min(t.xcd_weight[k][x], 4096));
+    for (int r = 0; r < 4; ++r)
+      t.round_weight[k][r] = std::min(std::max(t.round_weight[k][r], (rmax + 1) / 2), rmax);
+    for (int x = 0; x < 2; ++x)
+      t.xcd_weight[k][x] = std::min(std::max(t.xcd_weight[k][x], (xmax + 1) / 2), xmax);
+  }
+  return t;
+}
+
+}  // namespace
+
+const DecodeTuning& decode_tuning() {
+  static const DecodeTuning t = read_tuning();   // thread-safe one-time initialisation
+  return t;
+}
+
 DecodeKernel selected_decode_kernel() {
   // KVQ_DECODE_KERNEL=valu selects the plain VALU kernel (kept as the
   // measured comparison point for the MFMA kernel); default is MFMA.
@@ -77,31 +123,23 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   const int64_t last_chunk = (int2_end + kChunkTokens - 1) / kChunkTokens;   // exclusive
   const int64_t n_chunks = int2_end > d.n_sink ? last_chunk - first_chunk : 0;
   const int64_t heads = int64_t(batch) * d.n_kv_heads;
-  // Even splits: about two work items per resident work-group of the
-  // persistent decode (2048 = 256 CUs x 4 x 2), but no split shorter than
-  // 256 chunks (4096 tokens): the item prologue and the combine are paid per
-  // item.  (Big-then-small splits, n_split_small > 0, are supported; with
-  // resident work-groups of different age on one CU they finish late, since
-  // the instruction arbiter favours the oldest waves.)
-  int64_t nb = (2048 + heads - 1) / std::max<int64_t>(heads, 1), nsm = 0;
+  // VALU decode: even splits, about two work-groups per resident slot of the
+  // GPU (2048 = 256 CUs x 4 x 2), but no split shorter than 256 chunks (4096
+  // tokens): the split prologue and its share of the combine are paid per
+  // split.
+  int64_t nb = (2048 + heads - 1) / std::max<int64_t>(heads, 1);
   nb = std::min<int64_t>(nb, std::max<int64_t>(1, n_chunks / 256));
   nb = std::max<int64_t>(1, std::min<int64_t>(nb, 512));
-  const int forced = env_int("KVQ_NSPLIT", 0);          // even split override (tuning)
-  if (forced > 0) { nb = std::min(forced, 4096); nsm = 0; }
-  const int forced_small = env_int("KVQ_NSPLIT_SMALL", -1);
-  if (forced > 0 && forced_small > 0) nsm = std::min(forced_small, 4096);
-  if (n_chunks == 0) { nb = 1; nsm = 0; }
-  p.n_split_big = static_cast<int>(nb);
-  p.n_split_small = static_cast<int>(nsm);
-  p.n_split_int2 = p.n_split_big + p.n_split_small;
+  if (n_chunks == 0) nb = 1;
+  p.n_split_int2 = static_cast<int>(nb);
   // The MFMA decode deals the token-by-token list out over its INT2 items;
   // the VALU decode (also used for G > 8) gives it a work-group of its own.
   const int G_plan = d.n_q_heads / d.n_kv_heads;
   const bool own_token_item = selected_decode_kernel() == kDecodeValu || G_plan > 8;
   p.n_split = p.n_split_int2 + (own_token_item ? 1 : 0);
   const int G = d.n_q_heads / d.n_kv_heads;
-  // arrival tickets [B * Hkv] + the persistent kernel's two work counters
-  p.ticket_bytes = ((size_t(heads + 2) * sizeof(int32_t) + 255) / 256) * 256;
+  // arrival tickets [B * Hkv] of the VALU decode's last-arrival combine
+  p.ticket_bytes = ((size_t(heads) * sizeof(int32_t) + 255) / 256) * 256;
   p.qrot_bytes = size_t(batch) * d.n_q_heads * kQStride * sizeof(float);
   p.bq_bytes = size_t(heads) * kBqWords * sizeof(uint32_t);
   // tile prefix [B + 1], range starts [kChainGroups + 1], pair ranges [B Hkv]
@@ -122,8 +160,7 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
     const int64_t max_list = int64_t(d.n_sink) + 15 + (16 * npt - 1) + d.n_recent;
     p.n_tok_slices = static_cast<int>((max_list + 63) / 64);
     p.tok_slot0 = int64_t(kChainGroups) + heads;
-    p.piece_cost =
-        std::max(0, env_int("KVQ_PIECE_COST", gp == 8 ? kPieceCostChunksG8 : kPieceCostChunks)) / npt;
+    p.piece_cost = decode_tuning().piece_cost[gp == 8 ? 1 : 0] / npt;
   }
   const size_t slots = own_token_item
                            ? size_t(heads) * p.n_split

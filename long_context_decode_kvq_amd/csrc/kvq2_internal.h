@@ -33,10 +33,8 @@ constexpr int chunks_per_tile(int gp) { return gp >= 8 ? 2 : 16 / (2 * gp); }
 
 // Resolved decode geometry shared by the workspace query and the launch.
 struct DecodePlan {
-  int n_split_int2;   // work items per (sequence, KV head) over INT2 chunk tiles
-  int n_split_big;    //   of which cover the first 3/4 of the tiles (queued first)
-  int n_split_small;  //   and the last 1/4 (queued after all big ones)
-  int n_split;        // n_split_int2 + 1 (the last one takes the bf16 segments)
+  int n_split_int2;   // VALU decode: even splits per (sequence, KV head) of its INT2 chunks
+  int n_split;        // VALU decode: n_split_int2 + 1 (the last one takes the bf16 segments)
   size_t ticket_bytes;
   size_t qrot_bytes;    // rotated queries [B][Hq][kQStride] fp32
   size_t bq_bytes;      // QK MFMA operand per (b, h): [64 lanes][16 dwords] + [64][2] fp32
@@ -62,6 +60,18 @@ constexpr int kPieceCostChunks = 80;
 constexpr int kPieceCostChunksG8 = 150;
 
 DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len);
+
+// Tuning constants of the MFMA decode, read once per process from the
+// environment (KVQ_PIECE_COST, KVQ_ROUND_WEIGHTS, KVQ_XCD_WEIGHTS) with the
+// measured defaults.  Range weights are clamped so that the largest is at
+// most four times the smallest: with at least four virtual tiles per range
+// on average (the cut's precondition) no weighted range is then empty.
+struct DecodeTuning {
+  int piece_cost[2];        // chunks charged per piece start: [G <= 4, G = 8]
+  int round_weight[2][4];   // [G <= 4, G = 8][dispatch round], 1/1024 units
+  int xcd_weight[2][2];     // [G <= 4, G = 8][even, odd XCD]
+};
+const DecodeTuning& decode_tuning();
 
 // Kernel variants of the decode path.
 enum DecodeKernel { kDecodeMfma = 0, kDecodeValu = 1 };
