@@ -159,31 +159,35 @@ def copy_probe(n_bytes=1 << 30, reps=5):
     log(f"[copy-probe] {reps} copies of {n_bytes} bytes")
 
 
-def cpu_baseline(w, W, seconds_budget=10.0, max_steps=100):
-    """The CPU oracle on a bounded sample of the workload: one (sequence, KV
-    head) pair at the full context, decode steps (append one token + decode
-    its query heads) repeated until about `seconds_budget` of timed work,
-    single-threaded.  The oracle's bulk build of the pair's cache is untimed."""
+def _oracle_pair_run(w, b, h, seconds_budget, max_steps, barrier=None):
+    """The CPU oracle on one (sequence b, KV head h) pair of workload w: build
+    the pair's cache to L - 1 tokens (untimed), then decode steps (append one
+    token + decode the G query heads) until about `seconds_budget` of timed
+    work.  Single-threaded.  Host-drawn tokens of the workload's distribution
+    (the same recipe as the device draw).  Returns (bytes, seconds, steps,
+    build seconds)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as O
+    from long_context_decode_kvq_amd import workloads as W
 
-    L = int(w.seq_lens()[0])
+    L = int(w.seq_lens()[b])
     with threadpool_limits(limits=1):
         q_c, k_c, v_c = W.calibration_tokens(w, 256)
-        cal = O.calibrate(q_c[:, :w.group], k_c[:, :1], v_c[:, :1], w.group, 1,
-                          1 / math.sqrt(HEAD_DIM), 0.999)
-        k, v = W.sequence_kv_device(w, 0, 0, L + max_steps, "cuda")
-        k = k[:, :1].cpu().numpy().view(np.uint16)
-        v = v[:, :1].cpu().numpy().view(np.uint16)
+        cal = O.calibrate(q_c[:, h * w.group:(h + 1) * w.group], k_c[:, h:h + 1], v_c[:, h:h + 1],
+                          w.group, 1, 1 / math.sqrt(HEAD_DIM), 0.999)
+        k, v = W.sequence_kv(w, b, L + max_steps)
+        k, v = k[:, h:h + 1], v[:, h:h + 1]
         od = O.Dims(w.group, 1, w.page_size, w.n_sink, w.n_recent)
         npg = math.ceil((L + max_steps) / w.page_size)
         oc = O.OracleCache(od, 1, npg, np.arange(npg, dtype=np.int32)[None])
         t0 = time.perf_counter()
         oc.append(cal.R_K, cal.R_V, cal.clip_K, cal.clip_V, 0, 0, k[:L - 1], v[:L - 1])
         build_s = time.perf_counter() - t0
-        q = W.decode_queries_device(w, 0, "cuda")[:1, :w.group].cpu().numpy().view(np.uint16)
+        q = W.decode_queries(w)[b:b + 1, h * w.group:(h + 1) * w.group]
+        if barrier is not None:
+            barrier.wait()
         timed, steps, nbytes = 0.0, 0, 0
         while steps < max_steps and timed < seconds_budget:
             t0 = time.perf_counter()
@@ -195,28 +199,122 @@ def cpu_baseline(w, W, seconds_budget=10.0, max_steps=100):
             nbytes += (INT2_BYTES * n_i + BF16_BYTES * (p + 1 - n_i) + w.group * HEAD_DIM * 6
                        + 2 * HEAD_DIM * HEAD_DIM * 4)
             steps += 1
+    return nbytes, timed, steps, build_s
+
+
+_POOL_BARRIER = None
+
+
+def _pool_init(barrier):
+    global _POOL_BARRIER
+    _POOL_BARRIER = barrier
+
+
+def _pool_task(args):
+    name, b, h, budget, max_steps = args
+    from long_context_decode_kvq_amd import workloads as W
+    return _oracle_pair_run(W.WORKLOADS[name], b, h, budget, max_steps, _POOL_BARRIER)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class OraclePool:
+    """Worker processes for the all-cores oracle leg, forked at start-up,
+    before anything in this process touches the GPU (the workers only run
+    NumPy).  One worker per host core, at most 16 (the host share of one GPU)."""
+
+    def __init__(self):
+        import multiprocessing as mp
+        self.n = max(1, min(16, os.cpu_count() or 1))
+        ctx = mp.get_context("fork")
+        self.barrier = ctx.Barrier(self.n, timeout=600)
+        self.pool = ctx.Pool(self.n, initializer=_pool_init, initargs=(self.barrier,))
+
+    def run(self, w, seconds_budget, max_steps):
+        # distinct (sequence, KV head) pairs, one per worker
+        pairs = [(b % w.batch, (b // w.batch) % w.n_kv_heads) for b in range(self.n)]
+        tasks = [(w.name, b, h, seconds_budget, max_steps) for b, h in pairs]
+        res = self.pool.map_async(_pool_task, tasks, chunksize=1).get(timeout=900)
+        return res
+
+    def close(self):
+        self.pool.terminate()
+        self.pool.join()
+
+
+def cpu_baseline(w, pool, single_s=6.0, multi_s=10.0, max_steps=400):
+    """The oracle timed on the host cores: (i) one core, (ii) every worker of
+    `pool` at once, one (sequence, KV head) pair each; bytes are the
+    algorithmic bytes of the steps each ran."""
+    nb1, t1, s1, b1 = _oracle_pair_run(w, 0, 0, single_s, max_steps)
+    res = pool.run(w, multi_s, max_steps) if pool is not None else []
+    single = nb1 / t1 / 1e9
+    if res:
+        agg = sum(r[0] for r in res) / max(r[1] for r in res) / 1e9
+        steps = sum(r[2] for r in res)
+        cores = len(res)
+    else:
+        agg, steps, cores = single, s1, 1
+    L = int(w.seq_lens()[0])
     return {
-        "value": nbytes / timed / 1e9,
+        "value": agg,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"one (sequence, KV head) of the workload at context {L}: {steps} steps of "
-                   f"append 1 token + decode {w.group} query heads, NumPy fp64 oracle, 1 thread, "
-                   f"{timed:.1f}s timed (cache build {build_s:.1f}s untimed)"),
+        "sample": (f"{cores} worker processes at once, each one (sequence, KV head) pair of the "
+                   f"workload at context ~{L}: decode steps (append 1 token + decode {w.group} "
+                   f"query heads), NumPy fp64 oracle, 1 thread per worker, ~{multi_s:.0f}s timed "
+                   f"per worker, {steps} steps in all (pair cache builds untimed)"),
+        "single_core_value": single,
+        "single_core_sample": f"one pair, {s1} steps, {t1:.1f}s timed (cache build {b1:.1f}s untimed)",
+        "host_cpu_count": os.cpu_count(),
+        "host_cpu_model": cpu_model(),
     }
+
+
+def int2_chunk_offsets(w, bt, lens):
+    """Byte offsets in the pool of every INT2 chunk the decode streams, in
+    (sequence, KV head, chunk) order: the access pattern of the read probe."""
+    import numpy as np
+    P, Hkv = w.page_size, w.n_kv_heads
+    cpp = P // 16
+    out = []
+    for b, L in enumerate(lens):
+        int2_end = max(w.n_sink, int(L) - w.n_recent)
+        c = np.arange(w.n_sink // 16, (int2_end + 15) // 16, dtype=np.int64)
+        if int2_end <= w.n_sink or c.size == 0:
+            continue
+        pages = bt[b, (c * 16) // P].astype(np.int64)
+        cip = (c * 16 % P) // 16
+        for h in range(Hkv):
+            out.append(((pages * Hkv + h) * cpp + cip) * 1152)
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # Sustained decode: the first ~100 back-to-back calls after an idle GPU
-    # run through a clock/power transient (calls 6-30 up to 30 % slower, then
-    # back to steady state), so the default warm-up is long enough to time
-    # the steady state.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
+    # After an idle spell, back-to-back calls go through a power-state
+    # transient (calls 6-35 up to 30 % slower; it recurs after every idle or
+    # low-duty spell, so it is not a first-touch cost).  A fixed spell of
+    # untimed decode calls before the warm-up puts any --warmup/--steps
+    # setting in the sustained state; it is reported on its own.
+    ap.add_argument("--prewarm-s", type=float, default=0.5,
+                    help="seconds of untimed back-to-back decode calls before the warm-up")
     ap.add_argument("--workload", default="conc_28x100k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the read-ceiling probes")
     ap.add_argument("--two-calls", action="store_true",
                     help="run each step as kvq_quantize_append + kvq_decode_attention instead "
                          "of one kvq_decode_step")
@@ -232,6 +330,11 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(one process, one MI355X). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    # the oracle's worker processes are forked before this process touches the GPU
+    pool = None
+    if not args.no_cpu_baseline and not args.copy_probe:
+        pool = OraclePool()
 
     import numpy as np
     import torch
@@ -264,6 +367,7 @@ def main():
     cu1 = torch.arange(w.batch + 1, dtype=torch.int32, device=device)
     starts = [torch.from_numpy((lens_before + k).astype(np.int32)).to(device) for k in range(n_steps)]
     seqs = [torch.from_numpy((lens_before + k + 1).astype(np.int32)).to(device) for k in range(n_steps)]
+    seq0 = torch.from_numpy(lens_before.astype(np.int32)).to(device)
     qs = [W.decode_queries_device(w, k, device) for k in range(n_steps)]
     new_kv = [W.sequence_kv_device(w, b, int(lens_before[b]), n_steps, device) for b in range(w.batch)]
     k_new = [torch.stack([new_kv[b][0][k] for b in range(w.batch)]).contiguous() for k in range(n_steps)]
@@ -279,6 +383,34 @@ def main():
         else:
             kvq2.decode_step(kd, lay, h, w.batch, starts[k], cu1, w.batch, 1, k_new[k], v_new[k],
                              seqs[k], max_len, qs[k], out, ws, stream)
+
+    # ---- untimed pre-warm: back-to-back decode calls over the cache as built
+    # (the state before the first step), at most two groups of ~10 ms queued
+    # so that the host stays just ahead of the GPU; no idle gap before the
+    # warm-up steps.
+    def pre_call(i):
+        kvq2.decode_attention(kd, lay, handles[i % copies], w.batch, seq0, max_len, qs[0], out,
+                              ws, stream)
+
+    pre_call(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pre_call(1)
+    torch.cuda.synchronize()
+    est_s = max(time.perf_counter() - t0, 1e-5)
+    group = max(1, int(0.010 / est_s))
+    n_pre, marks = 2, []
+    t_pre = time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(group):
+            pre_call(n_pre)
+            n_pre += 1
+        e = torch.cuda.Event()
+        e.record(stream)
+        marks.append(e)
+        if len(marks) > 2:
+            marks.pop(0).synchronize()
+    prewarm_wall = time.perf_counter() - t_pre
 
     for k in range(args.warmup):
         step(k)
@@ -305,8 +437,9 @@ def main():
         a1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e_begin.elapsed_time(e_end) / args.steps
-    dec_ms = [a0.elapsed_time(a1) for a0, a1 in ev]
+    dec_ms = np.array([a0.elapsed_time(a1) for a0, a1 in ev])
     dec_avg_ms = float(np.mean(dec_ms))
+    pct = {p: float(np.percentile(dec_ms, p)) * 1e3 for p in (10, 50, 90)}
 
     step_bytes = []
     for i in range(args.steps):
@@ -315,16 +448,22 @@ def main():
     value = float(np.sum(step_bytes)) / (ms_per_step * 1e-3 * args.steps) / 1e9
     dec_bytes = decode_bytes(w, lens_before + last + 1)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us; "
-        f"decode {dec_avg_ms * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); "
-        f"decode {achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+    log(f"[bench] pre-warm {n_pre} decode calls in {prewarm_wall:.2f}s; step "
+        f"{ms_per_step * 1e3:.1f} us; decode {dec_avg_ms * 1e3:.1f} us (p10 {pct[10]:.1f}, "
+        f"p50 {pct[50]:.1f}, p90 {pct[90]:.1f}); decode {achieved:.0f} GB/s = "
+        f"{100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+
+    ceiling = None
+    if not args.no_probes:
+        ceiling = read_ceilings(w, kvq2, dc, pools, lens_before + last + 1, stream, achieved)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if pool is not None:
         t0 = time.time()
-        cpu = cpu_baseline(w, W)
-        log(f"[bench] cpu baseline {cpu['value']:.4f} GB/s in {time.time() - t0:.1f}s")
+        cpu = cpu_baseline(w, pool)
+        pool.close()
+        log(f"[bench] cpu baseline {cpu['value']:.4f} GB/s on {cpu['cores']} cores "
+            f"({cpu['single_core_value']:.4f} GB/s on one) in {time.time() - t0:.1f}s")
 
     kernel = os.environ.get("KVQ_DECODE_KERNEL", "mfma")
     rec = {
@@ -355,7 +494,16 @@ def main():
                          else "kvq_decode_step",
             "us_per_step": round(ms_per_step * 1e3, 2),
             "decode_us": round(dec_avg_ms * 1e3, 2),
+            "decode_us_p10": round(pct[10], 2),
+            "decode_us_p50": round(pct[50], 2),
+            "decode_us_p90": round(pct[90], 2),
             "step_pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "prewarm": {
+            "seconds": round(prewarm_wall, 3),
+            "decode_calls": n_pre,
+            "note": "untimed back-to-back decode calls before the warm-up steps (power-state "
+                    "transient after an idle spell)",
         },
         "roofline": {
             "bound": "hbm",
@@ -366,9 +514,54 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.name),
         },
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def read_ceilings(w, kvq2, dc, pools, lens, stream, achieved, reps=5):
+    """What plain reads reach on this GPU (include/kvq2_probe.h): a 2 GiB
+    sequential pass, and the decode's own 1152-byte INT2 chunks in the order
+    it streams them (pool copies rotated as in the timed steps).  Median of
+    `reps` launches each, timed with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    dev = dc.pool.device
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    t_stream = []
+    for _ in range(reps):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        kvq2.probe_stream_read(buf, sink, 8192, stream)
+        a1.record(stream)
+        t_stream.append((a0, a1))
+    offs_np = int2_chunk_offsets(w, dc.block_table.cpu().numpy(), lens)
+    t_chunk = []
+    if offs_np.size:
+        offs = torch.from_numpy(offs_np).to(dev)
+        for i in range(reps):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            kvq2.probe_chunk_read(pools[i % len(pools)], offs, sink, 2048, stream)
+            a1.record(stream)
+            t_chunk.append((a0, a1))
+    torch.cuda.synchronize()
+    del buf
+    ms = lambda ev: float(np.median([a.elapsed_time(b) for a, b in ev]))
+    stream_gbs = (2 << 30) / (ms(t_stream) * 1e-3) / 1e9
+    rec = {"unit": "GB/s", "stream_read": round(stream_gbs, 1),
+           "stream_read_bytes": 2 << 30,
+           "decode_frac_of_stream_read": round(achieved / stream_gbs, 4)}
+    if t_chunk:
+        chunk_gbs = offs_np.size * 1152 / (ms(t_chunk) * 1e-3) / 1e9
+        rec.update({"int2_chunk_read": round(chunk_gbs, 1),
+                    "int2_chunk_bytes": int(offs_np.size * 1152),
+                    "decode_frac_of_int2_chunk_read": round(achieved / chunk_gbs, 4)})
+    log(f"[bench] read ceilings: {rec}")
+    return rec
 
 
 if __name__ == "__main__":

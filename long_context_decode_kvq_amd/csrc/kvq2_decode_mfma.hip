@@ -166,13 +166,16 @@ __device__ __forceinline__ float (*wave_o())[GP][kHeadDim] {
 // any LDS read.  The kernel waits explicitly (vmcnt) for the one tile it
 // reads; no other vector-memory instruction is issued inside the tile loop.
 // M0 holds the LDS destination; lane i writes size bytes at M0 + size * i.
+// The loads carry the non-temporal hint: every chunk is read once, and on
+// the MI355X the scattered 1152-byte chunk pattern streams at ~6.55 TB/s
+// with it against ~5.85 TB/s without (global->LDS probe, 2.1 GB of chunks).
 
 // 16 bytes per lane from sbase + voff.
 __device__ __forceinline__ void dma_x4(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
+      "global_load_lds_dwordx4 %0, %1 nt"
       :
       : "v"(voff), "s"(sbase), "s"(lds)
       : "memory", "m0");
@@ -183,7 +186,7 @@ __device__ __forceinline__ void dma_x1(const uint8_t* vaddr, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %0, off"
+      "global_load_lds_dword %0, off nt"
       :
       : "v"(vaddr), "s"(lds)
       : "memory", "m0");

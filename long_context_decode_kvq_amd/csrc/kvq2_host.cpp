@@ -65,22 +65,22 @@ void set_last_error(const char* msg) { g_last_error = msg ? msg : ""; }
 
 namespace {
 
-// Range weights of the MFMA decode's cut.  The resident work-groups do not
-// stream at one rate:
-//  * by dispatch round: on the 28 x 100000-token batch (four work-groups per
-//    CU) equal ranges stream at 2.88, 2.68, 2.45 and 2.31 tiles/us from the
-//    first to the fourth dispatched; on the 64-sequence G = 8 batch (three
-//    per CU) the third round ends ~29 us after the first;
-//  * by XCD: work-groups on odd XCDs (i mod 8 odd) end 10-15 us after those
-//    on even XCDs (per-work-group timestamps, stable from call to call on
-//    the MI355X they were taken on).
-// The defaults, a little steeper than the measured rates, gave the shortest
-// sustained decode in A/B runs (28 x 100000: 334 -> 328 us per step;
-// 64-sequence G = 8: 403 -> 392 us).
+// Range weights of the MFMA decode's cut.  The resident work-groups of one
+// CU do not stream at one rate: the instruction arbiter favours the oldest
+// waves, so on the 28 x 100000-token batch (four work-groups per CU) equal
+// ranges stream at 2.88, 2.68, 2.45 and 2.31 tiles/us from the first to the
+// fourth dispatched, and on the 64-sequence G = 8 batch (three per CU) the
+// third round ends ~29 us after the first.  The round weights, a little
+// steeper than those rates, gave the shortest sustained decode in A/B runs
+// (28 x 100000: 334 -> 328 us per step; 64-sequence G = 8: 403 -> 392 us).
+// A per-XCD weight is supported but left even: one MI355X showed odd XCDs
+// ending 10-15 us late, another ran fastest with even weights (decode call
+// 298 us even against 304-311 us with a 1060/988 or 1100/950 skew), so the
+// skew belongs to the machine, not to the kernel.
 DecodeTuning read_tuning() {
   DecodeTuning t = {{kPieceCostChunks, kPieceCostChunksG8},
                     {{1230, 1100, 940, 830}, {1120, 1024, 930, 1024}},
-                    {{1060, 988}, {1036, 1012}}};
+                    {{1024, 1024}, {1024, 1024}}};
   const int pc = env_int("KVQ_PIECE_COST", -1);
   if (pc >= 0) t.piece_cost[0] = t.piece_cost[1] = std::min(pc, 4096);
   for (int k = 0; k < 2; ++k) {

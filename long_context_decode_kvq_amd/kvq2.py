@@ -44,6 +44,7 @@ class KvqCache(C.Structure):
 
 EXPORTS = ("kvq_calibrate", "kvq_quantize_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_step", "kvq_status_string", "kvq_last_error")
+PROBE_EXPORTS = ("kvq_probe_stream_read", "kvq_probe_chunk_read")
 
 
 def lib():
@@ -73,6 +74,10 @@ def lib():
         L.kvq_status_string.restype = C.c_char_p
         L.kvq_last_error.argtypes = []
         L.kvq_last_error.restype = C.c_char_p
+        L.kvq_probe_stream_read.argtypes = [P, SZ, P, I32, P]
+        L.kvq_probe_stream_read.restype = C.c_int
+        L.kvq_probe_chunk_read.argtypes = [P, P, I64, P, I32, P]
+        L.kvq_probe_chunk_read.restype = C.c_int
         _lib = L
     return _lib
 
@@ -169,6 +174,23 @@ def decode_step(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, start_pos,
                                _ptr(seq_len), max_seq_len, _ptr(q), _ptr(out), _ptr(workspace),
                                nbytes, _stream_handle(stream))
     _check(rc, "kvq_decode_step")
+
+
+# ------------------------------------------------------------------ read-bandwidth probes
+
+def probe_stream_read(src, sink, work_groups: int, stream=None):
+    """kvq_probe_stream_read: one sequential pass over `src` (a device tensor)."""
+    nbytes = src.numel() * src.element_size()
+    rc = lib().kvq_probe_stream_read(_ptr(src), nbytes, _ptr(sink), work_groups,
+                                     _stream_handle(stream))
+    _check(rc, "kvq_probe_stream_read")
+
+
+def probe_chunk_read(pool, chunk_off, sink, work_groups: int, stream=None):
+    """kvq_probe_chunk_read: the 1152-byte chunks at byte offsets `chunk_off` (int64 tensor)."""
+    rc = lib().kvq_probe_chunk_read(_ptr(pool), _ptr(chunk_off), chunk_off.numel(), _ptr(sink),
+                                    work_groups, _stream_handle(stream))
+    _check(rc, "kvq_probe_chunk_read")
 
 
 # ------------------------------------------------------------------ device cache holder

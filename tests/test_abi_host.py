@@ -28,6 +28,11 @@ def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "kvq2.h")).read()
     names = set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(kvq_\w+)\s*\(", header, re.M))
     assert names == set(kvq2.EXPORTS)
+    probe = open(os.path.join(ROOT, "include", "kvq2_probe.h")).read()
+    pnames = set(re.findall(r"^\s*int\s+(kvq_\w+)\s*\(", probe, re.M))
+    assert pnames == set(kvq2.PROBE_EXPORTS)
+    for n in kvq2.PROBE_EXPORTS:
+        assert hasattr(L, n)
     for n in names:
         assert hasattr(L, n), n
     assert L.kvq_status_string(0) == b"KVQ_OK"

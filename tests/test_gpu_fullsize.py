@@ -60,8 +60,11 @@ def gpu_cache(w, cal, lens, until=None):
     return kd, dc, lay, keep
 
 
-def oracle_pair(w, cal, b, h, L, q_bits):
-    """Oracle decode of the G query heads of (b, h) from its own cache."""
+def oracle_pair(w, cal, b, h, L, q_bits, dc=None):
+    """Oracle decode of the G query heads of (b, h) from its own cache.  With
+    the GPU cache `dc`, also check that (b, h)'s INT2 pages, ring and sink on
+    the GPU hold exactly the oracle's bytes (the bulk append's 256-token
+    work-groups wrote them)."""
     G = w.group
     od = O.Dims(G, 1, w.page_size, w.n_sink, w.n_recent)
     npg = math.ceil(L / w.page_size)
@@ -71,6 +74,17 @@ def oracle_pair(w, cal, b, h, L, q_bits):
     v = v[:, h:h + 1].cpu().numpy().view(np.uint16)
     R_K, R_V = cal.R_K[h:h + 1], cal.R_V[h:h + 1]
     oc.append(R_K, R_V, cal.clip_K, cal.clip_V, 0, 0, k, v)
+    if dc is not None:
+        bt = dc.block_table[b, :npg].long()
+        gpu_pages = dc.pool[bt, h].cpu().numpy()                  # [npg][P/16][1152]
+        bad = [lp for lp in range(npg) if not np.array_equal(gpu_pages[lp], oc.pool[lp, 0])]
+        assert not bad, f"pair ({b}, {h}): {len(bad)} INT2 pages differ, first logical page {bad[0]}"
+        ring = dc.recent[b, h].cpu().numpy().view(np.uint16)
+        assert np.array_equal(ring, oc.recent[0, 0]), f"pair ({b}, {h}): ring differs"
+        if w.n_sink:
+            sink = dc.sink[b, h].cpu().numpy().view(np.uint16)
+            assert np.array_equal(sink, oc.sink[0, 0]), f"pair ({b}, {h}): sink differs"
+        say(f"  pair (b={b}, h={h}): {npg} pages, ring and sink bytes identical to the oracle")
     return oc.decode(R_K, R_V, [L], q_bits[None, h * G:(h + 1) * G])[0]
 
 
@@ -104,7 +118,7 @@ def test_fullsize_sampled_pairs(name, pairs):
     q_bits = q.cpu().numpy().view(np.uint16)
     G = w.group
     for b, h in pairs:
-        ref = oracle_pair(w, cal, b, h, int(lens[b]), q_bits[b])
+        ref = oracle_pair(w, cal, b, h, int(lens[b]), q_bits[b], dc)
         e = rel_err(got[b, h * G:(h + 1) * G], ref)
         say(f"  pair (b={b}, h={h}) len={int(lens[b])}: rel_err={e:.3e}")
         assert e <= TOL, (name, b, h, e)
@@ -145,7 +159,7 @@ def test_fullsize_decode_step_sampled_pairs(name, pairs):
     q_bits = q.cpu().numpy().view(np.uint16)
     G = w.group
     for b, h in pairs:
-        ref = oracle_pair(w, cal, b, h, int(lens[b]), q_bits[b])
+        ref = oracle_pair(w, cal, b, h, int(lens[b]), q_bits[b], dc)
         e = rel_err(got[b, h * G:(h + 1) * G], ref)
         say(f"  pair (b={b}, h={h}) len={int(lens[b])}: rel_err={e:.3e}")
         assert e <= TOL, (name, b, h, e)
