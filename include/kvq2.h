@@ -179,6 +179,26 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer,
                          void* stream);
 
 /*
+ * kvq_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
+ * validation and results as kvq_decode_attention; the call itself allocates
+ * nothing.  Its workspace is a library-owned device scratch of 64 MiB per GPU
+ * (a static device array, present on every GPU the library is loaded on until
+ * the process ends); the decode's workspace (kvq_decode_workspace_bytes) must
+ * fit in it, else KVQ_ERR_WORKSPACE (kvq_last_error says why) before any
+ * launch.  The first call on a device resolves that device's scratch address.
+ * All calls on one GPU share its scratch and each leaves its contents behind:
+ * calls that may overlap in time on one GPU (different streams, or host
+ * threads without ordering) race and must not be issued; calls in one
+ * stream's order are safe.
+ */
+int kvq_decode_attention_noalloc(const kvq_dims* dims, const kvq_layer* layer,
+                                 const kvq_cache* cache, int32_t batch,
+                                 const int32_t* seq_len, int32_t max_seq_len,
+                                 const uint16_t* q, float* out, void* stream);
+
+/*
  * One decode step: kvq_quantize_append of the new tokens, then
  * kvq_decode_attention over the cache that includes them (OSCAR summary sec.
  * 2.2-B: quantize on eviction from the recent window, fused INT2 attention).
@@ -203,7 +223,9 @@ int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer,
 /* Human-readable name of a kvq_status value (static storage). */
 const char* kvq_status_string(int status);
 
-/* Last HIP error text recorded by this thread after KVQ_ERR_HIP ("" if none). */
+/* Last error text recorded by this thread: the HIP error after KVQ_ERR_HIP,
+ * or the reason of a KVQ_ERR_WORKSPACE of kvq_decode_attention_noalloc
+ * ("" if none). */
 const char* kvq_last_error(void);
 
 #ifdef __cplusplus

@@ -5,6 +5,7 @@
 // kvq_decode_step) and then the selected decode kernel.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "kvq2_append_common.h"
 #include "kvq2_decode_common.h"
@@ -294,7 +295,45 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(AppendArgs aa, Decod
                      *reinterpret_cast<PlanLds*>(arena + sizeof(PrologueLds<GP>)));
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += size_t(gridDim.x) * 256)
+    p[i] = 0u;
+}
+
+// The decode workspace of kvq_decode_attention_noalloc: one copy per GPU,
+// held from the first load of the library on that GPU until the process
+// ends.  Host code never uses this name as an address: its device address
+// comes from hipGetSymbolAddress, once per device (static_scratch).
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 }  // namespace
+
+int static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices];
+  static int status[kMaxDevices];
+  static std::once_flag once[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::call_once(once[dev], [dev] {
+    // runs with device `dev` current (the caller's current device)
+    status[dev] = static_cast<int>(hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)));
+  });
+  if (status[dev] != 0) return status[dev];
+  *ptr = addr[dev];
+  return 0;
+}
+
+int launch_zero_words(void* p, size_t bytes, void* stream) {
+  const size_t n = bytes / 4;
+  if (n == 0) return 0;
+  const unsigned grid = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(p), n);
+  return static_cast<int>(hipGetLastError());
+}
 
 int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
 void set_chain_geometry(DecodeArgs& a, int batch, int max_seq_len);

@@ -195,10 +195,11 @@ int check_append(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* 
   return KVQ_OK;
 }
 
-// Argument checks of a decode (before any HIP call); fills the plan.
-int check_decode(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
-                 int32_t batch, const int32_t* seq_len, int32_t max_seq_len, const uint16_t* q,
-                 float* out, void* workspace, size_t workspace_bytes, DecodePlan* plan) {
+// Argument checks of a decode other than its workspace (before any HIP
+// call); fills the plan.
+int check_decode_args(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
+                      int32_t batch, const int32_t* seq_len, int32_t max_seq_len,
+                      const uint16_t* q, float* out, DecodePlan* plan) {
   int rc = check_dims(dims);
   if (rc != KVQ_OK) return rc;
   if ((rc = check_layer(layer)) != KVQ_OK) return rc;
@@ -211,6 +212,15 @@ int check_decode(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* 
       (int64_t(1) << 31))
     return KVQ_ERR_UNSUPPORTED;
   *plan = make_decode_plan(*dims, batch, max_seq_len);
+  return KVQ_OK;
+}
+
+// Argument checks of a decode with a caller workspace.
+int check_decode(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
+                 int32_t batch, const int32_t* seq_len, int32_t max_seq_len, const uint16_t* q,
+                 float* out, void* workspace, size_t workspace_bytes, DecodePlan* plan) {
+  const int rc = check_decode_args(dims, layer, cache, batch, seq_len, max_seq_len, q, out, plan);
+  if (rc != KVQ_OK) return rc;
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan->total_bytes)
     return KVQ_ERR_WORKSPACE;
   return KVQ_OK;
@@ -268,6 +278,31 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq
   return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
                                   max_seq_len, q, out, workspace, plan, selected_decode_kernel(),
                                   stream));
+}
+
+int kvq_decode_attention_noalloc(const kvq_dims* dims, const kvq_layer* layer,
+                                 const kvq_cache* cache, int32_t batch, const int32_t* seq_len,
+                                 int32_t max_seq_len, const uint16_t* q, float* out,
+                                 void* stream) {
+  // Every argument check of kvq_decode_attention; the workspace this call
+  // needs must fit the library's scratch.
+  DecodePlan plan;
+  int rc = check_decode_args(dims, layer, cache, batch, seq_len, max_seq_len, q, out, &plan);
+  if (rc != KVQ_OK) return rc;
+  if (plan.total_bytes > kStaticScratchBytes) {
+    set_last_error("decode workspace larger than the library scratch of "
+                   "kvq_decode_attention_noalloc (64 MiB); use kvq_decode_attention");
+    return KVQ_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if ((rc = hip_status(static_scratch(&ws))) != KVQ_OK) return rc;
+  // The arrival counters of the VALU decode must start at zero; the scratch
+  // keeps whatever the previous call on this GPU left.
+  const DecodeKernel which = selected_decode_kernel();
+  if (which == kDecodeValu || dims->n_q_heads / dims->n_kv_heads > 8)
+    if ((rc = hip_status(launch_zero_words(ws, plan.ticket_bytes, stream))) != KVQ_OK) return rc;
+  return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
+                                  max_seq_len, q, out, ws, plan, which, stream));
 }
 
 int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,

@@ -103,6 +103,16 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                   int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
                   const DecodePlan& plan, DecodeKernel which, void* stream);
 
+// The library-owned decode scratch of kvq_decode_attention_noalloc: a
+// file-scope device array of kStaticScratchBytes per GPU.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+// Device address of the current device's scratch (resolved once per device
+// with hipGetSymbolAddress); returns a hipError_t value.
+int static_scratch(void** ptr);
+// Zero `bytes` (a multiple of 4) at device address p with a fill kernel
+// (no memset node, so the call can be captured in a HIP graph).
+int launch_zero_words(void* p, size_t bytes, void* stream);
+
 const char* hip_error_name(int err);
 void set_last_error(const char* msg);
 

@@ -43,7 +43,8 @@ class KvqCache(C.Structure):
 
 
 EXPORTS = ("kvq_calibrate", "kvq_quantize_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attention", "kvq_decode_step", "kvq_status_string", "kvq_last_error")
+           "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_decode_step",
+           "kvq_status_string", "kvq_last_error")
 PROBE_EXPORTS = ("kvq_probe_stream_read", "kvq_probe_chunk_read")
 
 
@@ -66,6 +67,9 @@ def lib():
         L.kvq_decode_attention.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
                                            C.POINTER(KvqCache), I32, P, I32, P, P, P, SZ, P]
         L.kvq_decode_attention.restype = C.c_int
+        L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
+                                                   C.POINTER(KvqCache), I32, P, I32, P, P, P]
+        L.kvq_decode_attention_noalloc.restype = C.c_int
         L.kvq_decode_step.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
                                       C.POINTER(KvqCache), I32, P, P, I32, I32, P, P, P, I32,
                                       P, P, P, SZ, P]
@@ -163,6 +167,15 @@ def decode_attention(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, seq_l
                                     max_seq_len, _ptr(q), _ptr(out), _ptr(workspace), nbytes,
                                     _stream_handle(stream))
     _check(rc, "kvq_decode_attention")
+
+
+def decode_attention_noalloc(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, seq_len,
+                             max_seq_len: int, q, out, stream=None):
+    """kvq_decode_attention_noalloc: the decode with the library's own scratch."""
+    rc = lib().kvq_decode_attention_noalloc(C.byref(d), C.byref(lay), C.byref(cch), batch,
+                                            _ptr(seq_len), max_seq_len, _ptr(q), _ptr(out),
+                                            _stream_handle(stream))
+    _check(rc, "kvq_decode_attention_noalloc")
 
 
 def decode_step(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, start_pos, cu_new,

@@ -228,3 +228,28 @@ def test_calibrate_rejects_bad_input():
     huge = to_bf16_bits(np.full((32, 2, 128), 30000.0, np.float32))
     with pytest.raises(kvq2.KvqError, match="NUMERIC"):          # clip > 16384
         kvq2.calibrate(d, q, huge, v, 0.999)
+
+
+def _noalloc(d, lay, cch, batch=2, seq=FAKE, max_len=100, q=FAKE, out=FAKE):
+    return _lib().kvq_decode_attention_noalloc(C.byref(d), C.byref(lay), C.byref(cch), batch, seq,
+                                               max_len, q, out, None)
+
+
+def test_noalloc_decode_validates_before_launch():
+    """The no-alloc decode checks what kvq_decode_attention checks, and
+    refuses a decode whose workspace exceeds its 64 MiB scratch, all before
+    any HIP call."""
+    d, lay, cch = _args()
+    assert _noalloc(d, lay, cch, q=FAKE + 2) == ERR_ARG
+    assert _noalloc(d, lay, cch, out=0) == ERR_ARG
+    assert _noalloc(d, lay, cch, seq=0) == ERR_ARG
+    assert _noalloc(d, lay, cch, batch=0) == ERR_ARG
+    assert _noalloc(d, lay, cch, max_len=8 * 16 + 1) == ERR_ARG
+    d, lay, cch = _args(P=8)
+    assert _noalloc(d, lay, cch) == ERR_UNSUP
+    # 2000 sequences of 64 query heads: the rotated queries alone take 67 MB
+    d, lay, cch = _args(Hq=64, Hkv=8)
+    need = _lib().kvq_decode_workspace_bytes(C.byref(d), 2000, 100)
+    assert need > 64 << 20
+    assert _noalloc(d, lay, cch, batch=2000) == ERR_WS
+    assert b"64 MiB" in _lib().kvq_last_error()
