@@ -508,6 +508,36 @@ class OracleCache:
         return out
 
 
+def decode_multi(cache: "OracleCache", R_K, R_V, seq_len, n_query: int,
+                 q_bits: np.ndarray) -> np.ndarray:
+    """Multi-query attention over the cache: out fp32 [B][M][Hq][128].
+
+    The M = n_query queries of sequence b sit at its last M positions
+    L - M .. L - 1 (their keys and values already appended, so the cache
+    length L includes them; L >= M); query m attends causally to the stored
+    keys and values of positions 0 .. L - M + m, dequantized as in decode.
+    Speculative verification and chunked prefill over the INT2 cache
+    [OSCAR-S 2.2-B: the same mixed-precision cache serves every query].
+    q' = R_K^T q, softmax over the visible positions, o = R_V o' (fp64).
+    """
+    d = cache.d
+    G = d.group
+    B = cache.batch
+    out = np.full((B, n_query, d.n_q_heads, HEAD_DIM), np.nan, np.float32)
+    for b in range(B):
+        L = int(seq_len[b])
+        for h in range(d.n_kv_heads):
+            K, V = cache.gather(b, h, L)
+            for m in range(n_query):
+                visible = L - n_query + m + 1
+                for g in range(h * G, (h + 1) * G):
+                    q = bf16_bits_to_f32(q_bits[b, m, g]).astype(np.float64)
+                    qr = np.asarray(R_K[h], np.float64).T @ q
+                    o_rot = attention(qr, K[:visible], V[:visible], d.sm_scale)
+                    out[b, m, g] = (np.asarray(R_V[h], np.float64) @ o_rot).astype(np.float32)
+    return out
+
+
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> np.ndarray:
     """Plain softmax attention of one query over [n][d] keys/values in fp64."""
     if K.shape[0] == 0:

@@ -481,3 +481,80 @@ def test_segment_counts_and_bits_per_element():
     assert O.int2_bits_per_element() == 2.25
     # bytes per (token, KV head): 2 * (32 + 4) INT2 vs 2 * 256 bf16 -> 7.1x less
     assert 2 * 256 / (2 * (32 + 4)) == pytest.approx(7.111, rel=1e-3)
+
+
+# ---------------------------------------------------------------- multi-query attention
+
+def test_decode_multi_one_query_is_decode():
+    d, oc, (R_K, R_V) = _multi_setup()
+    q = bf16(rng.standard_normal((2, 1, 4, 128)).astype(np.float32))
+    a = O.decode_multi(oc, R_K, R_V, [70, 45], 1, q)
+    b = oc.decode(R_K, R_V, [70, 45], q[:, 0])
+    assert np.array_equal(a[:, 0], b)
+
+
+def _multi_setup(lens=(70, 45), W=8, ns=4):
+    d = O.Dims(4, 2, 16, ns, W)
+    npg = [math.ceil(L / 16) for L in lens]
+    bt = np.zeros((len(lens), max(npg)), np.int32)
+    perm = rng.permutation(sum(npg))
+    i = 0
+    for b, n in enumerate(npg):
+        bt[b, :n] = perm[i:i + n]
+        i += n
+    oc = O.OracleCache(d, len(lens), sum(npg), bt)
+    R_K, R_V = _rand_R(2), _rand_R(2)
+    for b, L in enumerate(lens):
+        k = bf16(rng.standard_normal((L, 2, 128)).astype(np.float32) * 2)
+        v = bf16(rng.standard_normal((L, 2, 128)).astype(np.float32))
+        oc.append(R_K, R_V, 6.0, 6.0, b, 0, k, v)
+    return d, oc, (R_K, R_V)
+
+
+def test_decode_multi_bf16_cache_is_causal_sdpa():
+    """With R = I and every position in bf16 (L <= n_sink + W), multi-query
+    attention is scaled-dot-product attention with a bottom-right causal mask
+    (torch, float64): query m of M sees the first L - M + m + 1 keys."""
+    import torch
+    Hq, Hkv, L, M, W, ns = 6, 2, 37, 5, 40, 4
+    G = Hq // Hkv
+    d = O.Dims(Hq, Hkv, 16, ns, W)
+    npg = math.ceil(L / 16)
+    oc = O.OracleCache(d, 1, npg, np.arange(npg, dtype=np.int32)[None])
+    I = np.stack([np.eye(128, dtype=np.float32)] * Hkv)
+    k = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32))
+    v = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32))
+    oc.append(I, I, 8.0, 8.0, 0, 0, k, v)
+    q = bf16(rng.standard_normal((1, M, Hq, 128)).astype(np.float32))
+    got = O.decode_multi(oc, I, I, [L], M, q)[0]                         # [M][Hq][128]
+    to64 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double()
+    qt, kt, vt = to64(q[0]), to64(k), to64(v)                            # [M][Hq][d], [L][Hkv][d]
+    mask = torch.zeros(M, L, dtype=torch.bool)
+    for m in range(M):
+        mask[m, :L - M + m + 1] = True
+    for g in range(Hq):
+        h = g // G
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[:, g][None, None], kt[:, h][None, None], vt[:, h][None, None], attn_mask=mask,
+            scale=d.sm_scale)[0, 0]
+        assert np.allclose(got[:, g], ref.numpy().astype(np.float32), rtol=0, atol=1e-6)
+
+
+def test_decode_multi_rows_differ_only_by_visible_prefix():
+    """Across the M queries the visible prefix grows by one position: giving
+    every query the same vector, row m equals a one-query decode of a cache
+    truncated to L - M + m + 1 positions when all of them are still bf16."""
+    Hq, Hkv, L, M = 4, 2, 20, 4
+    d = O.Dims(Hq, Hkv, 16, 4, 32)
+    npg = math.ceil(L / 16)
+    oc = O.OracleCache(d, 1, npg, np.arange(npg, dtype=np.int32)[None])
+    R_K, R_V = _rand_R(Hkv), _rand_R(Hkv)
+    k = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32))
+    v = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32))
+    oc.append(R_K, R_V, 8.0, 8.0, 0, 0, k, v)
+    q1 = bf16(rng.standard_normal((1, Hq, 128)).astype(np.float32))
+    q = np.repeat(q1[:, None], M, axis=1)
+    got = O.decode_multi(oc, R_K, R_V, [L], M, q)[0]
+    for m in range(M):
+        ref = oc.decode(R_K, R_V, [L - M + m + 1], q1)[0]
+        assert np.allclose(got[m], ref, rtol=0, atol=1e-6), m
