@@ -515,7 +515,9 @@ def decode_multi(cache: "OracleCache", R_K, R_V, seq_len, n_query: int,
     The M = n_query queries of sequence b sit at its last M positions
     L - M .. L - 1 (their keys and values already appended, so the cache
     length L includes them; L >= M); query m attends causally to the stored
-    keys and values of positions 0 .. L - M + m, dequantized as in decode.
+    keys and values of positions 0 .. L - M + m, dequantized as in decode; a
+    query with no such position (L - M + m < 0, a sequence shorter than M)
+    attends to nothing and gives 0, like the decode of an empty sequence.
     Speculative verification and chunked prefill over the INT2 cache
     [OSCAR-S 2.2-B: the same mixed-precision cache serves every query].
     q' = R_K^T q, softmax over the visible positions, o = R_V o' (fp64).
@@ -529,7 +531,7 @@ def decode_multi(cache: "OracleCache", R_K, R_V, seq_len, n_query: int,
         for h in range(d.n_kv_heads):
             K, V = cache.gather(b, h, L)
             for m in range(n_query):
-                visible = L - n_query + m + 1
+                visible = max(0, L - n_query + m + 1)
                 for g in range(h * G, (h + 1) * G):
                     q = bf16_bits_to_f32(q_bits[b, m, g]).astype(np.float64)
                     qr = np.asarray(R_K[h], np.float64).T @ q

@@ -558,3 +558,21 @@ def test_decode_multi_rows_differ_only_by_visible_prefix():
     for m in range(M):
         ref = oc.decode(R_K, R_V, [L - M + m + 1], q1)[0]
         assert np.allclose(got[m], ref, rtol=0, atol=1e-6), m
+
+
+def test_decode_multi_sequence_shorter_than_the_queries():
+    """L < M: query m sees positions 0 .. L - M + m, none when that is
+    negative (output 0); the others equal the truncated one-query decodes."""
+    Hq, Hkv, L, M = 4, 2, 2, 4
+    d = O.Dims(Hq, Hkv, 16, 4, 8)
+    oc = O.OracleCache(d, 1, 1, np.zeros((1, 1), np.int32))
+    R_K, R_V = _rand_R(Hkv), _rand_R(Hkv)
+    k = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32))
+    v = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32))
+    oc.append(R_K, R_V, 8.0, 8.0, 0, 0, k, v)
+    q1 = bf16(rng.standard_normal((1, Hq, 128)).astype(np.float32))
+    got = O.decode_multi(oc, R_K, R_V, [L], M, np.repeat(q1[:, None], M, axis=1))[0]
+    assert np.array_equal(got[0], np.zeros((Hq, 128), np.float32))
+    assert np.array_equal(got[1], np.zeros((Hq, 128), np.float32))
+    assert np.allclose(got[2], oc.decode(R_K, R_V, [1], q1)[0], rtol=0, atol=1e-6)
+    assert np.allclose(got[3], oc.decode(R_K, R_V, [2], q1)[0], rtol=0, atol=1e-6)
