@@ -47,26 +47,30 @@ def segment_counts(L, ns, W):
     return n_s, n_i, L - n_s - n_i
 
 
-def decode_bytes(w, lens):
-    """Algorithmic HBM bytes of one decode launch (what the method must move)."""
+def decode_bytes(w, lens, n_query=1):
+    """Algorithmic HBM bytes of one decode launch (what the method must move);
+    with n_query queries per sequence the cache is read once for all of them."""
     tot = 0
     for L in lens:
         _, n_i, _ = segment_counts(int(L), w.n_sink, w.n_recent)
         n_b = int(L) - n_i
         tot += w.n_kv_heads * (INT2_BYTES * n_i + BF16_BYTES * n_b)
         tot += 4 * math.ceil(int(L) / w.page_size)                  # block-table entries
-    tot += w.batch * w.n_q_heads * HEAD_DIM * (2 + 4)               # q bf16 in, out fp32
+    tot += w.batch * n_query * w.n_q_heads * HEAD_DIM * (2 + 4)     # q bf16 in, out fp32
     tot += 2 * w.n_kv_heads * HEAD_DIM * HEAD_DIM * 4               # R_K, R_V
     return tot
 
 
-def append_bytes(w, lens_before):
-    """Algorithmic HBM bytes of one single-token quantize-append launch."""
+def append_bytes(w, lens_before, n_new=1):
+    """Algorithmic HBM bytes of one quantize-append launch of n_new tokens
+    per sequence."""
     per_vec = 256 + 256                                             # new bf16 in, ring write
     tot = 0
-    for L in lens_before:
-        evict = int(L) - w.n_recent >= w.n_sink and int(L) >= w.n_sink
-        tot += w.n_kv_heads * 2 * (per_vec + ((256 + 36) if evict else 0))
+    for L0 in lens_before:
+        for j in range(n_new):
+            L = int(L0) + j
+            evict = L - w.n_recent >= w.n_sink and L >= w.n_sink
+            tot += w.n_kv_heads * 2 * (per_vec + ((256 + 36) if evict else 0))
     tot += 2 * w.n_kv_heads * HEAD_DIM * HEAD_DIM * 4               # R_K, R_V
     return tot
 
@@ -313,6 +317,9 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=0.5,
                     help="seconds of untimed back-to-back decode calls before the warm-up")
     ap.add_argument("--workload", default="conc_28x100k")
+    ap.add_argument("--n-query", type=int, default=1,
+                    help="queries per sequence and step: M > 1 times multi-query attention "
+                         "(kvq_quantize_append of M tokens + kvq_decode_multi_attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the read-ceiling probes")
     ap.add_argument("--two-calls", action="store_true",
@@ -332,8 +339,9 @@ def main():
         sys.exit(2)
 
     # the oracle's worker processes are forked before this process touches the GPU
+    # (the oracle leg times the one-query decode step; multi-query lines go without it)
     pool = None
-    if not args.no_cpu_baseline and not args.copy_probe:
+    if not args.no_cpu_baseline and not args.copy_probe and args.n_query == 1:
         pool = OraclePool()
 
     import numpy as np
@@ -349,8 +357,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     device = torch.device("cuda:0")
     n_steps = args.warmup + args.steps
-    lens_before = w.seq_lens() - 1               # the first step appends token L-1
-    kd, dc, lay, keep = build_cache(w, kvq2, W, lens_before, n_steps, device)
+    M = args.n_query
+    lens_before = w.seq_lens() - M               # the first step appends tokens L-M .. L-1
+    kd, dc, lay, keep = build_cache(w, kvq2, W, lens_before, n_steps * M, device)
 
     # Small caches would be served from the 256 MB Infinity Cache: rotate
     # independent pool copies so every step reads its pages from HBM.
@@ -360,23 +369,40 @@ def main():
     handles = [dc.handle] + [kvq2.cache(p, dc.num_pages, dc.sink if w.n_sink > 0 else None,
                                         dc.recent, dc.block_table) for p in pools[1:]]
 
-    max_len = int(lens_before.max()) + n_steps
-    ws = torch.zeros(kvq2.decode_workspace_bytes(kd, w.batch, max_len), dtype=torch.uint8,
-                     device=device)
-    out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=device)
-    cu1 = torch.arange(w.batch + 1, dtype=torch.int32, device=device)
-    starts = [torch.from_numpy((lens_before + k).astype(np.int32)).to(device) for k in range(n_steps)]
-    seqs = [torch.from_numpy((lens_before + k + 1).astype(np.int32)).to(device) for k in range(n_steps)]
+    max_len = int(lens_before.max()) + n_steps * M
+    ws = torch.zeros(kvq2.decode_multi_workspace_bytes(kd, w.batch, max_len, M),
+                     dtype=torch.uint8, device=device)
+    out = torch.empty((w.batch, M, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=device)
+    cu1 = torch.arange(w.batch + 1, dtype=torch.int32, device=device) * M
+    starts = [torch.from_numpy((lens_before + k * M).astype(np.int32)).to(device)
+              for k in range(n_steps)]
+    seqs = [torch.from_numpy((lens_before + (k + 1) * M).astype(np.int32)).to(device)
+            for k in range(n_steps)]
     seq0 = torch.from_numpy(lens_before.astype(np.int32)).to(device)
-    qs = [W.decode_queries_device(w, k, device) for k in range(n_steps)]
-    new_kv = [W.sequence_kv_device(w, b, int(lens_before[b]), n_steps, device) for b in range(w.batch)]
-    k_new = [torch.stack([new_kv[b][0][k] for b in range(w.batch)]).contiguous() for k in range(n_steps)]
-    v_new = [torch.stack([new_kv[b][1][k] for b in range(w.batch)]).contiguous() for k in range(n_steps)]
+    # queries [B][M][Hq][128] of step k (M draws of the step's query generator)
+    qs = [torch.stack([W.decode_queries_device(w, k * M + j, device) for j in range(M)], 1)
+          .contiguous() for k in range(n_steps)]
+    new_kv = [W.sequence_kv_device(w, b, int(lens_before[b]), n_steps * M, device)
+              for b in range(w.batch)]
+    k_new = [torch.cat([new_kv[b][0][k * M:(k + 1) * M] for b in range(w.batch)]).contiguous()
+             for k in range(n_steps)]
+    v_new = [torch.cat([new_kv[b][1][k * M:(k + 1) * M] for b in range(w.batch)]).contiguous()
+             for k in range(n_steps)]
     stream = torch.cuda.current_stream()
+
+    def decode_call(h, seq, q):
+        if M == 1:
+            kvq2.decode_attention(kd, lay, h, w.batch, seq, max_len, q, out, ws, stream)
+        else:
+            kvq2.decode_multi_attention(kd, lay, h, w.batch, seq, max_len, M, q, out, ws, stream)
 
     def step(k):
         h = handles[k % copies]
-        if args.two_calls:
+        if M > 1:
+            kvq2.quantize_append(kd, lay, h, w.batch, starts[k], cu1, w.batch * M, M, k_new[k],
+                                 v_new[k], stream)
+            decode_call(h, seqs[k], qs[k])
+        elif args.two_calls:
             kvq2.quantize_append(kd, lay, h, w.batch, starts[k], cu1, w.batch, 1, k_new[k],
                                  v_new[k], stream)
             kvq2.decode_attention(kd, lay, h, w.batch, seqs[k], max_len, qs[k], out, ws, stream)
@@ -389,8 +415,7 @@ def main():
     # so that the host stays just ahead of the GPU; no idle gap before the
     # warm-up steps.
     def pre_call(i):
-        kvq2.decode_attention(kd, lay, handles[i % copies], w.batch, seq0, max_len, qs[0], out,
-                              ws, stream)
+        decode_call(handles[i % copies], seq0, qs[0])
 
     pre_call(0)
     torch.cuda.synchronize()
@@ -432,8 +457,7 @@ def main():
           for _ in range(args.steps)]
     for a0, a1 in ev:
         a0.record(stream)
-        kvq2.decode_attention(kd, lay, handles[last % copies], w.batch, seqs[last], max_len,
-                              qs[last], out, ws, stream)
+        decode_call(handles[last % copies], seqs[last], qs[last])
         a1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e_begin.elapsed_time(e_end) / args.steps
@@ -443,10 +467,10 @@ def main():
 
     step_bytes = []
     for i in range(args.steps):
-        lb = lens_before + args.warmup + i
-        step_bytes.append(decode_bytes(w, lb + 1) + append_bytes(w, lb))
+        lb = lens_before + (args.warmup + i) * M
+        step_bytes.append(decode_bytes(w, lb + M, M) + append_bytes(w, lb, M))
     value = float(np.sum(step_bytes)) / (ms_per_step * 1e-3 * args.steps) / 1e9
-    dec_bytes = decode_bytes(w, lens_before + last + 1)
+    dec_bytes = decode_bytes(w, lens_before + (last + 1) * M, M)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     log(f"[bench] pre-warm {n_pre} decode calls in {prewarm_wall:.2f}s; step "
         f"{ms_per_step * 1e3:.1f} us; decode {dec_avg_ms * 1e3:.1f} us (p10 {pct[10]:.1f}, "
@@ -455,7 +479,7 @@ def main():
 
     ceiling = None
     if not args.no_probes:
-        ceiling = read_ceilings(w, kvq2, dc, pools, lens_before + last + 1, stream, achieved)
+        ceiling = read_ceilings(w, kvq2, dc, pools, lens_before + (last + 1) * M, stream, achieved)
 
     cpu = None
     if pool is not None:
@@ -485,13 +509,16 @@ def main():
         "config": {
             "workload": w.name,
             "batch": w.batch,
-            "context": int(lens_before.max()) + 1,
-            "context_note": "step k decodes at context + k (one appended token per step)",
+            "context": int(lens_before.max()) + M,
+            "context_note": (f"step k appends {M} token(s) per sequence and decodes at context "
+                             f"+ {M} k"),
+            "n_query": M,
             "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": HEAD_DIM,
             "page_size": w.page_size, "n_sink": w.n_sink, "n_recent": w.n_recent,
             "layers": 1, "decode_kernel": kernel, "pool_copies": copies,
-            "step_call": "kvq_quantize_append + kvq_decode_attention" if args.two_calls
-                         else "kvq_decode_step",
+            "step_call": ("kvq_quantize_append + kvq_decode_multi_attention" if M > 1 else
+                          "kvq_quantize_append + kvq_decode_attention" if args.two_calls
+                          else "kvq_decode_step"),
             "us_per_step": round(ms_per_step * 1e3, 2),
             "decode_us": round(dec_avg_ms * 1e3, 2),
             "decode_us_p10": round(pct[10], 2),

@@ -179,6 +179,36 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer,
                          void* stream);
 
 /*
+ * Multi-query attention over the same cache (speculative verification,
+ * chunked prefill; OSCAR summary sec. 2.2-B: one fused kernel serves the
+ * mixed-precision cache).  Each sequence b has n_query = M queries at its
+ * last M positions L - M .. L - 1, whose keys and values were appended
+ * before this call (seq_len holds L, including them); query m attends
+ * causally to positions 0 .. L - M + m.  Same rotation, segments, softmax
+ * and output mapping as kvq_decode_attention, which is the case M = 1.
+ *   n_query      1 <= M <= n_recent, else KVQ_ERR_ARG (every query then
+ *                sees the whole INT2 history, so the causal mask touches
+ *                the bf16 window only)
+ *   q            device bf16 [batch][M][Hq][128]
+ *   out          device fp32 [batch][M][Hq][128]; a query with no visible
+ *                position (L < M) gives 0
+ *   workspace    kvq_decode_multi_workspace_bytes(dims, batch, max_seq_len, M)
+ *                bytes, zero-filled once, reusable as for kvq_decode_attention
+ * The queries of a (sequence, KV head) share the passes over its pages: the
+ * matrix-core decode takes up to 8 rows (queries x Hq / Hkv) per pass, the
+ * VALU decode up to 16, so M queries cost ceil(M Hq / Hkv / 8) passes
+ * instead of M decodes.
+ */
+size_t kvq_decode_multi_workspace_bytes(const kvq_dims* dims, int32_t batch,
+                                        int32_t max_seq_len, int32_t n_query);
+int kvq_decode_multi_attention(const kvq_dims* dims, const kvq_layer* layer,
+                               const kvq_cache* cache, int32_t batch,
+                               const int32_t* seq_len, int32_t max_seq_len,
+                               int32_t n_query, const uint16_t* q, float* out,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * kvq_decode_attention without a caller workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments (minus the workspace),

@@ -170,7 +170,7 @@ __device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int 
   for (int k = 0; k < KG * kHeadDim / 256; ++k) {
     const int i = tid + 256 * k, g = i / kHeadDim, c = i % kHeadDim;
     qs[g][c] = g < G ? bf16_bits_to_float(
-                           a.q[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c])
+                           a.q[row_offset(a, b, h, g) + c])
                      : 0.f;
   }
   __syncthreads();
@@ -206,7 +206,7 @@ __device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int 
     for (int g = 0; g < KG; ++g) part[half][g][c] = acc[g];
   }
   __syncthreads();
-  float* dst = a.qrot + (int64_t(b) * a.n_q_heads + int64_t(h) * G) * kQStride;
+  float* dst = a.qrot + qrot_offset(a, b, h);
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int g = i / kHeadDim, c = i % kHeadDim;
     const float v = (part[0][g][c] + part[1][g][c]) * a.alpha;
@@ -344,7 +344,8 @@ namespace {
 DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                             const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
                             const uint16_t* q, float* out, void* workspace,
-                            const DecodePlan& plan, DecodeKernel which) {
+                            const DecodePlan& plan, DecodeKernel which, int32_t n_query,
+                            int32_t query_base, int32_t query_count) {
   DecodeArgs a{};
   a.R_K = layer.R_K;
   a.R_V = layer.R_V;
@@ -356,7 +357,11 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
   a.bt_stride = cache.bt_stride;
   a.n_q_heads = d.n_q_heads;
   a.n_kv_heads = d.n_kv_heads;
-  a.group = d.n_q_heads / d.n_kv_heads;
+  a.head_group = d.n_q_heads / d.n_kv_heads;
+  a.n_query = n_query;
+  a.query_base = query_base;
+  a.query_count = query_count;
+  a.group = a.head_group * n_query;
   a.page_size = d.page_size;
   a.n_sink = d.n_sink;
   a.n_recent = d.n_recent;
@@ -402,9 +407,10 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
 int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                   const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
                   int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
-                  const DecodePlan& plan, DecodeKernel which, void* stream) {
+                  const DecodePlan& plan, DecodeKernel which, void* stream, int32_t n_query,
+                  int32_t query_base, int32_t query_count) {
   DecodeArgs a = make_decode_args(d, sm_scale, layer, cache, batch, seq_len, q, out, workspace,
-                                  plan, which);
+                                  plan, which, n_query, query_base, query_count);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
   const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch);
@@ -426,7 +432,7 @@ int launch_decode_step(const kvq_dims& d, float sm_scale, const kvq_layer& layer
                        const uint16_t* q, float* out, void* workspace, const DecodePlan& plan,
                        void* stream) {
   DecodeArgs a = make_decode_args(d, sm_scale, layer, cache, batch, seq_len, q, out, workspace,
-                                  plan, kDecodeMfma);
+                                  plan, kDecodeMfma, 1, 0, 1);
   const AppendArgs aa = make_append_args(d, layer, cache, batch, start_pos, cu_new, total_new,
                                          k_new, v_new);
   if (a.gp == 0 || aa.tokens_per_block != kWaves) return -1;   // not a fused-step shape

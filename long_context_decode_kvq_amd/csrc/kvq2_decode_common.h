@@ -25,7 +25,16 @@ struct DecodeArgs {
   const uint16_t* recent;
   const int32_t* block_table;
   int32_t bt_stride;
-  int n_q_heads, n_kv_heads, group, page_size, n_sink, n_recent;
+  int n_q_heads, n_kv_heads, page_size, n_sink, n_recent;
+  // Rows of one (sequence, KV head): the head_group = Hq / Hkv query heads
+  // of each of the n_query queries this launch takes, queries query_base ..
+  // query_base + n_query - 1 of the query_count queries of every sequence
+  // (1 for decode; M for multi-query attention, whose queries sit at the
+  // sequence's last M positions).  Row r is query query_base + r /
+  // head_group, head h head_group + r % head_group; group = n_query *
+  // head_group rows share the KV head's tiles (the MFMA decode's "heads" are
+  // these rows).
+  int group, head_group, n_query, query_base, query_count;
   float alpha;                 // sm_scale * log2(e): logits are kept in base-2 units
   float sigma_v;               // power of two with sigma_v * s_V <= 1 for every V scale
   int log2_sigma_v;            // log2(sigma_v)
@@ -84,6 +93,18 @@ struct Int2Range {
   int cf, cl;     // tiled chunks [cf, cl), cl - cf a multiple of npt
 };
 
+// Element offset of row r of (b, h) in q and out, both [B][query_count][Hq][128].
+__device__ __forceinline__ int64_t row_offset(const DecodeArgs& a, int b, int h, int r) {
+  const int m = r / a.head_group, g = r - m * a.head_group;
+  return ((int64_t(b) * a.query_count + a.query_base + m) * a.n_q_heads +
+          int64_t(h) * a.head_group + g) * kHeadDim;
+}
+
+// First rotated-query record of (b, h) in qrot ([B][Hkv][rows][kQStride]).
+__device__ __forceinline__ int64_t qrot_offset(const DecodeArgs& a, int b, int h) {
+  return (int64_t(b) * a.n_kv_heads + h) * a.group * kQStride;
+}
+
 __device__ __forceinline__ Int2Range int2_range(const DecodeArgs& a, int L, int npt) {
   Int2Range r;
   r.int2_end = max(a.n_sink, L - a.n_recent);
@@ -119,7 +140,7 @@ template <int GP>
 __device__ void load_queries(const DecodeArgs& a, int b, int h, float (*qs)[kHeadDim],
                              float* qsum, int* qexp) {
   const int G = a.group;
-  const float* src = a.qrot + (int64_t(b) * a.n_q_heads + int64_t(h) * G) * kQStride;
+  const float* src = a.qrot + qrot_offset(a, b, h);
   for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x)
     qs[i / kHeadDim][i % kHeadDim] = src[(i / kHeadDim) * kQStride + i % kHeadDim];
   if (threadIdx.x < G) {
@@ -162,7 +183,7 @@ __device__ __forceinline__ void softmax_tile16(int G, int qq, float* lg, float* 
 // int2_end)), the INT2 end tail [16 cl, int2_end) and the bf16 recent window
 // [max(n_sink, L - W), L).
 struct TokenList {
-  int n_sk, n_hd, n_en, n_all, e_begin, r_begin;
+  int n_sk, n_hd, n_en, n_all, e_begin, r_begin, L;
 };
 
 __device__ __forceinline__ TokenList token_list(const DecodeArgs& a, int L, const Int2Range& rg) {
@@ -173,6 +194,7 @@ __device__ __forceinline__ TokenList token_list(const DecodeArgs& a, int L, cons
   t.n_en = max(0, rg.int2_end - t.e_begin);
   t.r_begin = max(a.n_sink, L - a.n_recent);
   t.n_all = t.n_sk + t.n_hd + t.n_en + max(0, L - t.r_begin);
+  t.L = L;
   return t;
 }
 
@@ -215,10 +237,10 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
   const int lane = threadIdx.x & 63, t = lane >> 2, qq = lane & 3;
   const int64_t sh = int64_t(b) * a.n_kv_heads + h;
   // token t: kind (0 none, 1 bf16 row, 2 INT2 chunk slot ts) and base address
-  int kind = 0, ts = 0;
+  int kind = 0, ts = 0, pos = 0;
   const uint8_t* base = a.pool;
   if (t < nt) {
-    const int pos = token_position(a, tl, tile * 16 + t);
+    pos = token_position(a, tl, tile * 16 + t);
     if (pos >= a.n_sink && pos < rg.int2_end) {
       const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
                                        a.page_size, b, h, pos);
@@ -319,7 +341,12 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
     float d = dot[g];
     d += dpp_move<kQuadXor1>(d);
     d += dpp_move<kQuadXor2>(d);
-    lg[g] = (kind != 0 && g < G) ? fmaf(ksc, d, kzr * qsum[g]) : -INFINITY;
+    // row g's query sits at position L - query_count + query_base + g /
+    // head_group and sees the positions up to it (with query_count <=
+    // n_recent only recent-window tokens can lie beyond it; for decode every
+    // position is visible)
+    const bool seen = pos <= tl.L - a.query_count + a.query_base + g / a.head_group;
+    lg[g] = (kind != 0 && g < G && seen) ? fmaf(ksc, d, kzr * qsum[g]) : -INFINITY;
   }
   float corr[GP];
   softmax_tile16<GP>(G, qq, lg, corr, m, l);
@@ -541,7 +568,7 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   __syncthreads();
   for (int k = tid; k < G * kHeadDim; k += blockDim.x) {
     const int g = k / kHeadDim, c = k % kHeadDim;
-    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] = red[0][g][c] + red[1][g][c];
+    a.out[row_offset(a, b, h, g) + c] = red[0][g][c] + red[1][g][c];
   }
 }
 
@@ -661,7 +688,7 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
     float o = 0.f;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) o += red[q][tid];
-    a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + tid] = o;
+    a.out[row_offset(a, b, h, g) + tid] = o;
   }
 }
 
@@ -796,7 +823,7 @@ __device__ void finish_work_group(const DecodeArgs& a, int b, int h, int64_t par
     __syncthreads();
     for (int k = tid; k < G * kHeadDim; k += blockDim.x) {
       const int g = k / kHeadDim, c = k % kHeadDim;
-      a.out[(int64_t(b) * a.n_q_heads + h * G + g) * kHeadDim + c] =
+      a.out[row_offset(a, b, h, g) + c] =
           red[g * kHeadDim + c] + red[(GP + g) * kHeadDim + c];
     }
   }

@@ -116,7 +116,14 @@ DecodeKernel selected_decode_kernel() {
   return kDecodeMfma;
 }
 
-DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len) {
+int multi_query_pass(const kvq_dims& d, int32_t n_query, DecodeKernel which) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const int rows = (which == kDecodeMfma && G <= 8) ? 8 : kMaxGroup;
+  return std::max(1, std::min<int>(n_query, rows / G));
+}
+
+DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len,
+                            int32_t n_query) {
   DecodePlan p{};
   const int64_t int2_end = std::max<int64_t>(d.n_sink, int64_t(max_seq_len) - d.n_recent);
   const int64_t first_chunk = d.n_sink / kChunkTokens;
@@ -134,13 +141,12 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   p.n_split_int2 = static_cast<int>(nb);
   // The MFMA decode deals the token-by-token list out over its INT2 items;
   // the VALU decode (also used for G > 8) gives it a work-group of its own.
-  const int G_plan = d.n_q_heads / d.n_kv_heads;
-  const bool own_token_item = selected_decode_kernel() == kDecodeValu || G_plan > 8;
+  const int G = (d.n_q_heads / d.n_kv_heads) * n_query;   // rows per (b, h)
+  const bool own_token_item = selected_decode_kernel() == kDecodeValu || G > 8;
   p.n_split = p.n_split_int2 + (own_token_item ? 1 : 0);
-  const int G = d.n_q_heads / d.n_kv_heads;
   // arrival tickets [B * Hkv] of the VALU decode's last-arrival combine
   p.ticket_bytes = ((size_t(heads) * sizeof(int32_t) + 255) / 256) * 256;
-  p.qrot_bytes = size_t(batch) * d.n_q_heads * kQStride * sizeof(float);
+  p.qrot_bytes = size_t(heads) * G * kQStride * sizeof(float);
   p.bq_bytes = size_t(heads) * kBqWords * sizeof(uint32_t);
   // tile prefix [B + 1], range starts [kChainGroups + 1], pair ranges [B Hkv]
   auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -199,27 +205,32 @@ int check_append(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* 
 // call); fills the plan.
 int check_decode_args(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
                       int32_t batch, const int32_t* seq_len, int32_t max_seq_len,
-                      const uint16_t* q, float* out, DecodePlan* plan) {
+                      const uint16_t* q, float* out, DecodePlan* plan, int32_t n_query = 1) {
   int rc = check_dims(dims);
   if (rc != KVQ_OK) return rc;
   if ((rc = check_layer(layer)) != KVQ_OK) return rc;
   if ((rc = check_cache(dims, cache)) != KVQ_OK) return rc;
   if (batch < 1 || max_seq_len < 0 || seq_len == nullptr) return KVQ_ERR_ARG;
+  // multi-query: every query must see the whole INT2 history (M <= W)
+  if (n_query < 1 || n_query > dims->n_recent) return KVQ_ERR_ARG;
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
   if (int64_t(max_seq_len) > int64_t(cache->bt_stride) * dims->page_size) return KVQ_ERR_ARG;
   // The MFMA decode counts virtual tiles of the whole batch in 32 bits.
   if (int64_t(batch) * dims->n_kv_heads * (int64_t(max_seq_len) / kChunkTokens + kPieceCostChunksG8 + 2) >=
       (int64_t(1) << 31))
     return KVQ_ERR_UNSUPPORTED;
-  *plan = make_decode_plan(*dims, batch, max_seq_len);
+  *plan = make_decode_plan(*dims, batch, max_seq_len,
+                           multi_query_pass(*dims, n_query, selected_decode_kernel()));
   return KVQ_OK;
 }
 
 // Argument checks of a decode with a caller workspace.
 int check_decode(const kvq_dims* dims, const kvq_layer* layer, const kvq_cache* cache,
                  int32_t batch, const int32_t* seq_len, int32_t max_seq_len, const uint16_t* q,
-                 float* out, void* workspace, size_t workspace_bytes, DecodePlan* plan) {
-  const int rc = check_decode_args(dims, layer, cache, batch, seq_len, max_seq_len, q, out, plan);
+                 float* out, void* workspace, size_t workspace_bytes, DecodePlan* plan,
+                 int32_t n_query = 1) {
+  const int rc =
+      check_decode_args(dims, layer, cache, batch, seq_len, max_seq_len, q, out, plan, n_query);
   if (rc != KVQ_OK) return rc;
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan->total_bytes)
     return KVQ_ERR_WORKSPACE;
@@ -278,6 +289,37 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq
   return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
                                   max_seq_len, q, out, workspace, plan, selected_decode_kernel(),
                                   stream));
+}
+
+size_t kvq_decode_multi_workspace_bytes(const kvq_dims* dims, int32_t batch,
+                                        int32_t max_seq_len, int32_t n_query) {
+  if (check_dims(dims) != KVQ_OK || batch < 1 || max_seq_len < 0 || n_query < 1) return 0;
+  const int pass = multi_query_pass(*dims, n_query, selected_decode_kernel());
+  return make_decode_plan(*dims, batch, max_seq_len, pass).total_bytes;
+}
+
+int kvq_decode_multi_attention(const kvq_dims* dims, const kvq_layer* layer,
+                               const kvq_cache* cache, int32_t batch, const int32_t* seq_len,
+                               int32_t max_seq_len, int32_t n_query, const uint16_t* q,
+                               float* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  DecodePlan plan;
+  const int rc = check_decode(dims, layer, cache, batch, seq_len, max_seq_len, q, out, workspace,
+                              workspace_bytes, &plan, n_query);
+  if (rc != KVQ_OK) return rc;
+  // Passes of at most `pass` queries, each over all pages, in stream order
+  // on the one workspace.
+  const DecodeKernel which = selected_decode_kernel();
+  const int pass = multi_query_pass(*dims, n_query, which);
+  for (int m0 = 0; m0 < n_query; m0 += pass) {
+    const int nq = std::min(pass, n_query - m0);
+    const DecodePlan p = nq == pass ? plan : make_decode_plan(*dims, batch, max_seq_len, nq);
+    const int err = launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
+                                  max_seq_len, q, out, workspace, p, which, stream, nq, m0,
+                                  n_query);
+    if (err != 0) return hip_status(err);
+  }
+  return KVQ_OK;
 }
 
 int kvq_decode_attention_noalloc(const kvq_dims* dims, const kvq_layer* layer,

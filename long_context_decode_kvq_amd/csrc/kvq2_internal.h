@@ -59,7 +59,11 @@ constexpr int kChainGroups = 1024;
 constexpr int kPieceCostChunks = 80;
 constexpr int kPieceCostChunksG8 = 150;
 
-DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len);
+// Plan of a decode with n_query queries per sequence (1 for decode; M for
+// multi-query attention): its rows per (sequence, KV head) are
+// n_query * Hq / Hkv.
+DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len,
+                            int32_t n_query = 1);
 
 // Tuning constants of the MFMA decode, read once per process from the
 // environment (KVQ_PIECE_COST, KVQ_ROUND_WEIGHTS, KVQ_XCD_WEIGHTS) with the
@@ -101,7 +105,13 @@ int launch_decode_step(const kvq_dims& d, float sm_scale, const kvq_layer& layer
 int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                   const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
                   int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
-                  const DecodePlan& plan, DecodeKernel which, void* stream);
+                  const DecodePlan& plan, DecodeKernel which, void* stream,
+                  int32_t n_query = 1, int32_t query_base = 0, int32_t query_count = 1);
+
+// Queries per launch of a multi-query attention of M queries per sequence:
+// the matrix-core decode takes at most 8 rows (queries x Hq / Hkv) per pass
+// over the pages, the VALU decode 16.
+int multi_query_pass(const kvq_dims& d, int32_t n_query, DecodeKernel which);
 
 // The library-owned decode scratch of kvq_decode_attention_noalloc: a
 // file-scope device array of kStaticScratchBytes per GPU.

@@ -43,7 +43,8 @@ class KvqCache(C.Structure):
 
 
 EXPORTS = ("kvq_calibrate", "kvq_quantize_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_decode_step",
+           "kvq_decode_attention", "kvq_decode_multi_workspace_bytes",
+           "kvq_decode_multi_attention", "kvq_decode_attention_noalloc", "kvq_decode_step",
            "kvq_status_string", "kvq_last_error")
 PROBE_EXPORTS = ("kvq_probe_stream_read", "kvq_probe_chunk_read")
 
@@ -67,6 +68,12 @@ def lib():
         L.kvq_decode_attention.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
                                            C.POINTER(KvqCache), I32, P, I32, P, P, P, SZ, P]
         L.kvq_decode_attention.restype = C.c_int
+        L.kvq_decode_multi_workspace_bytes.argtypes = [C.POINTER(KvqDims), I32, I32, I32]
+        L.kvq_decode_multi_workspace_bytes.restype = SZ
+        L.kvq_decode_multi_attention.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
+                                                 C.POINTER(KvqCache), I32, P, I32, I32, P, P, P,
+                                                 SZ, P]
+        L.kvq_decode_multi_attention.restype = C.c_int
         L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
                                                    C.POINTER(KvqCache), I32, P, I32, P, P, P]
         L.kvq_decode_attention_noalloc.restype = C.c_int
@@ -167,6 +174,20 @@ def decode_attention(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, seq_l
                                     max_seq_len, _ptr(q), _ptr(out), _ptr(workspace), nbytes,
                                     _stream_handle(stream))
     _check(rc, "kvq_decode_attention")
+
+
+def decode_multi_workspace_bytes(d: KvqDims, batch: int, max_seq_len: int, n_query: int) -> int:
+    return int(lib().kvq_decode_multi_workspace_bytes(C.byref(d), batch, max_seq_len, n_query))
+
+
+def decode_multi_attention(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, seq_len,
+                           max_seq_len: int, n_query: int, q, out, workspace, stream=None):
+    """kvq_decode_multi_attention: q, out [batch][n_query][Hq][128]."""
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kvq_decode_multi_attention(C.byref(d), C.byref(lay), C.byref(cch), batch,
+                                          _ptr(seq_len), max_seq_len, n_query, _ptr(q), _ptr(out),
+                                          _ptr(workspace), nbytes, _stream_handle(stream))
+    _check(rc, "kvq_decode_multi_attention")
 
 
 def decode_attention_noalloc(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, seq_len,

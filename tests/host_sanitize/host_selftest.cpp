@@ -84,6 +84,21 @@ int main() {
   CHECK(kvq_decode_step(&d, &lay, &c, 2, i32, i32, 2, 1, u16, u16, i32, 100, u16, f32, ws, need, nullptr) == KVQ_OK);
   CHECK(kvq_quantize_append(&d, &lay, &c, 2, i32, i32, 0, 0, nullptr, nullptr, nullptr) == KVQ_OK);
 
+  // ---- multi-query attention: 1 <= M <= n_recent, passes of at most 8 rows
+  const size_t need4 = kvq_decode_multi_workspace_bytes(&d, 2, 100, 4);
+  const size_t need2 = kvq_decode_multi_workspace_bytes(&d, 2, 100, 2);
+  CHECK(need2 > need);                                  // 8 rows: more partials
+  CHECK(need4 == need2);                                // 16 rows: two passes of 8
+  CHECK(kvq_decode_multi_workspace_bytes(&d, 2, 100, 1) == need);
+  const int before_multi = kvq::g_launches;
+  CHECK(kvq_decode_multi_attention(&d, &lay, &c, 2, i32, 100, 5, u16, f32, ws, need4, nullptr) == KVQ_OK);
+  CHECK(kvq::g_launches == before_multi + 3);           // queries 0-1, 2-3, 4
+  CHECK(kvq_decode_multi_attention(&d, &lay, &c, 2, i32, 100, 4, u16, f32, ws, need4 - 1, nullptr) == KVQ_ERR_WORKSPACE);
+  CHECK(kvq_decode_multi_attention(&d, &lay, &c, 2, i32, 100, 0, u16, f32, ws, need4, nullptr) == KVQ_ERR_ARG);
+  kvq_dims w2 = d;
+  w2.n_recent = 2;
+  CHECK(kvq_decode_multi_attention(&w2, &lay, &c, 2, i32, 100, 3, u16, f32, ws, 1 << 30, nullptr) == KVQ_ERR_ARG);
+
   // ---- planning over a sweep of shapes (no overflow, monotone in batch)
   for (int G : {1, 2, 3, 4, 8, 16})
     for (int P : {16, 32, 64})
