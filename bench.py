@@ -322,6 +322,9 @@ def main():
                          "(kvq_quantize_append of M tokens + kvq_decode_multi_attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the read-ceiling probes")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps from the host one by one instead of replaying "
+                         "them as one captured HIP graph")
     ap.add_argument("--two-calls", action="store_true",
                     help="run each step as kvq_quantize_append + kvq_decode_attention instead "
                          "of one kvq_decode_step")
@@ -390,32 +393,47 @@ def main():
              for k in range(n_steps)]
     stream = torch.cuda.current_stream()
 
-    def decode_call(h, seq, q):
+    def decode_call(h, seq, q, st):
         if M == 1:
-            kvq2.decode_attention(kd, lay, h, w.batch, seq, max_len, q, out, ws, stream)
+            kvq2.decode_attention(kd, lay, h, w.batch, seq, max_len, q, out, ws, st)
         else:
-            kvq2.decode_multi_attention(kd, lay, h, w.batch, seq, max_len, M, q, out, ws, stream)
+            kvq2.decode_multi_attention(kd, lay, h, w.batch, seq, max_len, M, q, out, ws, st)
 
-    def step(k):
+    def step(k, st):
         h = handles[k % copies]
         if M > 1:
             kvq2.quantize_append(kd, lay, h, w.batch, starts[k], cu1, w.batch * M, M, k_new[k],
-                                 v_new[k], stream)
-            decode_call(h, seqs[k], qs[k])
+                                 v_new[k], st)
+            decode_call(h, seqs[k], qs[k], st)
         elif args.two_calls:
             kvq2.quantize_append(kd, lay, h, w.batch, starts[k], cu1, w.batch, 1, k_new[k],
-                                 v_new[k], stream)
-            kvq2.decode_attention(kd, lay, h, w.batch, seqs[k], max_len, qs[k], out, ws, stream)
+                                 v_new[k], st)
+            kvq2.decode_attention(kd, lay, h, w.batch, seqs[k], max_len, qs[k], out, ws, st)
         else:
             kvq2.decode_step(kd, lay, h, w.batch, starts[k], cu1, w.batch, 1, k_new[k], v_new[k],
-                             seqs[k], max_len, qs[k], out, ws, stream)
+                             seqs[k], max_len, qs[k], out, ws, st)
 
-    # ---- untimed pre-warm: back-to-back decode calls over the cache as built
-    # (the state before the first step), at most two groups of ~10 ms queued
-    # so that the host stays just ahead of the GPU; no idle gap before the
-    # warm-up steps.
+    for k in range(args.warmup):
+        step(k, stream)
+    torch.cuda.synchronize()
+    # The K timed steps, captured as one HIP graph (replayed once below): a
+    # serving loop launches its decode step that way, and at batch 1 the
+    # per-call host cost of launching from Python exceeds the GPU time.
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.steps):
+                step(args.warmup + i, cap)
+        torch.cuda.synchronize()
+
+    # ---- untimed pre-warm: back-to-back decode calls over the cache (whose
+    # contents they only read), at most two groups of ~10 ms queued so that
+    # the host stays just ahead of the GPU.
     def pre_call(i):
-        decode_call(handles[i % copies], seq0, qs[0])
+        decode_call(handles[i % copies], seq0, qs[0], stream)
 
     pre_call(0)
     torch.cuda.synchronize()
@@ -436,17 +454,18 @@ def main():
         if len(marks) > 2:
             marks.pop(0).synchronize()
     prewarm_wall = time.perf_counter() - t_pre
-
-    for k in range(args.warmup):
-        step(k)
     torch.cuda.synchronize()
+
     # Timed region: K whole steps back to back, one event pair around them
     # (an event recorded between kernels costs ~5 us of GPU time per event).
     e_begin = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     e_begin.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i, stream)
     e_end.record(stream)
     # The decode launch on its own, for the roofline: K launches over the
     # cache after the last step, each bracketed by HIP events on the stream it
@@ -457,7 +476,7 @@ def main():
           for _ in range(args.steps)]
     for a0, a1 in ev:
         a0.record(stream)
-        decode_call(handles[last % copies], seqs[last], qs[last])
+        decode_call(handles[last % copies], seqs[last], qs[last], stream)
         a1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e_begin.elapsed_time(e_end) / args.steps
@@ -519,6 +538,8 @@ def main():
             "step_call": ("kvq_quantize_append + kvq_decode_multi_attention" if M > 1 else
                           "kvq_quantize_append + kvq_decode_attention" if args.two_calls
                           else "kvq_decode_step"),
+            "launch": ("host loop" if graph is None
+                       else f"one HIP graph of the {args.steps} steps, replayed once"),
             "us_per_step": round(ms_per_step * 1e3, 2),
             "decode_us": round(dec_avg_ms * 1e3, 2),
             "decode_us_p10": round(pct[10], 2),
