@@ -101,6 +101,19 @@ def hadamard(n: int = HEAD_DIM) -> np.ndarray:
     return sign / math.sqrt(n)
 
 
+def hadamard_blocks(n: int = HEAD_DIM, block: int = HEAD_DIM) -> np.ndarray:
+    """Block-diagonal Hadamard: n / block copies of hadamard(block) on the
+    diagonal (block = n is the full transform).  [OSCAR-S 2.2-A item 3 does
+    not fix the transform's size; a block Hadamard is the reading under which
+    smaller quantization groups keep their channel mixing local.]"""
+    assert n % block == 0
+    H = np.zeros((n, n))
+    Hb = hadamard(block)
+    for k in range(n // block):
+        H[k * block:(k + 1) * block, k * block:(k + 1) * block] = Hb
+    return H
+
+
 def bitrev(i: int, bits: int = 7) -> int:
     r = 0
     for _ in range(bits):
@@ -138,9 +151,11 @@ def eigenbasis(C: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return w, U
 
 
-def composite_rotation(U: np.ndarray) -> np.ndarray:
-    """R = U . H_Had . P_br in fp64 [OSCAR-S 2.2-A item 3, the formula R_K = U_Q H P]."""
-    return U @ hadamard(U.shape[0]) @ bitrev_permutation(U.shape[0])
+def composite_rotation(U: np.ndarray, hadamard_block: int = HEAD_DIM) -> np.ndarray:
+    """R = U . H_Had . P_br in fp64 [OSCAR-S 2.2-A item 3, the formula R_K = U_Q H P];
+    H_Had is the full Sylvester transform, or its block-diagonal form."""
+    n = U.shape[0]
+    return U @ hadamard_blocks(n, hadamard_block) @ bitrev_permutation(n)
 
 
 # --------------------------------------------------------------------------
@@ -208,7 +223,7 @@ class Calibration:
 
 def calibrate(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
               n_q_heads: int, n_kv_heads: int, sm_scale: float,
-              clip_quantile: float = 0.999) -> Calibration:
+              clip_quantile: float = 0.999, hadamard_block: int = HEAD_DIM) -> Calibration:
     """Offline calibration of one layer [OSCAR-S 2.2-A items 1-4].
 
     q_bits [N][Hq][128], k_bits / v_bits [N][Hkv][128] bf16 bit patterns.
@@ -229,8 +244,8 @@ def calibrate(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         qg = q[:, h * G:(h + 1) * G, :]
         wq, UQ = eigenbasis(query_covariance(qg))
         ws, US = eigenbasis(score_covariance(qg, k[:, h, :], v[:, h, :], sm_scale))
-        R_K[h] = composite_rotation(UQ).astype(np.float32)
-        R_V[h] = composite_rotation(US).astype(np.float32)
+        R_K[h] = composite_rotation(UQ, hadamard_block).astype(np.float32)
+        R_V[h] = composite_rotation(US, hadamard_block).astype(np.float32)
         eQ[h], eS[h] = wq, ws
     rk = np.stack([rotate(k_bits[:, h, :], R_K[h]) for h in range(n_kv_heads)])
     rv = np.stack([rotate(v_bits[:, h, :], R_V[h]) for h in range(n_kv_heads)])
@@ -263,8 +278,25 @@ def rotate(x_bits: np.ndarray, R: np.ndarray) -> np.ndarray:
 # Online path, step 2: clip + asymmetric INT2 quantization (pinned fp32 steps)
 # --------------------------------------------------------------------------
 
+def quantize_groups(r_bits: np.ndarray, clip: float, group: int):
+    """quantize() on each contiguous group of `group` channels of the rotated
+    vectors [..., 128] separately: codes uint8 [..., 128] and fp16 bits of
+    (scale, zero) [..., 128 / group], group k covering channels
+    [k group, (k + 1) group).  [OSCAR-S 2.2-A item 3: P_br balances the
+    dynamic range inside the quantization groups; with group < 128 each group
+    has its own scale and zero.]"""
+    r = np.asarray(r_bits, np.uint16)
+    ng = HEAD_DIM // group
+    parts = [quantize(r[..., k * group:(k + 1) * group], clip) for k in range(ng)]
+    codes = np.concatenate([p[0] for p in parts], axis=-1)
+    s = np.stack([p[1] for p in parts], axis=-1)
+    z = np.stack([p[2] for p in parts], axis=-1)
+    return codes, s, z
+
+
 def quantize(r_bits: np.ndarray, clip: float):
-    """Quantize rotated bf16 vectors [..., 128] to 2-bit codes + fp16 (scale, zero).
+    """Quantize rotated bf16 vectors [..., n] (one group each) to 2-bit codes +
+    fp16 (scale, zero).
 
     [OSCAR-S 1 and 2.2-B: INT2 = 4 levels; 2.2-A item 4: per-layer clipping of
     rotated activations.]  Steps, all IEEE fp32 with RNE:
@@ -273,7 +305,7 @@ def quantize(r_bits: np.ndarray, clip: float):
       s_h = fp16(s), z_h = fp16(mn)
       if s_h == 0: codes = 0
       else: inv = 1 / s_h; t = (x - z_h) * inv (two roundings); code = clamp(rint(t), 0, 3)
-    Returns (codes uint8 [..., 128], s_h bits uint16 [...], z_h bits uint16 [...]).
+    Returns (codes uint8 [..., n], s_h bits uint16 [...], z_h bits uint16 [...]).
     """
     r = bf16_bits_to_f32(r_bits)
     c = np.float32(clip)
@@ -300,6 +332,16 @@ def dequantize(codes: np.ndarray, s_bits: np.ndarray, z_bits: np.ndarray) -> np.
     return z[..., None] + codes.astype(np.float64) * s[..., None]
 
 
+def dequantize_groups(codes: np.ndarray, s_bits: np.ndarray, z_bits: np.ndarray) -> np.ndarray:
+    """x_hat = z_k + code * s_k on every channel of group k: codes [..., 128],
+    s_bits / z_bits [..., 128 / group]."""
+    ng = s_bits.shape[-1]
+    gs = HEAD_DIM // ng
+    s = np.repeat(f16_bits_to_f32(s_bits).astype(np.float64), gs, axis=-1)
+    z = np.repeat(f16_bits_to_f32(z_bits).astype(np.float64), gs, axis=-1)
+    return z + codes.astype(np.float64) * s
+
+
 # --------------------------------------------------------------------------
 # Online path, step 3: byte layout of one 16-token chunk (one KV head)
 # --------------------------------------------------------------------------
@@ -316,9 +358,19 @@ def v_byte_offset(t: int, g: int) -> int:
     return V_CODES_OFF + 32 * (g & 15) + 8 * (t >> 2) + 4 * (g >> 4) + (t & 3)
 
 
-def param_offset(kind: int, t: int) -> int:
-    """kind 0 = K, 1 = V; bytes [off, off+2) scale, [off+2, off+4) zero (little endian)."""
-    return (K_PARAMS_OFF if kind == 0 else V_PARAMS_OFF) + 4 * t
+def param_offset(kind: int, t: int, group: int = HEAD_DIM, k: int = 0) -> int:
+    """(scale, zero) of quantization group k of slot t: kind 0 = K, 1 = V;
+    bytes [off, off+2) scale, [off+2, off+4) zero (little endian).  With
+    ng = 128 / group pairs per slot the K pairs fill [1024, 1024 + 64 ng) and
+    the V pairs the next 64 ng bytes, slot-major (group 128: 1024 + 4 t and
+    1088 + 4 t)."""
+    ng = HEAD_DIM // group
+    return K_CODES_OFF + 1024 + kind * 64 * ng + 4 * (t * ng + k)
+
+
+def chunk_bytes(group: int = HEAD_DIM) -> int:
+    """Bytes of one 16-token chunk: 1024 code bytes + 2 x 16 x (128 / group) x 4."""
+    return 1024 + 128 * (HEAD_DIM // group)
 
 
 _T = np.arange(CHUNK_TOKENS)[:, None]
@@ -353,6 +405,7 @@ class Dims:
     n_recent: int
     sm_scale: float = 1.0 / math.sqrt(HEAD_DIM)
     head_dim: int = HEAD_DIM
+    quant_group: int = HEAD_DIM          # channels per (scale, zero) pair: 32, 64 or 128
 
     @property
     def group(self) -> int:
@@ -362,7 +415,7 @@ class Dims:
 class OracleCache:
     """Caller-visible state of the cache, byte for byte.
 
-    pool   uint8 [num_pages][Hkv][P/16][1152]      INT2 history
+    pool   uint8 [num_pages][Hkv][P/16][chunk_bytes(quant_group)]  INT2 history
     sink   uint16 (bf16) [B][Hkv][n_sink][2][128]  rotated K (index 0) and V (1)
     recent uint16 (bf16) [B][Hkv][n_recent][2][128] ring: position pos lives in
            slot (pos - n_sink) mod n_recent
@@ -380,7 +433,8 @@ class OracleCache:
         self.num_pages = num_pages
         self.block_table = np.asarray(block_table, dtype=np.int32)
         cpp = d.page_size // CHUNK_TOKENS
-        self.pool = np.full((num_pages, d.n_kv_heads, cpp, CHUNK_BYTES), fill, np.uint8)
+        self.pool = np.full((num_pages, d.n_kv_heads, cpp, chunk_bytes(d.quant_group)), fill,
+                            np.uint8)
         self.sink = np.full((batch, d.n_kv_heads, max(d.n_sink, 0), 2, HEAD_DIM), fill * 0x0101, np.uint16)
         self.recent = np.full((batch, d.n_kv_heads, d.n_recent, 2, HEAD_DIM), fill * 0x0101, np.uint16)
 
@@ -391,27 +445,30 @@ class OracleCache:
         cpp = P // CHUNK_TOKENS
         pages = self.block_table[b, positions // P].astype(np.int64)
         chunk_in_page = (positions % P) // CHUNK_TOKENS
-        return ((pages * self.d.n_kv_heads + h) * cpp + chunk_in_page) * CHUNK_BYTES
+        return ((pages * self.d.n_kv_heads + h) * cpp + chunk_in_page) * chunk_bytes(
+            self.d.quant_group)
 
     def write_int2(self, b: int, h: int, kind: int, positions, r_bits: np.ndarray, clip: float):
         """Quantize rotated bf16 vectors r_bits [n][128] and store them at `positions`."""
         positions = np.asarray(positions, dtype=np.int64)
         if positions.size == 0:
             return
-        codes, s, z = quantize(r_bits, clip)
+        gs = self.d.quant_group
+        codes, s, z = quantize_groups(r_bits, clip, gs)              # s, z [n][ng]
         packed = pack_codes(codes)                                   # [n][32]
         base = self._chunk_bases(b, h, positions)                    # [n]
         t = positions % CHUNK_TOKENS
         table = K_BYTE_TABLE if kind == 0 else V_BYTE_TABLE
         flat = self.pool.reshape(-1)
         flat[base[:, None] + table[t]] = packed
-        off = base + np.array([param_offset(kind, int(tt)) for tt in t], dtype=np.int64)
-        sb = s.astype(np.uint16)
-        zb = z.astype(np.uint16)
-        flat[off + 0] = (sb & 0xFF).astype(np.uint8)
-        flat[off + 1] = (sb >> 8).astype(np.uint8)
-        flat[off + 2] = (zb & 0xFF).astype(np.uint8)
-        flat[off + 3] = (zb >> 8).astype(np.uint8)
+        for k in range(HEAD_DIM // gs):
+            off = base + np.array([param_offset(kind, int(tt), gs, k) for tt in t], np.int64)
+            sb = s[:, k].astype(np.uint16)
+            zb = z[:, k].astype(np.uint16)
+            flat[off + 0] = (sb & 0xFF).astype(np.uint8)
+            flat[off + 1] = (sb >> 8).astype(np.uint8)
+            flat[off + 2] = (zb & 0xFF).astype(np.uint8)
+            flat[off + 3] = (zb >> 8).astype(np.uint8)
 
     def read_int2(self, b: int, h: int, kind: int, positions) -> np.ndarray:
         """Dequantized fp64 vectors [n][128] of INT2 positions."""
@@ -421,10 +478,15 @@ class OracleCache:
         table = K_BYTE_TABLE if kind == 0 else V_BYTE_TABLE
         flat = self.pool.reshape(-1)
         codes = unpack_codes(flat[base[:, None] + table[t]])
-        off = base + np.array([param_offset(kind, int(tt)) for tt in t], dtype=np.int64)
-        s = flat[off].astype(np.uint16) | (flat[off + 1].astype(np.uint16) << 8)
-        z = flat[off + 2].astype(np.uint16) | (flat[off + 3].astype(np.uint16) << 8)
-        return dequantize(codes, s, z)
+        gs = self.d.quant_group
+        ng = HEAD_DIM // gs
+        s = np.zeros((positions.size, ng), np.uint16)
+        z = np.zeros((positions.size, ng), np.uint16)
+        for k in range(ng):
+            off = base + np.array([param_offset(kind, int(tt), gs, k) for tt in t], np.int64)
+            s[:, k] = flat[off].astype(np.uint16) | (flat[off + 1].astype(np.uint16) << 8)
+            z[:, k] = flat[off + 2].astype(np.uint16) | (flat[off + 3].astype(np.uint16) << 8)
+        return dequantize_groups(codes, s, z)
 
     # -- append -------------------------------------------------------------
     def append(self, R_K, R_V, clip_K, clip_V, b: int, start: int,

@@ -42,15 +42,20 @@ def bf16_bits(x) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def hadamard_bitrev() -> np.ndarray:
-    """H P_br in fp64: column k is column bitrev7(k) of the Sylvester Hadamard / sqrt(128)."""
-    H = scipy.linalg.hadamard(D).astype(np.float64) / math.sqrt(D)
+def hadamard_bitrev(block: int = D) -> np.ndarray:
+    """H P_br in fp64: column k is column bitrev7(k) of the Sylvester Hadamard
+    / sqrt(128), or of its block-diagonal form with blocks of `block`."""
+    H = np.zeros((D, D))
+    Hb = scipy.linalg.hadamard(block).astype(np.float64) / math.sqrt(block)
+    for i in range(D // block):
+        H[i * block:(i + 1) * block, i * block:(i + 1) * block] = Hb
     cols = [int(format(k, "07b")[::-1], 2) for k in range(D)]
     return H[:, cols]
 
 
 class ClosedFormCalibration:
-    def __init__(self, n_q_heads: int = 4, n_kv_heads: int = 2, seed: int = 2024):
+    def __init__(self, n_q_heads: int = 4, n_kv_heads: int = 2, seed: int = 2024,
+                 hadamard_block: int = D):
         Hq, Hkv = n_q_heads, n_kv_heads
         G = Hq // Hkv
         rng = np.random.default_rng(seed)
@@ -75,7 +80,7 @@ class ClosedFormCalibration:
         import torch
         back = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
         assert np.array_equal(back(self.q), q) and np.array_equal(back(self.v), v)
-        HP = hadamard_bitrev()
+        HP = hadamard_bitrev(hadamard_block)
         self.R_K = np.zeros((Hkv, D, D))
         self.R_V = np.zeros((Hkv, D, D))
         self.eig_Q = np.zeros((Hkv, D))
@@ -93,10 +98,10 @@ class ClosedFormCalibration:
             self.R_V[h] = US @ HP
             self.eig_Q[h] = pool * self.alpha[::-1] ** 2 / N_TOKENS
             self.eig_S[h] = self.beta[h][order] ** 2 / N_TOKENS
-        # clip at p = 1: every rotated key entry is +-fp32(1/sqrt 128) times 1;
-        # the largest rotated value entry is beta_max times it (fp64 product,
-        # then fp32, then bf16)
-        c32 = np.float64(np.float32(1.0 / math.sqrt(D)))
+        # clip at p = 1: every nonzero rotated key entry is +-fp32(1/sqrt(block))
+        # times 1; the largest rotated value entry is beta_max times it (fp64
+        # product, then fp32, then bf16)
+        c32 = np.float64(np.float32(1.0 / math.sqrt(hadamard_block)))
         to_f = lambda x: float(back(bf16_bits(np.float32(x)))[()])
         self.clip_K = to_f(c32)
         self.clip_V = to_f(np.float32(max(b.max() for b in self.beta) * c32))

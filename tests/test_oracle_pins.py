@@ -576,3 +576,147 @@ def test_decode_multi_sequence_shorter_than_the_queries():
     assert np.array_equal(got[1], np.zeros((Hq, 128), np.float32))
     assert np.allclose(got[2], oc.decode(R_K, R_V, [1], q1)[0], rtol=0, atol=1e-6)
     assert np.allclose(got[3], oc.decode(R_K, R_V, [2], q1)[0], rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------- quantization groups < 128
+
+def test_block_hadamard_is_blockwise_sylvester():
+    for blk in (32, 64, 128):
+        H = O.hadamard_blocks(128, blk)
+        assert np.abs(H @ H.T - np.eye(128)).max() < 1e-12
+        ref = scipy.linalg.hadamard(blk) / math.sqrt(blk)
+        for k in range(128 // blk):
+            assert np.array_equal(H[k * blk:(k + 1) * blk, k * blk:(k + 1) * blk], ref)
+        off = H.copy()
+        for k in range(128 // blk):
+            off[k * blk:(k + 1) * blk, k * blk:(k + 1) * blk] = 0
+        assert not off.any()
+    assert np.array_equal(O.hadamard_blocks(128, 128), O.hadamard(128))
+
+
+def test_bitrev_spreads_one_hadamard_block_over_every_group():
+    """U = I, Hadamard blocks of 32: x = e_j with j in the first block lights
+    up H coordinates 0..31 only, and x' = R^T x = P H x puts coordinate
+    y = bitrev7(i) at channel i, i.e. at the channels i = 0 mod 4 -- eight in
+    each quantization group of 32, each of magnitude 1/sqrt(32)."""
+    R = O.composite_rotation(np.eye(128), 32).astype(np.float32)
+    e = np.zeros((1, 128), np.float32)
+    e[0, 9] = 1.0
+    r = O.bf16_bits_to_f32(O.rotate(bf16(e), R))[0]
+    nz = np.flatnonzero(r)
+    assert np.array_equal(nz, np.arange(0, 128, 4))
+    mag = O.bf16_bits_to_f32(bf16(np.float32(1 / math.sqrt(32))))
+    assert np.all(np.abs(r[nz]) == mag)
+    for g in range(4):
+        assert np.count_nonzero(r[32 * g:32 * (g + 1)]) == 8
+
+
+def _golden_by_name():
+    return {c[0]: c for c in _golden_quantizer_cases()}
+
+
+@pytest.mark.parametrize("group,names", [
+    (32, ("grid", "constant", "ties", "third")),
+    (64, ("ties", "grid")),
+    (32, ("negzero", "third", "constant", "grid")),
+])
+def test_quantizer_groups_are_independent_golden(group, names):
+    """Each group of `group` channels holds one hand-derived case (all with the
+    same clip): every group gets exactly that case's scale, zero and codes,
+    so nothing leaks between groups."""
+    gold = _golden_by_name()
+    clip = 8.0 if "grid" not in names else 4.0
+    parts = []
+    for n in names:
+        pat = np.resize(np.asarray(gold[n][2], np.float32), group)
+        parts.append(pat)
+    x = bf16(np.concatenate(parts)[None])
+    codes, s, z = O.quantize_groups(x, clip, group)
+    for k, n in enumerate(names):
+        _, _, _, sbits, zbits, cpat, _ = gold[n]
+        assert (int(s[0, k]), int(z[0, k])) == (sbits, zbits), (n, k)
+        assert np.array_equal(codes[0, k * group:(k + 1) * group],
+                              np.resize(np.asarray(cpat, np.uint8), group)), (n, k)
+
+
+def test_quantizer_groups_128_is_quantize_and_bound_holds_per_group():
+    x = bf16((rng.standard_normal((50, 128)) * rng.uniform(0.1, 5, (50, 1))).astype(np.float32))
+    c1, s1, z1 = O.quantize(x, 6.0)
+    c2, s2, z2 = O.quantize_groups(x, 6.0, 128)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2[:, 0]) and np.array_equal(z1, z2[:, 0])
+    for g in (32, 64):
+        c, s, z = O.quantize_groups(x, 6.0, g)
+        xh = O.dequantize_groups(c, s, z)
+        xc = np.minimum(np.maximum(O.bf16_bits_to_f32(x).astype(np.float64), -6.0), 6.0)
+        sh = np.repeat(O.f16_bits_to_f32(s).astype(np.float64), g, axis=-1)
+        zh = np.repeat(O.f16_bits_to_f32(z).astype(np.float64), g, axis=-1)
+        inside = (xc >= zh) & (xc <= zh + 3 * sh)
+        assert np.all(np.abs(xc - xh)[inside] <= (sh / 2 * (1 + 2 ** -18))[inside])
+        # finer groups never quantize worse than the whole vector on average
+        err_g = np.abs(xc - xh).mean()
+        err_128 = np.abs(xc - O.dequantize(c1, s1, z1)).mean()
+        assert err_g <= err_128
+
+
+def test_group_chunk_layout_covers_the_chunk_once():
+    for g in (32, 64, 128):
+        ng = 128 // g
+        cb = O.chunk_bytes(g)
+        assert cb == 1024 + 128 * ng
+        offs = sorted(O.param_offset(kind, t, g, k) + j for kind in (0, 1) for t in range(16)
+                      for k in range(ng) for j in range(4))
+        assert offs == list(range(1024, cb))
+    assert O.param_offset(0, 3) == 1024 + 12 and O.param_offset(1, 3) == 1088 + 12
+    # slot-major pairs: slot t's ng pairs are contiguous (literal layout)
+    assert O.param_offset(0, 3, 32, 2) == 1024 + 4 * (3 * 4 + 2)
+    assert O.param_offset(1, 15, 32, 3) == 1024 + 256 + 4 * (15 * 4 + 3) == 1532
+    assert O.param_offset(1, 1, 64, 1) == 1024 + 128 + 4 * 3
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_group_cache_decode_is_dense_attention_over_groupwise_dequantized(group):
+    """Bulk == token-by-token bytes with quantization groups, and decode equal
+    to dense attention over K/V dequantized group by group straight from
+    quantize_groups of the rotated tokens (no cache involved)."""
+    Hq, Hkv, P, ns, W, L = 4, 2, 16, 4, 8, 90
+    d = O.Dims(Hq, Hkv, P, ns, W, quant_group=group)
+    npg = math.ceil(L / P)
+    bt = rng.permutation(npg).astype(np.int32)[None]
+    R_K, R_V = _rand_R(Hkv), _rand_R(Hkv)
+    k = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32) * 2)
+    v = bf16(rng.standard_normal((L, Hkv, 128)).astype(np.float32))
+    c1 = O.OracleCache(d, 1, npg, bt)
+    c2 = O.OracleCache(d, 1, npg, bt)
+    c1.append(R_K, R_V, 5.0, 5.0, 0, 0, k, v)
+    O.append_token_by_token(c2, R_K, R_V, 5.0, 5.0, 0, 0, k, v)
+    assert np.array_equal(c1.pool, c2.pool) and np.array_equal(c1.recent, c2.recent)
+    q = bf16(rng.standard_normal((1, Hq, 128)).astype(np.float32))
+    got = c1.decode(R_K, R_V, [L], q)[0]
+    G = Hq // Hkv
+    for h in range(Hkv):
+        Kr = np.zeros((L, 128))
+        Vr = np.zeros((L, 128))
+        for pos in range(L):
+            rk, rv = O.rotate(k[pos:pos + 1, h], R_K[h]), O.rotate(v[pos:pos + 1, h], R_V[h])
+            if ns <= pos < L - W:
+                Kr[pos] = O.dequantize_groups(*O.quantize_groups(rk, 5.0, group))[0]
+                Vr[pos] = O.dequantize_groups(*O.quantize_groups(rv, 5.0, group))[0]
+            else:
+                Kr[pos], Vr[pos] = O.bf16_bits_to_f32(rk)[0], O.bf16_bits_to_f32(rv)[0]
+        for g in range(h * G, (h + 1) * G):
+            qr = R_K[h].astype(np.float64).T @ O.bf16_bits_to_f32(q[0, g]).astype(np.float64)
+            lg = d.sm_scale * (Kr @ qr)
+            p = np.exp(lg - lg.max())
+            ref = R_V[h].astype(np.float64) @ ((p @ Vr) / p.sum())
+            assert np.allclose(got[g], ref, rtol=0, atol=1e-5)
+
+
+def test_calibrate_block_hadamard_closed_form():
+    from calib_fixture import ClosedFormCalibration
+    fx = ClosedFormCalibration(n_q_heads=4, n_kv_heads=2, hadamard_block=32)
+    cal = O.calibrate(fx.q, fx.k, fx.v, 4, 2, 1 / math.sqrt(128), clip_quantile=1.0,
+                      hadamard_block=32)
+    for h in range(2):
+        assert np.abs(cal.R_K[h] - fx.R_K[h].astype(np.float32)).max() <= 1e-7
+        assert np.abs(cal.R_V[h] - fx.R_V[h].astype(np.float32)).max() <= 1e-7
+    assert (cal.clip_K, cal.clip_V) == (fx.clip_K, fx.clip_V)
