@@ -22,7 +22,9 @@
  *     once with o = R_V o'.
  *   - Rotation of a new vector: fp64 accumulation over j = 0..127 in order,
  *     rounded to fp32 then to bf16 (round-to-nearest-even).
- *   - INT2 quantizer per (token, KV head, K|V) group of 128 channels:
+ *   - INT2 quantizer per (token, KV head, K|V) group of quant_group
+ *     contiguous rotated channels (128: the whole vector; 32 or 64: 4 or 2
+ *     groups, each with its own pair):
  *     x = clamp(r, -clip, clip) + 0; s = fp16((max x - min x) / 3);
  *     z = fp16(min x); code = clamp(rint((x - z) * (1 / s)), 0, 3) with each
  *     fp32 step rounded separately; s == 0 gives all-zero codes.
@@ -33,8 +35,10 @@
  *       recent [max(n_sink, L - n_recent), L)      bf16 ring, rotated
  *
  * Memory layout (all device buffers are owned by the caller):
- *   pool         uint8 [num_pages][n_kv_heads][page_size/16][1152]
- *                One 1152-byte chunk holds 16 consecutive positions
+ *   pool         uint8 [num_pages][n_kv_heads][page_size/16][C]
+ *                with C = 1024 + 128 ng bytes, ng = 128 / quant_group
+ *                (1152 for one pair per vector, 1280 or 1536).
+ *                One C-byte chunk holds 16 consecutive positions
  *                16c..16c+15 of one sequence and one KV head.  Position pos
  *                lives in physical page block_table[b][pos / page_size],
  *                chunk (pos % page_size) / 16, slot t = pos % 16.
@@ -43,9 +47,12 @@
  *                  [   0,  512) K codes: byte 32*t + g
  *                  [ 512, 1024) V codes: byte 512 + 32*(g % 16) + 8*(t / 4)
  *                                              + 4*(g / 16) + (t % 4)
- *                  [1024, 1088) K params: slot t at 1024 + 4t: fp16 s, fp16 z
- *                  [1088, 1152) V params: slot t at 1088 + 4t: fp16 s, fp16 z
- *                (fp16 little-endian; g = channel / 4 in 0..31.)
+ *                  [1024, 1024 + 64 ng) K params: group k of slot t at
+ *                        1024 + 4 (t ng + k): fp16 s, fp16 z
+ *                  [1024 + 64 ng, C) V params: group k of slot t at
+ *                        1024 + 64 ng + 4 (t ng + k)
+ *                (fp16 little-endian; g = channel / 4 in 0..31; group k
+ *                covers channels [k quant_group, (k + 1) quant_group).)
  *                Slots of sink positions and of positions still in the recent
  *                window are never written or read.
  *   sink         bf16 [batch][n_kv_heads][n_sink][2][128]   (K' then V')
@@ -91,6 +98,11 @@ typedef struct kvq_dims {
   int32_t n_sink;      /* >= 0 bf16 sink tokens                             */
   int32_t n_recent;    /* >= 1 bf16 recent-window tokens (ring size)        */
   float sm_scale;      /* softmax scale; <= 0 selects 1/sqrt(head_dim)      */
+  int32_t quant_group; /* channels per INT2 (scale, zero) pair: 32, 64 or    */
+                       /* 128 (0 selects 128, one pair per vector)           */
+  int32_t hadamard_block; /* kvq_calibrate: size of the diagonal Hadamard   */
+                       /* blocks, 32, 64 or 128 (0 selects 128, the full    */
+                       /* transform); the online calls take R as given      */
 } kvq_dims;
 
 /* Per-layer calibration products (device pointers for the online calls). */

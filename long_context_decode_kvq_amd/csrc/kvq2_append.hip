@@ -67,8 +67,9 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
         const float r0 = bf16_bits_to_float(src[lane]);
         const float r1 = bf16_bits_to_float(src[lane + 64]);
         const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
-                                         a.page_size, b, h, pold);
-        if (off >= 0) quantize_store(a.pool + off, pold % kChunkTokens, kind, r0, r1, clip, lane);
+                                         a.page_size, b, h, pold, a.chunk_bytes);
+        if (off >= 0)
+          quantize_store(a.pool + off, pold % kChunkTokens, kind, r0, r1, clip, lane, a.ng);
       }
     }
 
@@ -94,10 +95,10 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
       dst[lane + 64] = static_cast<uint16_t>(rb1);
     } else if (!to_ring) {
       const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
-                                       a.page_size, b, h, pos);
+                                       a.page_size, b, h, pos, a.chunk_bytes);
       if (off >= 0)
         quantize_store(a.pool + off, pos % kChunkTokens, kind, bf16_bits_to_float(rb0),
-                       bf16_bits_to_float(rb1), clip, lane);
+                       bf16_bits_to_float(rb1), clip, lane, a.ng);
     } else {
       uint16_t* dst = a.recent + (seq_head * W + (pos - ns) % W) * 2 * kHeadDim + kind * kHeadDim;
       dst[lane] = static_cast<uint16_t>(rb0);

@@ -27,30 +27,51 @@ struct AppendArgs {
   int total_new;
   int tokens_per_block;        // multiple of kWaves
   const uint16_t* x_new[2];
+  int ng;                      // (scale, zero) pairs per vector: 1, 2 or 4
+  int chunk_bytes;             // 1024 + 128 ng
 };
 
-// Quantize one rotated vector (channels lane and lane + 64) and store its
-// packed codes and fp16 (scale, zero) in slot t of the chunk at `chunk`.
-// Pinned fp32 steps, each rounded separately (no contraction).
-__device__ void quantize_store(uint8_t* chunk, int t, int kind, float r0, float r1, float clip,
-                               int lane) {
-  const float x0 = fminf(fmaxf(r0, -clip), clip) + 0.0f;   // + 0 turns -0 into +0
-  const float x1 = fminf(fmaxf(r1, -clip), clip) + 0.0f;
-  const float mn = wave_min(fminf(x0, x1));
-  const float mx = wave_max(fmaxf(x0, x1));
+// The pinned quantizer of one value of a group with range [mn, mx]: fp16
+// (scale, zero) bits and the code, each fp32 step rounded separately.
+struct Quant {
+  uint32_t s_bits, z_bits, code;
+};
+__device__ __forceinline__ Quant quantize_value(float x, float mn, float mx) {
+  Quant q;
   const float s = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
-  const uint32_t s_bits = float_to_f16_bits(s);
-  const uint32_t z_bits = float_to_f16_bits(mn);
-  const float sf = f16_bits_to_float(s_bits);
-  const float zf = f16_bits_to_float(z_bits);
-  uint32_t c0 = 0, c1 = 0;
+  q.s_bits = float_to_f16_bits(s);
+  q.z_bits = float_to_f16_bits(mn);
+  const float sf = f16_bits_to_float(q.s_bits);
+  const float zf = f16_bits_to_float(q.z_bits);
+  q.code = 0;
   if (sf != 0.0f) {
     const float inv = __fdiv_rn(1.0f, sf);
-    const float t0 = __fmul_rn(__fsub_rn(x0, zf), inv);
-    const float t1 = __fmul_rn(__fsub_rn(x1, zf), inv);
-    c0 = static_cast<uint32_t>(fminf(fmaxf(rintf(t0), 0.0f), 3.0f));
-    c1 = static_cast<uint32_t>(fminf(fmaxf(rintf(t1), 0.0f), 3.0f));
+    const float tt = __fmul_rn(__fsub_rn(x, zf), inv);
+    q.code = static_cast<uint32_t>(fminf(fmaxf(rintf(tt), 0.0f), 3.0f));
   }
+  return q;
+}
+
+// Quantize one rotated vector (channels lane and lane + 64) and store its
+// packed codes and fp16 (scale, zero) pairs in slot t of the chunk at
+// `chunk`: one pair for the vector (ng = 1), one per half of it (ng = 2:
+// channel lane is in group 0, lane + 64 in group 1) or per quarter (ng = 4:
+// groups lane / 32 and 2 + lane / 32).  Pinned fp32 steps, each rounded
+// separately (no contraction).
+__device__ void quantize_store(uint8_t* chunk, int t, int kind, float r0, float r1, float clip,
+                               int lane, int ng) {
+  const float x0 = fminf(fmaxf(r0, -clip), clip) + 0.0f;   // + 0 turns -0 into +0
+  const float x1 = fminf(fmaxf(r1, -clip), clip) + 0.0f;
+  const bool halves = ng == 4;
+  float mn0 = group_min(x0, halves), mx0 = group_max(x0, halves);
+  float mn1 = group_min(x1, halves), mx1 = group_max(x1, halves);
+  if (ng == 1) {
+    mn0 = mn1 = fminf(mn0, mn1);
+    mx0 = mx1 = fmaxf(mx0, mx1);
+  }
+  const Quant q0 = quantize_value(x0, mn0, mx0);
+  const Quant q1 = quantize_value(x1, mn1, mx1);
+  const uint32_t c0 = q0.code, c1 = q1.code;
   // Four consecutive channels form a byte: channel 4g + k at bits 2k.
   uint32_t b0 = c0 << (2 * (lane & 3));
   uint32_t b1 = c1 << (2 * (lane & 3));
@@ -69,9 +90,16 @@ __device__ void quantize_store(uint8_t* chunk, int t, int kind, float r0, float 
       chunk[base + 4] = static_cast<uint8_t>(b1);
     }
   }
-  if (lane == 0) {
-    const int off = (kind == 0 ? kKParamsOff : kVParamsOff) + 4 * t;
-    *reinterpret_cast<uint32_t*>(chunk + off) = s_bits | (z_bits << 16);
+  // (scale, zero) pairs: lane 0 stores its groups (and lane 32 the second
+  // half's with quarters)
+  if (lane == 0 || (halves && lane == 32)) {
+    const int k0 = ng == 4 ? lane / 32 : 0;                 // group of channel lane
+    const int k1 = ng == 4 ? 2 + lane / 32 : ng - 1;        // group of channel lane + 64
+    *reinterpret_cast<uint32_t*>(chunk + param_offset(kind, t, ng, k0)) =
+        q0.s_bits | (q0.z_bits << 16);
+    if (ng > 1)
+      *reinterpret_cast<uint32_t*>(chunk + param_offset(kind, t, ng, k1)) =
+          q1.s_bits | (q1.z_bits << 16);
   }
 }
 
@@ -139,12 +167,12 @@ __device__ __forceinline__ void append_step_block(const AppendArgs& a, int bx, i
     e0 = bf16_bits_to_float(src[lane]);
     e1 = bf16_bits_to_float(src[lane + 64]);
     evict_off = chunk_offset_uniform(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
-                                     a.page_size, b, h, pold);
+                                     a.page_size, b, h, pold, a.chunk_bytes);
   }
   int64_t int2_off = -1;
   if (ok && pos >= ns && !to_ring)
     int2_off = chunk_offset_uniform(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
-                                    a.page_size, b, h, pos);
+                                    a.page_size, b, h, pos, a.chunk_bytes);
   {
     float4* dst = reinterpret_cast<float4*>(Rs);
 #pragma unroll
@@ -155,7 +183,8 @@ __device__ __forceinline__ void append_step_block(const AppendArgs& a, int bx, i
   __syncthreads();
   if (!ok) return;
   const float clip = a.clip[kind];
-  if (evict_off >= 0) quantize_store(a.pool + evict_off, pold % kChunkTokens, kind, e0, e1, clip, lane);
+  if (evict_off >= 0)
+    quantize_store(a.pool + evict_off, pold % kChunkTokens, kind, e0, e1, clip, lane, a.ng);
 
   // Pinned rotation of the new vector.
   double acc0 = 0.0, acc1 = 0.0;
@@ -175,7 +204,7 @@ __device__ __forceinline__ void append_step_block(const AppendArgs& a, int bx, i
   } else if (!to_ring) {
     if (int2_off >= 0)
       quantize_store(a.pool + int2_off, pos % kChunkTokens, kind, bf16_bits_to_float(rb0),
-                     bf16_bits_to_float(rb1), clip, lane);
+                     bf16_bits_to_float(rb1), clip, lane, a.ng);
   } else {
     uint16_t* dst = a.recent + (seq_head * W + (pos - ns) % W) * 2 * kHeadDim + kind * kHeadDim;
     dst[lane] = static_cast<uint16_t>(rb0);
@@ -209,6 +238,8 @@ inline AppendArgs make_append_args(const kvq_dims& d, const kvq_layer& layer, co
   a.total_new = total_new;
   a.x_new[0] = k_new;
   a.x_new[1] = v_new;
+  a.ng = kHeadDim / (d.quant_group > 0 ? d.quant_group : kHeadDim);
+  a.chunk_bytes = chunk_bytes_for(a.ng);
   // Decode-step appends (a few tokens per sequence): one token per wave, for
   // parallelism; medium ones 16 per work-group; bulk appends 256, so that
   // each work-group stages R once per 256 vectors.

@@ -91,7 +91,9 @@ bool jacobi_eigh(std::vector<double>& A, std::vector<double>& V) {
 // Eigenbasis with descending eigenvalues and the sign rule, then
 // R = U . H . P (fp64) rounded to fp32.  H[i][j] = (-1)^popcount(i&j)/sqrt(D);
 // (A P)[i][j] = A[i][bitrev(j)].
-bool rotation_from_covariance(std::vector<double> C, float* R_out) {
+// R = U H P with H the Sylvester Hadamard of size `hb` on each diagonal
+// block of hb channels (hb = 128: the full transform), scaled by 1/sqrt(hb).
+bool rotation_from_covariance(std::vector<double> C, float* R_out, int hb) {
   std::vector<double> V;
   if (!jacobi_eigh(C, V)) return false;
   std::vector<int> order(D);
@@ -110,13 +112,15 @@ bool rotation_from_covariance(std::vector<double> C, float* R_out) {
     const double sign = V[arg * D + src] < 0 ? -1.0 : 1.0;
     for (int k = 0; k < D; ++k) U[k * D + c] = sign * V[k * D + src];
   }
-  const double inv_sqrt = 1.0 / std::sqrt(double(D));
+  const double inv_sqrt = 1.0 / std::sqrt(double(hb));
   for (int i = 0; i < D; ++i) {
     for (int j = 0; j < D; ++j) {
-      const int jb = bit_reverse7(j);
+      const int jb = bit_reverse7(j);   // column j of H P is column jb of H
+      const int blk = jb / hb;
       double acc = 0.0;
-      for (int k = 0; k < D; ++k)
-        acc += U[i * D + k] * ((__builtin_popcount(k & jb) & 1) ? -inv_sqrt : inv_sqrt);
+      for (int k = blk * hb; k < (blk + 1) * hb; ++k)
+        acc += U[i * D + k] *
+               ((__builtin_popcount((k % hb) & (jb % hb)) & 1) ? -inv_sqrt : inv_sqrt);
       R_out[i * D + j] = float(acc);
     }
   }
@@ -146,6 +150,8 @@ extern "C" int kvq_calibrate(const kvq_dims* dims, int32_t n_tokens, const uint1
     return KVQ_ERR_ARG;
   if (dims->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
   const int Hq = dims->n_q_heads, Hkv = dims->n_kv_heads;
+  const int hb = dims->hadamard_block > 0 ? dims->hadamard_block : D;
+  if (hb != 32 && hb != 64 && hb != 128) return KVQ_ERR_UNSUPPORTED;
   if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0 || n_tokens < 1) return KVQ_ERR_ARG;
   if (!(clip_quantile > 0.0) || !(clip_quantile <= 1.0)) return KVQ_ERR_ARG;
   const int G = Hq / Hkv;
@@ -208,8 +214,8 @@ extern "C" int kvq_calibrate(const kvq_dims* dims, int32_t n_tokens, const uint1
       CQ[i] *= inv;
       CS[i] *= inv;
     }
-    ok[h] = rotation_from_covariance(CQ, R_K + size_t(h) * D * D) &&
-            rotation_from_covariance(CS, R_V + size_t(h) * D * D);
+    ok[h] = rotation_from_covariance(CQ, R_K + size_t(h) * D * D, hb) &&
+            rotation_from_covariance(CS, R_V + size_t(h) * D * D, hb);
   };
   {
     const int n_threads = std::max(1, std::min(Hkv, 16));

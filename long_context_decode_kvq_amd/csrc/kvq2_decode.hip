@@ -373,7 +373,9 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
   a.sigma_v = std::ldexp(1.0f, a.log2_sigma_v);
   const int cpp = d.page_size / kChunkTokens;
   a.log2_cpp = cpp == 1 ? 0 : cpp == 2 ? 1 : 2;
-  a.page_bytes = int64_t(d.n_kv_heads) * cpp * kChunkBytes;
+  a.ng = d.quant_group == 0 ? 1 : kHeadDim / d.quant_group;
+  a.chunk_bytes = chunk_bytes_for(a.ng);
+  a.page_bytes = int64_t(d.n_kv_heads) * cpp * a.chunk_bytes;
   a.seq_len = seq_len;
   a.q = q;
   a.out = out;
@@ -393,7 +395,8 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
   a.partials = reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes +
                                         plan.prefix_bytes);
   const int G = a.group;
-  a.gp = (which == kDecodeValu || G > 8) ? 0 : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
+  // the matrix-core kernel reads one (s, z) pair per vector: groups of 128
+  a.gp = (which == kDecodeValu || G > 8 || a.ng != 1) ? 0 : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
   a.n_split_int2 = plan.n_split_int2;
   a.n_split = plan.n_split;
   a.piece_cost = plan.piece_cost;

@@ -39,7 +39,9 @@ struct DecodeArgs {
   float sigma_v;               // power of two with sigma_v * s_V <= 1 for every V scale
   int log2_sigma_v;            // log2(sigma_v)
   int log2_cpp;                // log2(page_size / 16)
-  int64_t page_bytes;          // bytes of one physical page: Hkv * page_size / 16 * 1152
+  int ng;                      // (scale, zero) pairs per vector: quantization groups of 128 / ng
+  int chunk_bytes;             // bytes of one 16-token chunk: 1024 + 128 ng
+  int64_t page_bytes;          // bytes of one physical page: Hkv * page_size / 16 * chunk_bytes
   const int32_t* seq_len;
   const uint16_t* q;
   float* out;
@@ -229,8 +231,8 @@ __device__ __forceinline__ global_u8* read_lane_ptr(const uint8_t* p, int lane) 
 template <int GP>
 __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& tl,
                            const Int2Range& rg, int tile, const float (*qs)[kHeadDim],
-                           const float* qsum, float (*pb)[GP], float* m, float* l, float* acc0,
-                           float* acc1) {
+                           const float* qsum, const float (*qsum4)[4], float (*pb)[GP], float* m,
+                           float* l, float* acc0, float* acc1) {
   const int nt = min(16, tl.n_all - tile * 16);
   if (nt <= 0) return;
   const int G = a.group;
@@ -243,7 +245,7 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
     pos = token_position(a, tl, tile * 16 + t);
     if (pos >= a.n_sink && pos < rg.int2_end) {
       const int64_t off = chunk_offset(a.block_table, a.bt_stride, a.num_pages, a.n_kv_heads,
-                                       a.page_size, b, h, pos);
+                                       a.page_size, b, h, pos, a.chunk_bytes);
       kind = 2;
       ts = pos % kChunkTokens;
       base = a.pool + (off < 0 ? 0 : off);   // an invalid page entry reads chunk 0 (memory-safe)
@@ -274,16 +276,18 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
   }
   u32x2 kc = *reinterpret_cast<global_u2*>(kind == 2 ? gbase + kKCodesOff + 32 * ts + 8 * qq
                                                            : gpool);
-  uint32_t kpar = *reinterpret_cast<global_u32*>(kind == 2 ? gbase + kKParamsOff + 4 * ts
-                                                                  : gpool);
+  // (s_K, z_K) of the quantization group of this lane's 32 key channels
+  const int ng = a.ng;
+  uint32_t kpar = *reinterpret_cast<global_u32*>(
+      kind == 2 ? gbase + param_offset(0, ts, ng, (qq * ng) >> 2) : gpool);
   // Values: one dword per lane and token (bf16: channels 2 lane, 2 lane + 1
   // of the value row; INT2: the dword holding this lane's code byte), and
-  // for INT2 tokens the (s_V, z_V) pair, the same for every lane, through the
-  // scalar cache.
+  // for INT2 tokens the (s_V, z_V) pair of the lane's value group: with one
+  // group the same for every lane, through the scalar cache.
   typedef const uint32_t __attribute__((address_space(4))) const_u32;
   uint32_t vword[16], vpar[16];
   int vkind[16];
-  const int cg = lane >> 1;
+  const int cg = lane >> 1, vgrp = (lane * ng) >> 6;
 #pragma unroll
   for (int tt = 0; tt < 16; ++tt) {
     vkind[tt] = __builtin_amdgcn_readlane(kind, 4 * tt);
@@ -292,9 +296,14 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
     const int boff = kVCodesOff + 32 * (cg & 15) + 8 * (s >> 2) + 4 * (cg >> 4);   // + (s & 3)
     const int woff = vkind[tt] == 1 ? 2 * kHeadDim + 4 * lane : boff;
     vword[tt] = *reinterpret_cast<global_u32*>(bp + woff);
-    const uint8_t* pp = vkind[tt] == 2 ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(bp)) + kVParamsOff + 4 * s
-                                       : a.pool;
-    vpar[tt] = *reinterpret_cast<const_u32*>(reinterpret_cast<uintptr_t>(pp));
+    if (ng == 1) {
+      const uint8_t* pp = vkind[tt] == 2 ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(bp)) + kVParamsOff + 4 * s
+                                         : a.pool;
+      vpar[tt] = *reinterpret_cast<const_u32*>(reinterpret_cast<uintptr_t>(pp));
+    } else {
+      vpar[tt] = *reinterpret_cast<global_u32*>(
+          vkind[tt] == 2 ? bp + param_offset(1, s, ng, vgrp) : gpool);
+    }
   }
   // Empty asm statements take the loaded values here: the compiler would
   // otherwise sink each load into the branch that uses it, one wait per load.
@@ -339,6 +348,9 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
     float d = dot[g];
+    // with several key groups each lane scales its own 32 channels (the
+    // logit is the quad sum of s_K (q'.c) + z_K sum(q') over the groups)
+    if (ng > 1 && kind == 2 && g < G) d = fmaf(ksc, d, kzr * qsum4[g][qq]);
     d += dpp_move<kQuadXor1>(d);
     d += dpp_move<kQuadXor2>(d);
     // row g's query sits at position L - query_count + query_base + g /
@@ -346,7 +358,8 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
     // n_recent only recent-window tokens can lie beyond it; for decode every
     // position is visible)
     const bool seen = pos <= tl.L - a.query_count + a.query_base + g / a.head_group;
-    lg[g] = (kind != 0 && g < G && seen) ? fmaf(ksc, d, kzr * qsum[g]) : -INFINITY;
+    const float logit = (kind == 2 && ng == 1) ? fmaf(ksc, d, kzr * qsum[g]) : d;
+    lg[g] = (kind != 0 && g < G && seen) ? logit : -INFINITY;
   }
   float corr[GP];
   softmax_tile16<GP>(G, qq, lg, corr, m, l);

@@ -743,7 +743,8 @@ __device__ void token_slice_item(const DecodeArgs& a, int idx) {
   float m[GP], l[GP], acc0[GP], acc1[GP];
 #pragma unroll
   for (int g = 0; g < GP; ++g) { m[g] = -INFINITY; l[g] = 0.f; acc0[g] = 0.f; acc1[g] = 0.f; }
-  token_tile<GP>(a, b, h, tl, rg, 4 * z + wave, qs, qsum, pbuf[wave], m, l, acc0, acc1);
+  token_tile<GP>(a, b, h, tl, rg, 4 * z + wave, qs, qsum, nullptr, pbuf[wave], m, l, acc0,
+             acc1);
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
     if (g < G) {

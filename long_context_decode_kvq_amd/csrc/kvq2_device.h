@@ -115,11 +115,40 @@ __device__ __forceinline__ int fetch_add_acq_rel_agent(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Byte offset of the 1152-byte chunk holding position `pos` of sequence b,
-// KV head h; -1 if the block-table entry is outside [0, num_pages).
+// Min / max over the lanes of one quantization group: the whole wave, or
+// (halves) each half of it (lanes 0-31 and 32-63).  All 64 lanes active.
+__device__ __forceinline__ float group_min(float v, bool halves) {
+  v = fminf(v, dpp_move<kQuadXor1>(v));
+  v = fminf(v, dpp_move<kQuadXor2>(v));
+  v = fminf(v, dpp_move<kRowHalfMirror>(v));
+  v = fminf(v, dpp_move<kRowMirror>(v));
+  const float lo = fminf(read_lane(v, 0), read_lane(v, 16));
+  const float hi = fminf(read_lane(v, 32), read_lane(v, 48));
+  return halves ? ((threadIdx.x & 32) ? hi : lo) : fminf(lo, hi);
+}
+
+__device__ __forceinline__ float group_max(float v, bool halves) {
+  v = fmaxf(v, dpp_move<kQuadXor1>(v));
+  v = fmaxf(v, dpp_move<kQuadXor2>(v));
+  v = fmaxf(v, dpp_move<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_move<kRowMirror>(v));
+  const float lo = fmaxf(read_lane(v, 0), read_lane(v, 16));
+  const float hi = fmaxf(read_lane(v, 32), read_lane(v, 48));
+  return halves ? ((threadIdx.x & 32) ? hi : lo) : fmaxf(lo, hi);
+}
+
+// Byte offset of (scale, zero) of quantization group k of slot t in a chunk
+// with ng groups per vector (kind 0 = K, 1 = V).
+__device__ __forceinline__ int param_offset(int kind, int t, int ng, int k) {
+  return 1024 + kind * 64 * ng + 4 * (t * ng + k);
+}
+
+// Byte offset of the chunk (chunk_bytes long) holding position `pos` of
+// sequence b, KV head h; -1 if the block-table entry is outside
+// [0, num_pages).
 __device__ __forceinline__ int64_t chunk_offset(const int32_t* block_table, int32_t bt_stride,
                                                 int64_t num_pages, int n_kv_heads, int page_size,
-                                                int b, int h, int pos) {
+                                                int b, int h, int pos, int chunk_bytes) {
   if (pos < 0) return -1;
   const int lp = pos / page_size;
   if (lp >= bt_stride) return -1;
@@ -127,7 +156,7 @@ __device__ __forceinline__ int64_t chunk_offset(const int32_t* block_table, int3
   if (page < 0 || page >= num_pages) return -1;
   const int cpp = page_size / kChunkTokens;
   return ((int64_t(page) * n_kv_heads + h) * cpp + (pos % page_size) / kChunkTokens) *
-         int64_t(kChunkBytes);
+         int64_t(chunk_bytes);
 }
 
 // Same, for a wave-uniform position: the block-table entry is read through the
@@ -135,7 +164,7 @@ __device__ __forceinline__ int64_t chunk_offset(const int32_t* block_table, int3
 __device__ __forceinline__ int64_t chunk_offset_uniform(const int32_t* block_table,
                                                         int32_t bt_stride, int64_t num_pages,
                                                         int n_kv_heads, int page_size, int b,
-                                                        int h, int pos) {
+                                                        int h, int pos, int chunk_bytes) {
   pos = __builtin_amdgcn_readfirstlane(pos);
   if (pos < 0) return -1;
   const int lp = pos / page_size;
@@ -145,7 +174,7 @@ __device__ __forceinline__ int64_t chunk_offset_uniform(const int32_t* block_tab
   if (page < 0 || page >= num_pages) return -1;
   const int cpp = page_size / kChunkTokens;
   return ((int64_t(page) * n_kv_heads + h) * cpp + (pos % page_size) / kChunkTokens) *
-         int64_t(kChunkBytes);
+         int64_t(chunk_bytes);
 }
 
 }  // namespace kvq

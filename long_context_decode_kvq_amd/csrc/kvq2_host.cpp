@@ -28,6 +28,12 @@ int check_dims(const kvq_dims* d) {
   if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64) return KVQ_ERR_UNSUPPORTED;
   if (d->n_sink < 0 || d->n_recent < 1) return KVQ_ERR_ARG;
   if (!std::isfinite(d->sm_scale)) return KVQ_ERR_ARG;
+  if (d->quant_group != 0 && d->quant_group != 32 && d->quant_group != 64 &&
+      d->quant_group != kHeadDim)
+    return KVQ_ERR_UNSUPPORTED;
+  if (d->hadamard_block != 0 && d->hadamard_block != 32 && d->hadamard_block != 64 &&
+      d->hadamard_block != kHeadDim)
+    return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -108,11 +114,14 @@ const DecodeTuning& decode_tuning() {
   return t;
 }
 
-DecodeKernel selected_decode_kernel() {
+DecodeKernel selected_decode_kernel(const kvq_dims& d) {
   // KVQ_DECODE_KERNEL=valu selects the plain VALU kernel (kept as the
-  // measured comparison point for the MFMA kernel); default is MFMA.
+  // measured comparison point for the MFMA kernel); default is MFMA.  The
+  // MFMA kernel reads one (s, z) pair per vector, so quantization groups
+  // narrower than 128 channels always take the VALU kernel.
   const char* s = std::getenv("KVQ_DECODE_KERNEL");
   if (s != nullptr && std::strcmp(s, "valu") == 0) return kDecodeValu;
+  if (d.quant_group != 0 && d.quant_group != kHeadDim) return kDecodeValu;
   return kDecodeMfma;
 }
 
@@ -142,7 +151,7 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
   // The MFMA decode deals the token-by-token list out over its INT2 items;
   // the VALU decode (also used for G > 8) gives it a work-group of its own.
   const int G = (d.n_q_heads / d.n_kv_heads) * n_query;   // rows per (b, h)
-  const bool own_token_item = selected_decode_kernel() == kDecodeValu || G > 8;
+  const bool own_token_item = selected_decode_kernel(d) == kDecodeValu || G > 8;
   p.n_split = p.n_split_int2 + (own_token_item ? 1 : 0);
   // arrival tickets [B * Hkv] of the VALU decode's last-arrival combine
   p.ticket_bytes = ((size_t(heads) * sizeof(int32_t) + 255) / 256) * 256;
@@ -220,7 +229,7 @@ int check_decode_args(const kvq_dims* dims, const kvq_layer* layer, const kvq_ca
       (int64_t(1) << 31))
     return KVQ_ERR_UNSUPPORTED;
   *plan = make_decode_plan(*dims, batch, max_seq_len,
-                           multi_query_pass(*dims, n_query, selected_decode_kernel()));
+                           multi_query_pass(*dims, n_query, selected_decode_kernel(*dims)));
   return KVQ_OK;
 }
 
@@ -287,14 +296,14 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq
                               workspace_bytes, &plan);
   if (rc != KVQ_OK) return rc;
   return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
-                                  max_seq_len, q, out, workspace, plan, selected_decode_kernel(),
+                                  max_seq_len, q, out, workspace, plan, selected_decode_kernel(*dims),
                                   stream));
 }
 
 size_t kvq_decode_multi_workspace_bytes(const kvq_dims* dims, int32_t batch,
                                         int32_t max_seq_len, int32_t n_query) {
   if (check_dims(dims) != KVQ_OK || batch < 1 || max_seq_len < 0 || n_query < 1) return 0;
-  const int pass = multi_query_pass(*dims, n_query, selected_decode_kernel());
+  const int pass = multi_query_pass(*dims, n_query, selected_decode_kernel(*dims));
   return make_decode_plan(*dims, batch, max_seq_len, pass).total_bytes;
 }
 
@@ -309,7 +318,7 @@ int kvq_decode_multi_attention(const kvq_dims* dims, const kvq_layer* layer,
   if (rc != KVQ_OK) return rc;
   // Passes of at most `pass` queries, each over all pages, in stream order
   // on the one workspace.
-  const DecodeKernel which = selected_decode_kernel();
+  const DecodeKernel which = selected_decode_kernel(*dims);
   const int pass = multi_query_pass(*dims, n_query, which);
   for (int m0 = 0; m0 < n_query; m0 += pass) {
     const int nq = std::min(pass, n_query - m0);
@@ -340,7 +349,7 @@ int kvq_decode_attention_noalloc(const kvq_dims* dims, const kvq_layer* layer,
   if ((rc = hip_status(static_scratch(&ws))) != KVQ_OK) return rc;
   // The arrival counters of the VALU decode must start at zero; the scratch
   // keeps whatever the previous call on this GPU left.
-  const DecodeKernel which = selected_decode_kernel();
+  const DecodeKernel which = selected_decode_kernel(*dims);
   if (which == kDecodeValu || dims->n_q_heads / dims->n_kv_heads > 8)
     if ((rc = hip_status(launch_zero_words(ws, plan.ticket_bytes, stream))) != KVQ_OK) return rc;
   return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
@@ -364,7 +373,7 @@ int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer, const kvq_cach
   const float scale = resolved_scale(dims);
   const int G = dims->n_q_heads / dims->n_kv_heads;
   if (!nothing && total_new <= kStepAppendMax && G <= 8 &&
-      selected_decode_kernel() == kDecodeMfma) {
+      selected_decode_kernel(*dims) == kDecodeMfma) {
     return hip_status(launch_decode_step(*dims, scale, *layer, *cache, batch, start_pos, cu_new,
                                          total_new, k_new, v_new, seq_len, max_seq_len, q, out,
                                          workspace, plan, stream));
@@ -376,7 +385,7 @@ int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer, const kvq_cach
     if (rc != KVQ_OK) return rc;
   }
   return hip_status(launch_decode(*dims, scale, *layer, *cache, batch, seq_len, max_seq_len, q,
-                                  out, workspace, plan, selected_decode_kernel(), stream));
+                                  out, workspace, plan, selected_decode_kernel(*dims), stream));
 }
 
 }  // extern "C"

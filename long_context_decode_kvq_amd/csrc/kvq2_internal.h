@@ -12,6 +12,10 @@ namespace kvq {
 constexpr int kHeadDim = 128;
 constexpr int kChunkTokens = 16;       // a page is a whole number of 16-token chunks
 constexpr int kChunkBytes = 1152;      // 512 K codes + 512 V codes + 64 + 64 params
+// With ng (scale, zero) pairs per vector (quantization groups of 128 / ng
+// channels) a chunk holds 1024 code bytes and 2 x 16 x ng x 4 param bytes:
+// K group k of slot t at 1024 + 4 (t ng + k), V at 1024 + 64 ng + 4 (t ng + k).
+constexpr int chunk_bytes_for(int ng) { return 1024 + 128 * ng; }
 constexpr int kKCodesOff = 0;
 constexpr int kVCodesOff = 512;
 constexpr int kKParamsOff = 1024;
@@ -79,7 +83,7 @@ const DecodeTuning& decode_tuning();
 
 // Kernel variants of the decode path.
 enum DecodeKernel { kDecodeMfma = 0, kDecodeValu = 1 };
-DecodeKernel selected_decode_kernel();
+DecodeKernel selected_decode_kernel(const kvq_dims& d);
 
 // Launchers (defined in the .hip sources).  They return a hipError_t value
 // (0 = success) so that the host validation code needs no HIP headers.

@@ -29,7 +29,8 @@ class KvqError(RuntimeError):
 class KvqDims(C.Structure):
     _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("page_size", C.c_int32), ("n_sink", C.c_int32), ("n_recent", C.c_int32),
-                ("sm_scale", C.c_float)]
+                ("sm_scale", C.c_float), ("quant_group", C.c_int32),
+                ("hadamard_block", C.c_int32)]
 
 
 class KvqLayer(C.Structure):
@@ -103,8 +104,15 @@ def _check(rc: int, what: str):
         raise KvqError(f"{what}: {status_string(rc)}" + (f" ({extra})" if extra else ""))
 
 
-def dims(n_q_heads, n_kv_heads, page_size, n_sink, n_recent, sm_scale=0.0, head_dim=HEAD_DIM):
-    return KvqDims(n_q_heads, n_kv_heads, head_dim, page_size, n_sink, n_recent, sm_scale)
+def dims(n_q_heads, n_kv_heads, page_size, n_sink, n_recent, sm_scale=0.0, head_dim=HEAD_DIM,
+         quant_group=0, hadamard_block=0):
+    return KvqDims(n_q_heads, n_kv_heads, head_dim, page_size, n_sink, n_recent, sm_scale,
+                   quant_group, hadamard_block)
+
+
+def chunk_bytes(quant_group: int = 0) -> int:
+    """Bytes of one 16-token chunk of the pool for this quantization group size."""
+    return 1024 + 128 * (HEAD_DIM // (quant_group or HEAD_DIM))
 
 
 def _ptr(t) -> int | None:
@@ -232,7 +240,7 @@ def probe_chunk_read(pool, chunk_off, sink, work_groups: int, stream=None):
 class DeviceCache:
     """Owns the torch device tensors of one layer's paged mixed-precision cache.
 
-    pool uint8 [num_pages][Hkv][P/16][1152]; sink / recent bf16 bit patterns
+    pool uint8 [num_pages][Hkv][P/16][chunk bytes]; sink / recent bf16 bit patterns
     (int16 tensors) [B][Hkv][n][2][128]; block_table int32 [B][stride].
     """
 
@@ -243,8 +251,8 @@ class DeviceCache:
         self.batch = batch
         self.num_pages = num_pages
         cpp = d.page_size // CHUNK_TOKENS
-        self.pool = torch.full((num_pages, d.n_kv_heads, cpp, CHUNK_BYTES), fill, dtype=torch.uint8,
-                               device=device)
+        self.pool = torch.full((num_pages, d.n_kv_heads, cpp, chunk_bytes(d.quant_group)), fill,
+                               dtype=torch.uint8, device=device)
         fill16 = np.int16(np.uint16(fill * 0x0101).view(np.int16))
         self.sink = torch.full((batch, d.n_kv_heads, max(d.n_sink, 1), 2, HEAD_DIM), int(fill16),
                                dtype=torch.int16, device=device)

@@ -48,20 +48,23 @@ def random_block_table(rng, lens, P, extra=3):
 class Scenario:
     """Same cache built by the oracle and on the GPU."""
 
-    def __init__(self, Hq, Hkv, P, ns, W, lens, seed=0, fill=0, k_scale=2.0, clip=None):
+    def __init__(self, Hq, Hkv, P, ns, W, lens, seed=0, fill=0, k_scale=2.0, clip=None,
+                 quant_group=128, hadamard_block=128):
         self.rng = np.random.default_rng(seed)
         self.seed = seed
         self.lens = list(lens)
         B = len(lens)
         self.B = B
-        self.od = O.Dims(Hq, Hkv, P, ns, W)
-        self.kd = kvq2.dims(Hq, Hkv, P, ns, W)
+        self.od = O.Dims(Hq, Hkv, P, ns, W, quant_group=quant_group)
+        self.kd = kvq2.dims(Hq, Hkv, P, ns, W, quant_group=quant_group,
+                            hadamard_block=hadamard_block)
         self.bt, self.num_pages = random_block_table(self.rng, lens, P)
         # rotations from the oracle's calibration on seeded tokens
         cq = normal_bits(seed * 7 + 1, (256, Hq, 128))
         ck = normal_bits(seed * 7 + 2, (256, Hkv, 128), np.float32(k_scale))
         cv = normal_bits(seed * 7 + 3, (256, Hkv, 128))
-        cal = O.calibrate(cq, ck, cv, Hq, Hkv, self.od.sm_scale, 0.999)
+        cal = O.calibrate(cq, ck, cv, Hq, Hkv, self.od.sm_scale, 0.999,
+                          hadamard_block=hadamard_block)
         self.R_K, self.R_V = cal.R_K, cal.R_V
         self.clip_K = cal.clip_K if clip is None else clip
         self.clip_V = cal.clip_V if clip is None else clip

@@ -85,6 +85,9 @@ def _step(d, lay, cch, batch=2, sp=FAKE, cu=FAKE, total=4, mx=2, k=FAKE, v=FAKE,
     (dict(clip_V=16385.0), ERR_ARG),
     (dict(clip_K=float("nan")), ERR_ARG),
     (dict(bt_stride=0), ERR_ARG),
+    (dict(quant_group=16), ERR_UNSUP),
+    (dict(quant_group=96), ERR_UNSUP),
+    (dict(hadamard_block=8), ERR_UNSUP),
 ])
 def test_validation_rejects_before_launch(over, rc):
     d, lay, cch = _args(**dict(over))
@@ -196,6 +199,34 @@ def test_calibrate_closed_form_wiring():
             assert np.abs(R_K[h] - fx.R_K[h]).max() <= 1e-6, f"R_K[{h}]"
             assert np.abs(R_V[h] - fx.R_V[h]).max() <= 1e-6, f"R_V[{h}]"
         assert (cK, cV) == (fx.clip_K, fx.clip_V)
+
+
+@pytest.mark.parametrize("hb", [32, 64])
+def test_calibrate_block_hadamard_matches_oracle(hb):
+    """kvq_calibrate with a block-diagonal Hadamard (dims.hadamard_block): the
+    closed-form fixture built for that block size, and the oracle's
+    calibration on the separated spectrum."""
+    from calib_fixture import ClosedFormCalibration
+    fx = ClosedFormCalibration(n_q_heads=4, n_kv_heads=2, seed=11, hadamard_block=hb)
+    d = kvq2.dims(4, 2, 16, 4, 128, quant_group=hb, hadamard_block=hb)
+    R_K, R_V, cK, cV = kvq2.calibrate(d, fx.q, fx.k, fx.v, 1.0)
+    for h in range(2):
+        assert np.abs(R_K[h] - fx.R_K[h]).max() <= 1e-6, f"R_K[{h}]"
+        assert np.abs(R_V[h] - fx.R_V[h]).max() <= 1e-6, f"R_V[{h}]"
+    assert (cK, cV) == (fx.clip_K, fx.clip_V)
+    q, k, v = _aniso_calibration()
+    R_K, R_V, cK, cV = kvq2.calibrate(d, q, k, v, 0.999)
+    cal = O.calibrate(q, k, v, 4, 2, 1 / math.sqrt(128), 0.999, hadamard_block=hb)
+    assert np.abs(R_K - cal.R_K).max() < 1e-4
+    assert np.abs(R_V - cal.R_V).max() < 5e-3
+
+
+def test_pool_layout_of_quantization_groups():
+    """Chunk sizes of the pool for groups of 128, 64 and 32 channels agree
+    between the binding and the oracle's layout."""
+    for g, nbytes in ((0, 1152), (128, 1152), (64, 1280), (32, 1536)):
+        assert kvq2.chunk_bytes(g) == nbytes
+        assert O.chunk_bytes(g or 128) == nbytes
 
 
 def test_calibrate_invariants_on_isotropic_data():
