@@ -47,21 +47,36 @@ def segment_counts(L, ns, W):
     return n_s, n_i, L - n_s - n_i
 
 
-def decode_bytes(w, lens, n_query=1):
+def int2_bytes(ng=1):
+    """Bytes of one INT2 (token, KV head): 2 x 32 code bytes and 2 x ng
+    fp16 (scale, zero) pairs (quantization groups of 128 / ng channels)."""
+    return 64 + 8 * ng
+
+
+def decode_bytes(w, lens, n_query=1, ng=1):
     """Algorithmic HBM bytes of one decode launch (what the method must move);
     with n_query queries per sequence the cache is read once for all of them."""
     tot = 0
     for L in lens:
         _, n_i, _ = segment_counts(int(L), w.n_sink, w.n_recent)
         n_b = int(L) - n_i
-        tot += w.n_kv_heads * (INT2_BYTES * n_i + BF16_BYTES * n_b)
+        tot += w.n_kv_heads * (int2_bytes(ng) * n_i + BF16_BYTES * n_b)
         tot += 4 * math.ceil(int(L) / w.page_size)                  # block-table entries
     tot += w.batch * n_query * w.n_q_heads * HEAD_DIM * (2 + 4)     # q bf16 in, out fp32
     tot += 2 * w.n_kv_heads * HEAD_DIM * HEAD_DIM * 4               # R_K, R_V
     return tot
 
 
-def append_bytes(w, lens_before, n_new=1):
+def shared_prefix_repeat_bytes(w, sharers, ng=1):
+    """INT2 bytes of the shared prefix pages that every sharer after the
+    first reads again (the unique bytes of a decode are decode_bytes minus
+    these)."""
+    if not w.shared_prefix or len(sharers) < 2:
+        return 0
+    return (len(sharers) - 1) * w.n_kv_heads * int2_bytes(ng) * (w.shared_prefix - w.n_sink)
+
+
+def append_bytes(w, lens_before, n_new=1, ng=1):
     """Algorithmic HBM bytes of one quantize-append launch of n_new tokens
     per sequence."""
     per_vec = 256 + 256                                             # new bf16 in, ring write
@@ -70,18 +85,19 @@ def append_bytes(w, lens_before, n_new=1):
         for j in range(n_new):
             L = int(L0) + j
             evict = L - w.n_recent >= w.n_sink and L >= w.n_sink
-            tot += w.n_kv_heads * 2 * (per_vec + ((256 + 36) if evict else 0))
+            tot += w.n_kv_heads * 2 * (per_vec + ((256 + 32 + 4 * ng) if evict else 0))
     tot += 2 * w.n_kv_heads * HEAD_DIM * HEAD_DIM * 4               # R_K, R_V
     return tot
 
 
-def build_cache(w, kvq2, W, lens_before, n_steps, device):
+def build_cache(w, kvq2, W, lens_before, n_steps, device, quant_group=0):
     """Calibrate, allocate and fill the cache to `lens_before` tokens per sequence."""
     import numpy as np
     import torch
 
     t0 = time.time()
-    kd = kvq2.dims(w.n_q_heads, w.n_kv_heads, w.page_size, w.n_sink, w.n_recent)
+    kd = kvq2.dims(w.n_q_heads, w.n_kv_heads, w.page_size, w.n_sink, w.n_recent,
+                   quant_group=quant_group, hadamard_block=quant_group)
     q_c, k_c, v_c = W.calibration_tokens(w)
     R_K, R_V, clip_K, clip_V = kvq2.calibrate(kd, q_c, k_c, v_c, 0.999)
     log(f"[bench] calibrated on {q_c.shape[0]} tokens in {time.time() - t0:.1f}s "
@@ -320,6 +336,9 @@ def main():
     ap.add_argument("--n-query", type=int, default=1,
                     help="queries per sequence and step: M > 1 times multi-query attention "
                          "(kvq_quantize_append of M tokens + kvq_decode_multi_attention)")
+    ap.add_argument("--quant-group", type=int, default=0, choices=(0, 32, 64, 128),
+                    help="channels per (scale, zero) pair (0 = 128); narrower groups also "
+                         "use a Hadamard of the same block size and run on the VALU decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the read-ceiling probes")
     ap.add_argument("--no-graph", action="store_true",
@@ -344,7 +363,8 @@ def main():
     # the oracle's worker processes are forked before this process touches the GPU
     # (the oracle leg times the one-query decode step; multi-query lines go without it)
     pool = None
-    if not args.no_cpu_baseline and not args.copy_probe and args.n_query == 1:
+    if (not args.no_cpu_baseline and not args.copy_probe and args.n_query == 1
+            and args.quant_group in (0, 128)):
         pool = OraclePool()
 
     import numpy as np
@@ -362,7 +382,9 @@ def main():
     n_steps = args.warmup + args.steps
     M = args.n_query
     lens_before = w.seq_lens() - M               # the first step appends tokens L-M .. L-1
-    kd, dc, lay, keep = build_cache(w, kvq2, W, lens_before, n_steps * M, device)
+    qg = args.quant_group
+    ng = HEAD_DIM // (qg or HEAD_DIM)
+    kd, dc, lay, keep = build_cache(w, kvq2, W, lens_before, n_steps * M, device, qg)
 
     # Small caches would be served from the 256 MB Infinity Cache: rotate
     # independent pool copies so every step reads its pages from HBM.
@@ -487,10 +509,15 @@ def main():
     step_bytes = []
     for i in range(args.steps):
         lb = lens_before + (args.warmup + i) * M
-        step_bytes.append(decode_bytes(w, lb + M, M) + append_bytes(w, lb, M))
+        step_bytes.append(decode_bytes(w, lb + M, M, ng) + append_bytes(w, lb, M, ng))
     value = float(np.sum(step_bytes)) / (ms_per_step * 1e-3 * args.steps) / 1e9
-    dec_bytes = decode_bytes(w, lens_before + (last + 1) * M, M)
+    dec_bytes = decode_bytes(w, lens_before + (last + 1) * M, M, ng)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    # A shared prefix is read by every sharer (its pages are then mostly
+    # served from the Infinity Cache): achieved counts the bytes every
+    # sequence reads, unique counts each physical page once.
+    _, _, sharers = W.page_assignment(w, lens_before + n_steps * M)
+    dec_unique = dec_bytes - shared_prefix_repeat_bytes(w, sharers, ng)
     log(f"[bench] pre-warm {n_pre} decode calls in {prewarm_wall:.2f}s; step "
         f"{ms_per_step * 1e3:.1f} us; decode {dec_avg_ms * 1e3:.1f} us (p10 {pct[10]:.1f}, "
         f"p50 {pct[50]:.1f}, p90 {pct[90]:.1f}); decode {achieved:.0f} GB/s = "
@@ -498,7 +525,8 @@ def main():
 
     ceiling = None
     if not args.no_probes:
-        ceiling = read_ceilings(w, kvq2, dc, pools, lens_before + (last + 1) * M, stream, achieved)
+        ceiling = read_ceilings(w, kvq2, dc, pools, lens_before + (last + 1) * M, stream, achieved,
+                                chunk_probe=(ng == 1))
 
     cpu = None
     if pool is not None:
@@ -508,7 +536,8 @@ def main():
         log(f"[bench] cpu baseline {cpu['value']:.4f} GB/s on {cpu['cores']} cores "
             f"({cpu['single_core_value']:.4f} GB/s on one) in {time.time() - t0:.1f}s")
 
-    kernel = os.environ.get("KVQ_DECODE_KERNEL", "mfma")
+    # narrower quantization groups always decode on the VALU kernel
+    kernel = os.environ.get("KVQ_DECODE_KERNEL", "mfma") if ng == 1 else "valu"
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -523,7 +552,7 @@ def main():
         # products on the f16 matrix cores (INT2 codes exact, q' and the
         # softmax weights as f16 hi + lo pairs), fp32 accumulation, softmax
         # and combine
-        "dtype": "f16/f32",
+        "dtype": "f16/f32" if kernel == "mfma" else "f32",
         "data": "synthetic",
         "config": {
             "workload": w.name,
@@ -535,6 +564,7 @@ def main():
             "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": HEAD_DIM,
             "page_size": w.page_size, "n_sink": w.n_sink, "n_recent": w.n_recent,
             "layers": 1, "decode_kernel": kernel, "pool_copies": copies,
+            "quant_group": qg or HEAD_DIM,
             "step_call": ("kvq_quantize_append + kvq_decode_multi_attention" if M > 1 else
                           "kvq_quantize_append + kvq_decode_attention" if args.two_calls
                           else "kvq_decode_step"),
@@ -546,6 +576,7 @@ def main():
             "decode_us_p50": round(pct[50], 2),
             "decode_us_p90": round(pct[90], 2),
             "step_pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "decode_bytes": int(dec_bytes),
         },
         "prewarm": {
             "seconds": round(prewarm_wall, 3),
@@ -563,16 +594,25 @@ def main():
             "traffic": measured_traffic(w.name),
         },
         "read_ceiling": ceiling,
+        "shared_prefix": None if not w.shared_prefix else {
+            "tokens": w.shared_prefix,
+            "sharers": len(sharers),
+            "decode_unique_bytes": int(dec_unique),
+            "decode_unique_gbs": round(dec_unique / (dec_avg_ms * 1e-3) / 1e9, 1),
+            "decode_effective_gbs": round(achieved, 1),
+            "note": "every sharer reads the shared prefix pages; unique counts each page once",
+        },
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
 
-def read_ceilings(w, kvq2, dc, pools, lens, stream, achieved, reps=5):
+def read_ceilings(w, kvq2, dc, pools, lens, stream, achieved, reps=5, chunk_probe=True):
     """What plain reads reach on this GPU (include/kvq2_probe.h): a 2 GiB
     sequential pass, and the decode's own 1152-byte INT2 chunks in the order
     it streams them (pool copies rotated as in the timed steps).  Median of
-    `reps` launches each, timed with HIP events on the launch stream."""
+    `reps` launches each, timed with HIP events on the launch stream.  The
+    chunk probe reads 1152-byte chunks (quantization groups of 128 only)."""
     import numpy as np
     import torch
 
@@ -586,7 +626,8 @@ def read_ceilings(w, kvq2, dc, pools, lens, stream, achieved, reps=5):
         kvq2.probe_stream_read(buf, sink, 8192, stream)
         a1.record(stream)
         t_stream.append((a0, a1))
-    offs_np = int2_chunk_offsets(w, dc.block_table.cpu().numpy(), lens)
+    offs_np = (int2_chunk_offsets(w, dc.block_table.cpu().numpy(), lens) if chunk_probe
+               else np.zeros(0, np.int64))
     t_chunk = []
     if offs_np.size:
         offs = torch.from_numpy(offs_np).to(dev)

@@ -1,0 +1,51 @@
+"""The bench's algorithmic byte counts against closed forms written out by
+hand from the cache layout (72 bytes per INT2 token and KV head with one
+(scale, zero) pair per vector, 512 per bf16 token), and against the oracle's
+chunk sizes for narrower quantization groups."""
+import math
+
+import numpy as np
+
+import bench
+import oracle as O
+from long_context_decode_kvq_amd import workloads as W
+
+
+def test_decode_bytes_of_28_sequences_at_100k():
+    w = W.WORKLOADS["conc_28x100k"]
+    n_int2 = 100000 - 256 - 4                     # sink 4, recent window 256
+    n_bf16 = 4 + 256
+    expect = (28 * 8 * (n_int2 * 72 + n_bf16 * 512)     # cache
+              + 28 * math.ceil(100000 / 16) * 4          # block-table entries
+              + 28 * 32 * 128 * (2 + 4)                  # q bf16 in, out fp32
+              + 2 * 8 * 128 * 128 * 4)                   # R_K, R_V
+    assert bench.decode_bytes(w, [100000] * 28) == expect
+    assert abs(expect / 1e6 - 1640.86) < 0.01
+
+
+def test_int2_bytes_follow_the_chunk_layout():
+    for g in (128, 64, 32):
+        ng = 128 // g
+        assert bench.int2_bytes(ng) * 16 == O.chunk_bytes(g)
+
+
+def test_shared_prefix_repeat_bytes():
+    w = W.WORKLOADS["qwen3_32b"]
+    lens = w.seq_lens()
+    _, _, sharers = W.page_assignment(w, lens)
+    assert len(sharers) >= 2
+    assert all(lens[b] > w.shared_prefix + w.n_recent for b in sharers)
+    # every sharer after the first reads the prefix's INT2 positions again
+    # (positions n_sink .. 16383; the sink itself is per sequence)
+    expect = (len(sharers) - 1) * 8 * 72 * (16384 - 4)
+    assert bench.shared_prefix_repeat_bytes(w, sharers) == expect
+    assert bench.shared_prefix_repeat_bytes(W.WORKLOADS["conc_28x100k"], []) == 0
+
+
+def test_append_bytes_of_one_token_step():
+    w = W.WORKLOADS["conc_28x100k"]
+    lens = np.full(28, 99999)
+    # per (sequence, KV head, K or V): new bf16 in + ring write, and the
+    # evicted token's ring read + 32 code bytes + one (scale, zero) pair
+    expect = 28 * 8 * 2 * (256 + 256 + 256 + 32 + 4) + 2 * 8 * 128 * 128 * 4
+    assert bench.append_bytes(w, lens) == expect
