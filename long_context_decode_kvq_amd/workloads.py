@@ -225,3 +225,16 @@ def decode_queries_device(w: Workload, step: int, device="cuda") -> torch.Tensor
     gen.manual_seed(9000 + 100 * w.index + step)
     q = torch.randn((w.batch, w.n_q_heads, HEAD_DIM), generator=gen, device=device)
     return q.to(torch.bfloat16).view(torch.int16).contiguous()
+
+
+# --------------------------------------------------------------------------
+# HQMQ inputs: the secondary codebook is S Haar-random unit quaternions per
+# (KV head, role), drawn without calibration; both the library and the CPU
+# oracle take them from here.
+# --------------------------------------------------------------------------
+
+def hqmq_secondary(seed: int, n_kv_heads: int, n_secondary: int) -> np.ndarray:
+    """fp32 [2][Hkv][S][4]: normalised standard-normal 4-vectors (uniform on
+    the 3-sphere), role 0 for K and 1 for V."""
+    g = np.random.default_rng(seed).standard_normal((2, n_kv_heads, n_secondary, 4))
+    return (g / np.linalg.norm(g, axis=-1, keepdims=True)).astype(np.float32)
