@@ -43,6 +43,24 @@ class KvqCache(C.Structure):
                 ("recent", C.c_void_p), ("block_table", C.c_void_p), ("bt_stride", C.c_int32)]
 
 
+class KvqHqmqDims(C.Structure):
+    _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("page_size", C.c_int32), ("n_secondary", C.c_int32), ("sm_scale", C.c_float)]
+
+
+class KvqHqmqLayer(C.Structure):
+    _fields_ = [("codebook_K", C.c_void_p), ("codebook_V", C.c_void_p)]
+
+
+class KvqHqmqCache(C.Structure):
+    _fields_ = [("pool", C.c_void_p), ("num_pages", C.c_int64), ("block_table", C.c_void_p),
+                ("bt_stride", C.c_int32)]
+
+
+HQMQ_EXPORTS = ("kvq_hqmq_codebook", "kvq_hqmq_append_workspace_bytes", "kvq_hqmq_append",
+                "kvq_hqmq_decode_workspace_bytes", "kvq_hqmq_decode_attention")
+HQMQ_TOKEN_BYTES = 192            # K and V records of one (position, KV head)
+
 EXPORTS = ("kvq_calibrate", "kvq_quantize_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_multi_workspace_bytes",
            "kvq_decode_multi_attention", "kvq_decode_attention_noalloc", "kvq_decode_step",
@@ -86,6 +104,17 @@ def lib():
         L.kvq_status_string.restype = C.c_char_p
         L.kvq_last_error.argtypes = []
         L.kvq_last_error.restype = C.c_char_p
+        HD, HL, HC = C.POINTER(KvqHqmqDims), C.POINTER(KvqHqmqLayer), C.POINTER(KvqHqmqCache)
+        L.kvq_hqmq_codebook.argtypes = [I32, P, P]
+        L.kvq_hqmq_codebook.restype = C.c_int
+        L.kvq_hqmq_append_workspace_bytes.argtypes = [HD, I32]
+        L.kvq_hqmq_append_workspace_bytes.restype = SZ
+        L.kvq_hqmq_append.argtypes = [HD, HL, HC, I32, P, P, I32, I32, P, P, P, SZ, P]
+        L.kvq_hqmq_append.restype = C.c_int
+        L.kvq_hqmq_decode_workspace_bytes.argtypes = [HD, I32, I32]
+        L.kvq_hqmq_decode_workspace_bytes.restype = SZ
+        L.kvq_hqmq_decode_attention.argtypes = [HD, HL, HC, I32, P, I32, P, P, P, SZ, P]
+        L.kvq_hqmq_decode_attention.restype = C.c_int
         L.kvq_probe_stream_read.argtypes = [P, SZ, P, I32, P]
         L.kvq_probe_stream_read.restype = C.c_int
         L.kvq_probe_chunk_read.argtypes = [P, P, I64, P, I32, P]
@@ -216,6 +245,73 @@ def decode_step(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, start_pos,
                                _ptr(seq_len), max_seq_len, _ptr(q), _ptr(out), _ptr(workspace),
                                nbytes, _stream_handle(stream))
     _check(rc, "kvq_decode_step")
+
+
+# ------------------------------------------------------------------ HQMQ codec (kvq2_hqmq.h)
+
+def hqmq_dims(n_q_heads, n_kv_heads, page_size, n_secondary, sm_scale=0.0,
+              head_dim=HEAD_DIM) -> KvqHqmqDims:
+    return KvqHqmqDims(n_q_heads, n_kv_heads, head_dim, page_size, n_secondary, sm_scale)
+
+
+def hqmq_codebook(secondary: np.ndarray) -> np.ndarray:
+    """kvq_hqmq_codebook on host fp32 [S][4] -> fp32 [24 S][4]."""
+    sec = np.ascontiguousarray(secondary, np.float32)
+    out = np.zeros((24 * sec.shape[0], 4), np.float32)
+    _check(lib().kvq_hqmq_codebook(sec.shape[0], _ptr(sec), _ptr(out)), "kvq_hqmq_codebook")
+    return out
+
+
+def hqmq_layer(codebook_K, codebook_V) -> KvqHqmqLayer:
+    """Device fp32 tensors [Hkv][24 S][4] (kept alive by the caller)."""
+    return KvqHqmqLayer(_ptr(codebook_K), _ptr(codebook_V))
+
+
+def hqmq_cache(pool, num_pages: int, block_table) -> KvqHqmqCache:
+    return KvqHqmqCache(_ptr(pool), num_pages, _ptr(block_table), int(block_table.shape[1]))
+
+
+def hqmq_append_workspace_bytes(d: KvqHqmqDims, total_new: int) -> int:
+    return int(lib().kvq_hqmq_append_workspace_bytes(C.byref(d), total_new))
+
+
+def hqmq_append(d: KvqHqmqDims, lay: KvqHqmqLayer, cch: KvqHqmqCache, batch: int, start_pos,
+                cu_new, total_new: int, max_new: int, k_new, v_new, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kvq_hqmq_append(C.byref(d), C.byref(lay), C.byref(cch), batch, _ptr(start_pos),
+                               _ptr(cu_new), total_new, max_new, _ptr(k_new), _ptr(v_new),
+                               _ptr(workspace), nbytes, _stream_handle(stream))
+    _check(rc, "kvq_hqmq_append")
+
+
+def hqmq_decode_workspace_bytes(d: KvqHqmqDims, batch: int, max_seq_len: int) -> int:
+    return int(lib().kvq_hqmq_decode_workspace_bytes(C.byref(d), batch, max_seq_len))
+
+
+def hqmq_decode_attention(d: KvqHqmqDims, lay: KvqHqmqLayer, cch: KvqHqmqCache, batch: int,
+                          seq_len, max_seq_len: int, q, out, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kvq_hqmq_decode_attention(C.byref(d), C.byref(lay), C.byref(cch), batch,
+                                         _ptr(seq_len), max_seq_len, _ptr(q), _ptr(out),
+                                         _ptr(workspace), nbytes, _stream_handle(stream))
+    _check(rc, "kvq_hqmq_decode_attention")
+
+
+class HqmqDeviceCache:
+    """Owns the device tensors of one layer's HQMQ cache: pool uint8
+    [num_pages][Hkv][P][192], block_table int32 [B][stride], and the append
+    workspace (zeroed once, as the library requires)."""
+
+    def __init__(self, d: KvqHqmqDims, num_pages: int, block_table, device="cuda", fill=0):
+        import torch
+        self.d = d
+        self.num_pages = num_pages
+        self.pool = torch.full((num_pages, d.n_kv_heads, d.page_size, HQMQ_TOKEN_BYTES), fill,
+                               dtype=torch.uint8, device=device)
+        self.block_table = torch.as_tensor(np.ascontiguousarray(block_table, np.int32)).to(device)
+        self.handle = hqmq_cache(self.pool, num_pages, self.block_table)
+        self.append_ws = torch.zeros(hqmq_append_workspace_bytes(d, 0), dtype=torch.uint8,
+                                     device=device)
 
 
 # ------------------------------------------------------------------ read-bandwidth probes

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "kvq2.h"
+#include "kvq2_hqmq.h"
 #include "kvq2_internal.h"
 
 namespace kvq {
@@ -139,6 +140,44 @@ int main() {
     q[3] = 0x7F80;   // +inf
     CHECK(kvq_calibrate(&s, N, q.data(), k.data(), v.data(), 0.999, RK.data(), RV.data(), &cK, &cV) == KVQ_ERR_NUMERIC);
     CHECK(kvq_calibrate(&s, N, q.data(), k.data(), v.data(), 1.5, RK.data(), RV.data(), &cK, &cV) == KVQ_ERR_ARG);
+  }
+  // ---- HQMQ codec: validation, planning, the host codebook product
+  {
+    kvq_hqmq_dims hd = {32, 8, 128, 16, 10, 0.0f};
+    kvq_hqmq_layer hl = {static_cast<const float*>(fake(0)), static_cast<const float*>(fake(0x1000))};
+    kvq_hqmq_cache hc = {static_cast<uint8_t*>(fake(0x200000)), 100,
+                         static_cast<const int32_t*>(fake(0x300000)), 8};
+    const size_t aws = kvq_hqmq_append_workspace_bytes(&hd, 100);
+    CHECK(aws > 0);
+    const int32_t* ip = static_cast<const int32_t*>(fake(0x400000));
+    const uint16_t* up = static_cast<const uint16_t*>(fake(0x500000));
+    const int before = kvq::g_launches;
+    CHECK(kvq_hqmq_append(&hd, &hl, &hc, 2, ip, ip, 4, 2, up, up, fake(0x600000), aws, nullptr) == KVQ_OK);
+    CHECK(kvq::g_launches == before + 1);
+    CHECK(kvq_hqmq_append(&hd, &hl, &hc, 2, ip, ip, 4, 2, up, up, fake(0x600000), aws - 1, nullptr) == KVQ_ERR_WORKSPACE);
+    CHECK(kvq_hqmq_append(&hd, &hl, &hc, 2, ip, ip, 0, 0, nullptr, nullptr, nullptr, 0, nullptr) == KVQ_OK);
+    for (int B : {1, 7, 64, 65535})
+      for (int L : {0, 1, 255, 4096, 131072, 1 << 30}) {
+        const size_t need = kvq_hqmq_decode_workspace_bytes(&hd, B, L);
+        CHECK(need > 0);
+        CHECK(kvq_hqmq_decode_attention(&hd, &hl, &hc, B, ip, L, up, static_cast<float*>(fake(0x700000)),
+                                        fake(0x800000), need, nullptr) == KVQ_OK);
+        CHECK(kvq::g_last_ws_bytes == need);
+      }
+    for (int G : {1, 4, 5, 8, 16}) {
+      kvq_hqmq_dims g = {8 * G, 8, 128, 64, 3, 0.0f};
+      CHECK(kvq_hqmq_decode_workspace_bytes(&g, 3, 1000) > 0);
+    }
+    kvq_hqmq_dims bad = hd;
+    bad.n_secondary = 11;
+    CHECK(kvq_hqmq_decode_workspace_bytes(&bad, 1, 10) == 0);
+    float sec[40], cb[960];
+    std::mt19937 r2(7);
+    for (float& x : sec) x = nd(r2);
+    for (int S = 1; S <= 10; ++S) CHECK(kvq_hqmq_codebook(S, sec, cb) == KVQ_OK);
+    CHECK(kvq_hqmq_codebook(0, sec, cb) == KVQ_ERR_ARG);
+    sec[5] = NAN;
+    CHECK(kvq_hqmq_codebook(4, sec, cb) == KVQ_ERR_NUMERIC);
   }
   if (g_fail) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);

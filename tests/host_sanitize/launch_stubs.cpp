@@ -4,6 +4,7 @@
 // asked to launch; none touches device memory.
 #include <cstdio>
 
+#include "kvq2_hqmq_internal.h"
 #include "kvq2_internal.h"
 
 namespace kvq {
@@ -44,5 +45,23 @@ int static_scratch(void** ptr) {
 int launch_zero_words(void*, size_t bytes, void*) { return bytes % 4 == 0 ? 0 : 1; }
 
 const char* hip_error_name(int err) { return err ? "stub launch error" : "no error"; }
+
+namespace hqmq {
+
+int launch_append(const kvq_hqmq_dims&, const kvq_hqmq_layer&, const kvq_hqmq_cache&, int32_t,
+                  const int32_t*, const int32_t*, int32_t total_new, const uint16_t*,
+                  const uint16_t*, void*, void*) {
+  ++g_launches;
+  return total_new > 0 ? 0 : 1;
+}
+
+int launch_decode(const kvq_hqmq_dims&, const kvq_hqmq_layer&, const kvq_hqmq_cache&, int32_t,
+                  const int32_t*, const uint16_t*, float*, void*, const DecodePlan& plan, void*) {
+  ++g_launches;
+  g_last_ws_bytes = plan.partial_bytes;
+  return plan.n_split >= 1 && plan.n_pass >= 1 ? 0 : 1;
+}
+
+}  // namespace hqmq
 
 }  // namespace kvq

@@ -17,6 +17,7 @@ HERE = os.path.join(ROOT, "tests", "host_sanitize")
 def test_host_code_clean_under_asan_and_ubsan(tmp_path):
     exe = str(tmp_path / "kvq2_host_selftest")
     srcs = [os.path.join(CSRC, "kvq2_host.cpp"), os.path.join(CSRC, "kvq2_calibrate.cpp"),
+            os.path.join(CSRC, "kvq2_hqmq_host.cpp"),
             os.path.join(HERE, "launch_stubs.cpp"), os.path.join(HERE, "host_selftest.cpp")]
     cmd = ["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
            "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-pthread",
