@@ -320,6 +320,197 @@ def int2_chunk_offsets(w, bt, lens):
     return np.concatenate(out) if out else np.zeros(0, np.int64)
 
 
+HQMQ_METRIC = "HQMQ paged decode-attention HBM GB/s (% of peak) + µs/step"
+HQMQ_TOKEN_BYTES = 192     # per (token, KV head): K and V records of 96 bytes
+
+
+def hqmq_decode_bytes(w, lens, n_secondary):
+    """Algorithmic HBM bytes of one HQMQ decode launch."""
+    tot = sum(w.n_kv_heads * HQMQ_TOKEN_BYTES * int(L) + 4 * math.ceil(int(L) / w.page_size)
+              for L in lens)
+    tot += w.batch * w.n_q_heads * HEAD_DIM * (2 + 4)               # q bf16 in, out fp32
+    tot += 2 * w.n_kv_heads * 24 * n_secondary * 16                 # codebooks
+    return tot
+
+
+def hqmq_append_bytes(w, n_new, n_secondary):
+    """Algorithmic HBM bytes of one HQMQ append of n_new tokens per sequence:
+    the new bf16 K and V in, their records out, the codebooks."""
+    return (w.batch * n_new * w.n_kv_heads * (2 * 256 + HQMQ_TOKEN_BYTES)
+            + 2 * w.n_kv_heads * 24 * n_secondary * 16)
+
+
+def run_hqmq(args):
+    """The HQMQ step (kvq_hqmq_append of one token per sequence, then
+    kvq_hqmq_decode_attention over every position) on the workload's shape,
+    timed like the INT2 step."""
+    import numpy as np
+    import torch
+
+    from long_context_decode_kvq_amd import kvq2
+    from long_context_decode_kvq_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    S = args.hqmq_secondary
+    device = torch.device("cuda:0")
+    n_steps = args.warmup + args.steps
+    lens_before = w.seq_lens() - 1
+    kd = kvq2.hqmq_dims(w.n_q_heads, w.n_kv_heads, w.page_size, S)
+    sec = W.hqmq_secondary(8000 + w.index, w.n_kv_heads, S)
+    cbs = [torch.from_numpy(np.stack([kvq2.hqmq_codebook(sec[r, h])
+                                      for h in range(w.n_kv_heads)])).to(device)
+           for r in range(2)]
+    lay = kvq2.hqmq_layer(cbs[0], cbs[1])
+    final = lens_before + n_steps
+    bt, n_pages, _ = W.page_assignment(w, final)
+    dc = kvq2.HqmqDeviceCache(kd, n_pages, bt, device=device)
+    t0 = time.time()
+    chunk = 8192
+    done = np.zeros(w.batch, np.int64)
+    while True:
+        todo = np.minimum(lens_before - done, chunk)
+        if todo.sum() == 0:
+            break
+        ks, vs = [], []
+        for b in range(w.batch):
+            if todo[b]:
+                k, v = W.sequence_kv_device(w, b, int(done[b]), int(todo[b]), device)
+                ks.append(k)
+                vs.append(v)
+        cu = np.zeros(w.batch + 1, np.int32)
+        cu[1:] = np.cumsum(todo)
+        kvq2.hqmq_append(kd, lay, dc.handle, w.batch,
+                         torch.from_numpy(done.astype(np.int32)).to(device),
+                         torch.from_numpy(cu).to(device), int(cu[-1]), int(todo.max()),
+                         torch.cat(ks), torch.cat(vs), dc.append_ws)
+        done += todo
+    torch.cuda.synchronize()
+    log(f"[bench] built HQMQ cache: {w.batch} x {int(lens_before.max())} tokens, {n_pages} pages "
+        f"({dc.pool.numel() / 2**30:.2f} GiB pool) in {time.time() - t0:.1f}s")
+    pool_bytes = dc.pool.numel()
+    copies = 1 if pool_bytes >= 512 * 2**20 else int(math.ceil(512 * 2**20 / pool_bytes))
+    pools = [dc.pool] + [dc.pool.clone() for _ in range(copies - 1)]
+    handles = [dc.handle] + [kvq2.hqmq_cache(p, n_pages, dc.block_table) for p in pools[1:]]
+    max_len = int(final.max())
+    ws = torch.empty(kvq2.hqmq_decode_workspace_bytes(kd, w.batch, max_len), dtype=torch.uint8,
+                     device=device)
+    out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=device)
+    cu1 = torch.arange(w.batch + 1, dtype=torch.int32, device=device)
+    starts = [torch.from_numpy((lens_before + k).astype(np.int32)).to(device)
+              for k in range(n_steps)]
+    seqs = [torch.from_numpy((lens_before + k + 1).astype(np.int32)).to(device)
+            for k in range(n_steps)]
+    qs = [W.decode_queries_device(w, k, device) for k in range(n_steps)]
+    new_kv = [W.sequence_kv_device(w, b, int(lens_before[b]), n_steps, device)
+              for b in range(w.batch)]
+    k_new = [torch.cat([new_kv[b][0][k:k + 1] for b in range(w.batch)]).contiguous()
+             for k in range(n_steps)]
+    v_new = [torch.cat([new_kv[b][1][k:k + 1] for b in range(w.batch)]).contiguous()
+             for k in range(n_steps)]
+    stream = torch.cuda.current_stream()
+
+    def decode_call(h, seq, q, st):
+        kvq2.hqmq_decode_attention(kd, lay, h, w.batch, seq, max_len, q, out, ws, st)
+
+    def step(k, st):
+        h = handles[k % copies]
+        kvq2.hqmq_append(kd, lay, h, w.batch, starts[k], cu1, w.batch, 1, k_new[k], v_new[k],
+                         dc.append_ws, st)
+        decode_call(h, seqs[k], qs[k], st)
+
+    for k in range(args.warmup):
+        step(k, stream)
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.steps):
+                step(args.warmup + i, cap)
+        torch.cuda.synchronize()
+    # untimed pre-warm (decode calls only read the cache)
+    t_pre, n_pre = time.perf_counter(), 0
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(8):
+            decode_call(handles[n_pre % copies], seqs[0], qs[0], stream)
+            n_pre += 1
+        torch.cuda.synchronize()
+    prewarm_wall = time.perf_counter() - t_pre
+    e_begin = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_begin.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i, stream)
+    e_end.record(stream)
+    last = args.warmup + args.steps - 1
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a0, a1 in ev:
+        a0.record(stream)
+        decode_call(handles[last % copies], seqs[last], qs[last], stream)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e_begin.elapsed_time(e_end) / args.steps
+    dec_ms = np.array([a0.elapsed_time(a1) for a0, a1 in ev])
+    dec_avg_ms = float(np.mean(dec_ms))
+    pct = {p: float(np.percentile(dec_ms, p)) * 1e3 for p in (10, 50, 90)}
+    step_bytes = [hqmq_decode_bytes(w, lens_before + args.warmup + i + 1, S) +
+                  hqmq_append_bytes(w, 1, S) for i in range(args.steps)]
+    value = float(np.sum(step_bytes)) / (ms_per_step * 1e-3 * args.steps) / 1e9
+    dec_bytes = hqmq_decode_bytes(w, lens_before + last + 1, S)
+    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    log(f"[bench] HQMQ step {ms_per_step * 1e3:.1f} us; decode {dec_avg_ms * 1e3:.1f} us "
+        f"(p10 {pct[10]:.1f}, p50 {pct[50]:.1f}, p90 {pct[90]:.1f}); decode {achieved:.0f} GB/s "
+        f"= {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+    rec = {
+        "metric": HQMQ_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "codec": "hqmq", "n_secondary": S,
+            "batch": w.batch, "context": int(lens_before.max()) + 1,
+            "context_note": "step k appends 1 token per sequence and decodes at context + k",
+            "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": HEAD_DIM,
+            "page_size": w.page_size, "layers": 1, "pool_copies": copies,
+            "step_call": "kvq_hqmq_append + kvq_hqmq_decode_attention",
+            "launch": ("host loop" if graph is None
+                       else f"one HIP graph of the {args.steps} steps, replayed once"),
+            "us_per_step": round(ms_per_step * 1e3, 2),
+            "decode_us": round(dec_avg_ms * 1e3, 2),
+            "decode_us_p10": round(pct[10], 2),
+            "decode_us_p50": round(pct[50], 2),
+            "decode_us_p90": round(pct[90], 2),
+            "decode_bytes": int(dec_bytes),
+        },
+        "prewarm": {"seconds": round(prewarm_wall, 3), "decode_calls": n_pre},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "hqmq decode",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +530,11 @@ def main():
     ap.add_argument("--quant-group", type=int, default=0, choices=(0, 32, 64, 128),
                     help="channels per (scale, zero) pair (0 = 128); narrower groups also "
                          "use a Hadamard of the same block size and run on the VALU decode")
+    ap.add_argument("--codec", default="int2", choices=("int2", "hqmq"),
+                    help="int2: the OSCAR-style INT2 cache (default); hqmq: the HQMQ codec "
+                         "(quaternion product codebook, Med3x fp16 chunks) on the same shape")
+    ap.add_argument("--hqmq-secondary", type=int, default=10,
+                    help="secondary quaternions S of the HQMQ codebook (24 S words)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the read-ceiling probes")
     ap.add_argument("--no-graph", action="store_true",
@@ -359,6 +555,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(one process, one MI355X). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.codec == "hqmq":
+        run_hqmq(args)
+        return
 
     # the oracle's worker processes are forked before this process touches the GPU
     # (the oracle leg times the one-query decode step; multi-query lines go without it)

@@ -165,6 +165,9 @@ __device__ __forceinline__ float (*wave_o())[GP][kHeadDim] {
 // ring slots apart and would otherwise wait for every outstanding DMA before
 // any LDS read.  The kernel waits explicitly (vmcnt) for the one tile it
 // reads; no other vector-memory instruction is issued inside the tile loop.
+// The outputs of an assembly block of several loads are early-clobber: a
+// load's destination must not share a register with an address that a later
+// load of the block still reads.
 // M0 holds the LDS destination; lane i writes size bytes at M0 + size * i.
 // The loads carry the non-temporal hint: every chunk is read once, and on
 // the MI355X the scattered 1152-byte chunk pattern streams at ~6.55 TB/s
@@ -346,7 +349,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           "ds_read_b128 %4, %7\n\t"
           "ds_read_b128 %5, %7 offset:64\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(kc0), "=v"(vc0), "=v"(kc1), "=v"(vc1), "=v"(kp), "=v"(vp)
+          : "=&v"(kc0), "=&v"(vc0), "=&v"(kc1), "=&v"(vc1), "=&v"(kp), "=&v"(vp)
           : "v"(acode), "v"(aprm)
           : "memory");
       after_reads();
@@ -461,7 +464,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           "ds_read_b128 %2, %5\n\t"
           "ds_read_b128 %3, %5 offset:64\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(kc[0]), "=v"(vc[0]), "=v"(kp), "=v"(vp)
+          : "=&v"(kc[0]), "=&v"(vc[0]), "=&v"(kp), "=&v"(vp)
           : "v"(acode), "v"(aprm)
           : "memory");
     } else if constexpr (NPT == 2) {
@@ -473,7 +476,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           "ds_read_b128 %4, %7\n\t"
           "ds_read_b128 %5, %7 offset:64\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(kc[0]), "=v"(vc[0]), "=v"(kc[1]), "=v"(vc[1]), "=v"(kp), "=v"(vp)
+          : "=&v"(kc[0]), "=&v"(vc[0]), "=&v"(kc[1]), "=&v"(vc[1]), "=&v"(kp), "=&v"(vp)
           : "v"(acode), "v"(aprm)
           : "memory");
     } else {
@@ -490,8 +493,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           "ds_read_b128 %8, %11\n\t"
           "ds_read_b128 %9, %11 offset:64\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(kc[0]), "=v"(vc[0]), "=v"(kc[1]), "=v"(vc[1]), "=v"(kc[2]), "=v"(vc[2]),
-            "=v"(kc[3]), "=v"(vc[3]), "=v"(kp), "=v"(vp)
+          : "=&v"(kc[0]), "=&v"(vc[0]), "=&v"(kc[1]), "=&v"(vc[1]), "=&v"(kc[2]), "=&v"(vc[2]),
+            "=&v"(kc[3]), "=&v"(vc[3]), "=&v"(kp), "=&v"(vp)
           : "v"(acode), "v"(aprm)
           : "memory");
     }

@@ -283,64 +283,105 @@ struct DecodeArgs {
   int n_split, n_pass;
 };
 
-// Sum over groups of N lanes (N = 8, 16, 32 consecutive lanes); every lane
-// of a group gets the group's total.
+// A tile is 16 consecutive positions of one (sequence, KV head): 3072
+// contiguous bytes of one page (pages hold a whole number of tiles).  Each
+// wave streams its tiles through a ring of kRing LDS slots with direct
+// HBM -> LDS loads (three 64-lane x 16-byte loads per tile, non-temporal:
+// every record is read once), so that kRing tiles are in flight per wave
+// while one is decoded.
+constexpr int kTileTokens = 16;
+constexpr int kTileBytes = kTileTokens * kTokenBytes;
+constexpr int kRing = 4;
+constexpr int kDmaPerTile = kTileBytes / 1024;
+
+// The loads and the LDS reads of the ring are written in assembly, with
+// explicit waits: the compiler does not count the direct loads, so a wait
+// of its own could not cover them.  Outputs of a block of several reads are
+// early-clobber (no destination may share a register with an address that a
+// later read of the block still uses).  M0 holds the LDS destination; lane i
+// writes 16 bytes at M0 + 16 i.
+__device__ __forceinline__ void dma_x4(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Sum over groups of N consecutive lanes (N = 16 or 32); every lane of a
+// group gets the group's total.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   v += dpp_move<kQuadXor1>(v);
   v += dpp_move<kQuadXor2>(v);
   v += dpp_move<kRowHalfMirror>(v);
-  if constexpr (N >= 16) v += dpp_move<kRowMirror>(v);
+  v += dpp_move<kRowMirror>(v);
   if constexpr (N >= 32) v = xor16_sum(v);
   return v;
 }
 
-// The words of one record a lane needs: index and radius bytes of its CPL
-// chunks, and the header + fp16 slots (r_max, flags, slots 0..2).
-template <int CPL>
+// The words of one record that a lane needs from LDS: the index and radius
+// bytes of its CPL chunks, r_max (low half of hdr.x) and the flags (hdr.y).
 struct RecWords {
   uint32_t idx, rad;
-  uint4 hdr;       // r_max | 0, flags, slot 0 (two dwords)
-  uint4 slots;     // slots 1 and 2
+  uint2 hdr;
 };
 
-// w, or all zeros when !ok (field by field: a select between two structs
-// would go through private memory)
 template <int CPL>
-__device__ __forceinline__ RecWords<CPL> keep_if(bool ok, const RecWords<CPL>& w) {
-  RecWords<CPL> r;
-  r.idx = ok ? w.idx : 0u;
-  r.rad = ok ? w.rad : 0u;
-  r.hdr = make_uint4(ok ? w.hdr.x : 0u, ok ? w.hdr.y : 0u, ok ? w.hdr.z : 0u, ok ? w.hdr.w : 0u);
-  r.slots = make_uint4(ok ? w.slots.x : 0u, ok ? w.slots.y : 0u, ok ? w.slots.z : 0u,
-                       ok ? w.slots.w : 0u);
-  return r;
-}
-
-template <int CPL>
-__device__ __forceinline__ RecWords<CPL> load_record(const uint8_t* rec, int sub) {
-  RecWords<CPL> w;
-  if constexpr (CPL == 4) {
-    w.idx = *reinterpret_cast<const uint32_t*>(rec + kIdxOff + 4 * sub);
-    w.rad = *reinterpret_cast<const uint32_t*>(rec + kRadOff + 4 * sub);
-  } else if constexpr (CPL == 2) {
-    w.idx = *reinterpret_cast<const uint16_t*>(rec + kIdxOff + 2 * sub);
-    w.rad = *reinterpret_cast<const uint16_t*>(rec + kRadOff + 2 * sub);
+__device__ __forceinline__ void read_record_pair(uint32_t rec, int sub, RecWords& k,
+                                                 RecWords& v) {
+  const uint32_t ai = rec + CPL * sub, ah = rec + kRmaxOff;
+  if constexpr (CPL == 2) {
+    asm volatile(
+        "ds_read_u16 %0, %6\n\t"
+        "ds_read_u16 %1, %6 offset:32\n\t"
+        "ds_read_b64 %2, %7\n\t"
+        "ds_read_u16 %3, %6 offset:96\n\t"
+        "ds_read_u16 %4, %6 offset:128\n\t"
+        "ds_read_b64 %5, %7 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k.idx), "=&v"(k.rad), "=&v"(k.hdr), "=&v"(v.idx), "=&v"(v.rad), "=&v"(v.hdr)
+        : "v"(ai), "v"(ah)
+        : "memory");
   } else {
-    w.idx = rec[kIdxOff + sub];
-    w.rad = rec[kRadOff + sub];
+    static_assert(CPL == 1, "lane layout");
+    asm volatile(
+        "ds_read_u8 %0, %6\n\t"
+        "ds_read_u8 %1, %6 offset:32\n\t"
+        "ds_read_b64 %2, %7\n\t"
+        "ds_read_u8 %3, %6 offset:96\n\t"
+        "ds_read_u8 %4, %6 offset:128\n\t"
+        "ds_read_b64 %5, %7 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k.idx), "=&v"(k.rad), "=&v"(k.hdr), "=&v"(v.idx), "=&v"(v.rad), "=&v"(v.hdr)
+        : "v"(ai), "v"(ah)
+        : "memory");
   }
-  w.hdr = *reinterpret_cast<const uint4*>(rec + kRmaxOff);
-  w.slots = *reinterpret_cast<const uint4*>(rec + kRmaxOff + 16);
-  return w;
 }
 
-// Chunk c of a lane's CPL chunks (chunk j = sub * CPL + c): its values
-// before the radius (the codeword, or for a kept chunk its fp16 values) and
-// the radius (code * r_max / 255, or 1 for a kept chunk).
+// fp16 values of kept chunk slot e of the record at LDS address rec.
+__device__ __forceinline__ float4 read_kept(uint32_t rec, int e) {
+  uint2 d;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(d)
+               : "v"(rec + kKeptOff + 8 * e)
+               : "memory");
+  return make_float4(f16_bits_to_float(d.x & 0xFFFFu), f16_bits_to_float(d.x >> 16),
+                     f16_bits_to_float(d.y & 0xFFFFu), f16_bits_to_float(d.y >> 16));
+}
+
+// Chunk c of a lane's CPL chunks (chunk j = sub CPL + c): its direction or
+// kept values v and its radius rh (code r_max / 255, or 1 when kept).
 template <int CPL, bool KEPT>
-__device__ __forceinline__ void chunk_value(const RecWords<CPL>& w, const float4* cb, int sub,
-                                            int c, float4& v, float& rh) {
+__device__ __forceinline__ void chunk_value(const RecWords& w, uint32_t rec, const float4* cb,
+                                            int sub, int c, float4& v, float& rh) {
   const uint32_t ix = (w.idx >> (8 * c)) & 0xFFu;
   const uint32_t rc = (w.rad >> (8 * c)) & 0xFFu;
   v = cb[ix];
@@ -349,15 +390,7 @@ __device__ __forceinline__ void chunk_value(const RecWords<CPL>& w, const float4
     const int j = sub * CPL + c;
     const uint32_t flags = w.hdr.y;
     if ((flags >> j) & 1u) {
-      const int e = __popc(flags & ((1u << j) - 1u));
-      // slot e by masks (a conditional choice would become an indexed
-      // access to private memory)
-      const uint32_t m0 = 0u - uint32_t(e == 0), m1 = 0u - uint32_t(e == 1);
-      const uint32_t m2 = 0u - uint32_t(e >= 2);
-      const uint32_t d0 = (w.hdr.z & m0) | (w.slots.x & m1) | (w.slots.z & m2);
-      const uint32_t d1 = (w.hdr.w & m0) | (w.slots.y & m1) | (w.slots.w & m2);
-      v = make_float4(f16_bits_to_float(d0 & 0xFFFFu), f16_bits_to_float(d0 >> 16),
-                      f16_bits_to_float(d1 & 0xFFFFu), f16_bits_to_float(d1 >> 16));
+      v = read_kept(rec, __popc(flags & ((1u << j) - 1u)));
       rh = 1.0f;
     }
   }
@@ -370,13 +403,14 @@ __device__ __forceinline__ uint32_t chunk_mask(int sub) {
 
 // Logit parts of a lane's CPL key chunks: part[g] += r_hat <q_j, c>.
 template <int CPL, int GP, bool KEPT>
-__device__ __forceinline__ void qk_chunks(const RecWords<CPL>& w, const float4* cb, int sub,
-                                          const float4 (&qv)[GP][CPL], float (&part)[GP]) {
+__device__ __forceinline__ void qk_chunks(const RecWords& w, uint32_t rec, const float4* cb,
+                                          int sub, const float4 (&qv)[GP][CPL],
+                                          float (&part)[GP]) {
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     float4 v;
     float rh;
-    chunk_value<CPL, KEPT>(w, cb, sub, c, v, rh);
+    chunk_value<CPL, KEPT>(w, rec, cb, sub, c, v, rh);
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
       const float d = fmaf(qv[g][c].x, v.x, fmaf(qv[g][c].y, v.y,
@@ -388,13 +422,14 @@ __device__ __forceinline__ void qk_chunks(const RecWords<CPL>& w, const float4* 
 
 // Value accumulation of a lane's CPL value chunks: acc[g][c] += (p r_hat) v.
 template <int CPL, int GP, bool KEPT>
-__device__ __forceinline__ void pv_chunks(const RecWords<CPL>& w, const float4* cb, int sub,
-                                          const float (&p)[GP], float4 (&acc)[GP][CPL]) {
+__device__ __forceinline__ void pv_chunks(const RecWords& w, uint32_t rec, const float4* cb,
+                                          int sub, const float (&p)[GP],
+                                          float4 (&acc)[GP][CPL]) {
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     float4 v;
     float rh;
-    chunk_value<CPL, KEPT>(w, cb, sub, c, v, rh);
+    chunk_value<CPL, KEPT>(w, rec, cb, sub, c, v, rh);
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
       const float wt = p[g] * rh;
@@ -409,16 +444,20 @@ __device__ __forceinline__ void pv_chunks(const RecWords<CPL>& w, const float4* 
 template <int CPL, int GP>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int LPT = 32 / CPL;          // lanes per token
-  constexpr int TPS = 64 / LPT;          // tokens per wave step
+  constexpr int TPS = 64 / LPT;          // tokens per pass
+  constexpr int PASSES = kTileTokens / TPS;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kTileBytes];
   __shared__ float4 cbs[2][kMaxWords];
   __shared__ float wm[4][GP], wl[4][GP];
-  __shared__ float wo[4][GP][kHeadDim];
+  static_assert(sizeof(ring) >= 4 * GP * kHeadDim * sizeof(float), "o' staging in the ring");
+  float (*wo)[GP][kHeadDim] = reinterpret_cast<float (*)[GP][kHeadDim]>(&ring[0][0][0]);
   const int s = blockIdx.x;
   const int h = blockIdx.y / a.n_pass, pass = blockIdx.y % a.n_pass;
   const int b = blockIdx.z;
   const int G = a.group;
   const int g0 = pass * GP;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int slot = lane / LPT, sub = lane % LPT;
   for (int i = threadIdx.x; i < 2 * a.n_words; i += 256) {
     const int role = i / a.n_words, k = i % a.n_words;
@@ -439,6 +478,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                              hi16(w.y) * a.alpha);
     }
   }
+  // wait for q here, once: a wait of the compiler's inside the tile loop
+  // would also drain the ring's loads
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      asm volatile("" : "+v"(qv[g][c].x), "+v"(qv[g][c].y), "+v"(qv[g][c].z), "+v"(qv[g][c].w));
+  const int L = a.seq_len[b];
   __syncthreads();
 
   float m[GP], l[GP], thr[GP];
@@ -452,87 +499,111 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int c = 0; c < CPL; ++c) acc[g][c] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  const int L = a.seq_len[b];
-  const int t0 = int(int64_t(L) * s / a.n_split), t1 = int(int64_t(L) * (s + 1) / a.n_split);
-  const int32_t* bt_row = a.block_table + int64_t(b) * a.bt_stride;
-  const int psz_mask = a.page_size - 1;
+  // this split's tiles [T0, T1); the wave takes tiles T0 + wave + 4 k
+  const int n_tiles_all = (L + kTileTokens - 1) / kTileTokens;
+  const int T0 = int(int64_t(n_tiles_all) * s / a.n_split);
+  const int T1 = int(int64_t(n_tiles_all) * (s + 1) / a.n_split);
+  const int my_tiles = T1 - T0 > wave ? (T1 - T0 - wave + 3) / 4 : 0;
+  typedef const int32_t __attribute__((address_space(4))) const_i32;
+  const_i32* bt_row = (const_i32*)(a.block_table + int64_t(b) * a.bt_stride);
+  const int32_t num_pages32 = static_cast<int32_t>(min(a.num_pages, int64_t(INT32_MAX)));
   const uint32_t my_mask = chunk_mask<CPL>(sub);
-  auto rec_of = [&](int pos) -> const uint8_t* {
-    int32_t page = -1;
-    const int lp = pos >> a.log2_page;
-    if (pos < t1 && lp < a.bt_stride) page = bt_row[lp];
-    if (page < 0 || page >= a.num_pages) return a.pool;    // invalid: a harmless record
-    return a.pool + ((int64_t(page) * a.n_kv_heads + h) * a.page_size + (pos & psz_mask)) *
-                        kTokenBytes;
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wave][0][0]));
+  // tile k of this wave (past the range, or on an invalid page: the pool's
+  // first bytes, read and never used)
+  auto issue = [&](int k, int r) {
+    const int tile = T0 + wave + 4 * k;
+    int64_t off = 0;
+    if (tile < T1) {
+      const int pos = tile * kTileTokens;
+      const int lp = pos >> a.log2_page;
+      const int32_t page = lp < a.bt_stride ? bt_row[lp] : -1;
+      if (page >= 0 && page < num_pages32)
+        off = ((int64_t(page) * a.n_kv_heads + h) * a.page_size + (pos & (a.page_size - 1))) *
+              kTileBytes / kTileTokens;
+    }
+    const uint8_t* src = a.pool + off;
+    const uint32_t lds = ring0 + r * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < kDmaPerTile; ++i) dma_x4(src + 1024 * i, 16u * lane, lds + 1024u * i);
   };
 
-  int base = t0 + wave * TPS;
-  RecWords<CPL> nk = keep_if(false, RecWords<CPL>{}), nv = nk;
-  if (base < t1) {
-    const uint8_t* r0 = rec_of(base + slot);
-    nk = load_record<CPL>(r0, sub);
-    nv = load_record<CPL>(r0 + kRecordBytes, sub);
-  }
-  for (; base < t1; base += 4 * TPS) {
-    const int pos = base + slot;
-    const bool valid = pos < t1;
-    // positions past the range read a harmless record; their words are
-    // replaced by zeros so that no value of it reaches the sums
-    const RecWords<CPL> wk = keep_if(valid, nk), wv = keep_if(valid, nv);
-    // prefetch the next step's records
-    if (base + 4 * TPS < t1) {
-      const uint8_t* rn = rec_of(base + 4 * TPS + slot);
-      nk = load_record<CPL>(rn, sub);
-      nv = load_record<CPL>(rn + kRecordBytes, sub);
-    }
-    // ---- logits
-    float part[GP];
+  if (my_tiles > 0) {
 #pragma unroll
-    for (int g = 0; g < GP; ++g) part[g] = 0.f;
-    if (__builtin_amdgcn_ballot_w64((wk.hdr.y & my_mask) != 0u) != 0)
-      qk_chunks<CPL, GP, true>(wk, cbs[0], sub, qv, part);
-    else
-      qk_chunks<CPL, GP, false>(wk, cbs[0], sub, qv, part);
-    float lg[GP];
-    bool up = false;
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      lg[g] = group_sum<LPT>(part[g]);
-      lg[g] = (valid && g0 + g < G) ? lg[g] : -INFINITY;
-      up |= lg[g] > thr[g];
-    }
-    // ---- lazy online softmax, one stream per token slot
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        const float mn = fmaxf(m[g], lg[g]);
-        if (mn > thr[g]) {
-          const float corr = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - mn);
-          l[g] *= corr;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            acc[g][c].x *= corr;
-            acc[g][c].y *= corr;
-            acc[g][c].z *= corr;
-            acc[g][c].w *= corr;
-          }
-          m[g] = mn;
-          thr[g] = mn + kTau;
+    for (int r = 0; r < kRing; ++r) issue(r, r);
+    for (int k = 0; k < my_tiles; ++k) {
+      const int r = k & (kRing - 1);
+      // kRing tiles are outstanding: this one and the kRing - 1 after it
+      wait_vmcnt<(kRing - 1) * kDmaPerTile>();
+      const int pos0 = (T0 + wave + 4 * k) * kTileTokens;
+      const uint32_t tile_lds = ring0 + r * kTileBytes;
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int t = ps * TPS + slot;
+        const bool valid = pos0 + t < L;
+        const uint32_t rec = tile_lds + t * kTokenBytes;
+        RecWords wk, wv;
+        read_record_pair<CPL>(rec, sub, wk, wv);
+        if (!valid) {
+          // positions past the sequence: zero words, so that nothing of
+          // their bytes reaches the sums
+          wk.idx = wk.rad = wv.idx = wv.rad = 0u;
+          wk.hdr = wv.hdr = make_uint2(0u, 0u);
         }
-      }
-    }
-    float p[GP];
+        // ---- logits
+        float part[GP];
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      p[g] = lg[g] == -INFINITY ? 0.f : exp2f(lg[g] - m[g]);
-      l[g] += p[g];
+        for (int g = 0; g < GP; ++g) part[g] = 0.f;
+        if (__builtin_amdgcn_ballot_w64((wk.hdr.y & my_mask) != 0u) != 0)
+          qk_chunks<CPL, GP, true>(wk, rec, cbs[0], sub, qv, part);
+        else
+          qk_chunks<CPL, GP, false>(wk, rec, cbs[0], sub, qv, part);
+        float lg[GP];
+        bool up = false;
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          lg[g] = group_sum<LPT>(part[g]);
+          lg[g] = (valid && g0 + g < G) ? lg[g] : -INFINITY;
+          up |= lg[g] > thr[g];
+        }
+        // ---- lazy online softmax, one stream per token slot
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+          for (int g = 0; g < GP; ++g) {
+            const float mn = fmaxf(m[g], lg[g]);
+            if (mn > thr[g]) {
+              const float corr = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - mn);
+              l[g] *= corr;
+#pragma unroll
+              for (int c = 0; c < CPL; ++c) {
+                acc[g][c].x *= corr;
+                acc[g][c].y *= corr;
+                acc[g][c].z *= corr;
+                acc[g][c].w *= corr;
+              }
+              m[g] = mn;
+              thr[g] = mn + kTau;
+            }
+          }
+        }
+        float p[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          p[g] = lg[g] == -INFINITY ? 0.f : exp2f(lg[g] - m[g]);
+          l[g] += p[g];
+        }
+        // ---- values
+        if (__builtin_amdgcn_ballot_w64((wv.hdr.y & my_mask) != 0u) != 0)
+          pv_chunks<CPL, GP, true>(wv, rec + kRecordBytes, cbs[1], sub, p, acc);
+        else
+          pv_chunks<CPL, GP, false>(wv, rec + kRecordBytes, cbs[1], sub, p, acc);
+      }
+      // every LDS read of the slot has completed (each read block waits for
+      // its data): refill it with the tile kRing steps ahead
+      issue(k + kRing, r);
     }
-    // ---- values
-    if (__builtin_amdgcn_ballot_w64((wv.hdr.y & my_mask) != 0u) != 0)
-      pv_chunks<CPL, GP, true>(wv, cbs[1], sub, p, acc);
-    else
-      pv_chunks<CPL, GP, false>(wv, cbs[1], sub, p, acc);
+    wait_vmcnt<0>();     // drain before the ring is reused as o' staging
   }
+  __syncthreads();
 
   // ---- merge the TPS token-slot streams of the wave (lanes sub + LPT k)
 #pragma unroll

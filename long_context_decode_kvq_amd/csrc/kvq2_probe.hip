@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256, 4) void chunk_read_kernel(const uint8_t* pool,
               "ds_read_b32 %1, %3 offset:1024\n\t"
               "ds_read_b32 %2, %4\n\t"
               "s_waitcnt lgkmcnt(0)"
-              : "=v"(w0), "=v"(w1), "=v"(w2)
+              : "=&v"(w0), "=&v"(w1), "=&v"(w2)
               : "v"(a_code), "v"(a_par)
               : "memory");
           acc ^= w0 ^ w1 ^ w2;

@@ -49,3 +49,12 @@ def test_append_bytes_of_one_token_step():
     # evicted token's ring read + 32 code bytes + one (scale, zero) pair
     expect = 28 * 8 * 2 * (256 + 256 + 256 + 32 + 4) + 2 * 8 * 128 * 128 * 4
     assert bench.append_bytes(w, lens) == expect
+
+
+def test_hqmq_bytes():
+    """192 bytes per (token, KV head): two 96-byte records (K, V)."""
+    w = W.WORKLOADS["conc_28x100k"]
+    expect = (28 * 8 * 192 * 100000 + 28 * math.ceil(100000 / 16) * 4
+              + 28 * 32 * 128 * 6 + 2 * 8 * 24 * 10 * 16)
+    assert bench.hqmq_decode_bytes(w, [100000] * 28, 10) == expect
+    assert bench.hqmq_append_bytes(w, 1, 10) == 28 * 8 * (512 + 192) + 2 * 8 * 240 * 16
