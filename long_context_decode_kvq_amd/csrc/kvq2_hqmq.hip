@@ -18,9 +18,9 @@
 // Decode: grid (n_split, Hkv x passes, B), 256 threads.  A token is taken by
 // LPT = 32 / CPL lanes, CPL chunks each (4 channels a chunk), so a wave step
 // covers 2 CPL tokens; every lane keeps q (scaled by sm_scale log2 e) and
-// the value accumulators of its CPL chunks for GP query heads (CPL x GP = 8:
-// two chunks and four heads, or one chunk and eight heads; larger groups
-// take several passes of eight heads).  Per chunk: the codeword from LDS, r_hat = code r_max/255,
+// the value accumulators of its CPL chunks for GP query heads (four chunks
+// and four heads, or one chunk and eight heads; larger groups take several
+// passes of eight heads).  Per chunk: the codeword from LDS, r_hat = code r_max/255,
 // logit part r_hat <q_j, c>, and after the LPT-lane sum and the lazy online
 // softmax o_j += (p r_hat) c.  Each group of LPT lanes (one token slot of the
 // wave step) runs its own softmax stream; the streams, the waves and the
@@ -315,14 +315,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Sum over groups of N consecutive lanes (N = 16 or 32); every lane of a
-// group gets the group's total.
+// Sum over groups of N consecutive lanes (N = 8, 16 or 32); every lane of
+// a group gets the group's total.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   v += dpp_move<kQuadXor1>(v);
   v += dpp_move<kQuadXor2>(v);
   v += dpp_move<kRowHalfMirror>(v);
-  v += dpp_move<kRowMirror>(v);
+  if constexpr (N >= 16) v += dpp_move<kRowMirror>(v);
   if constexpr (N >= 32) v = xor16_sum(v);
   return v;
 }
@@ -338,7 +338,19 @@ template <int CPL>
 __device__ __forceinline__ void read_record_pair(uint32_t rec, int sub, RecWords& k,
                                                  RecWords& v) {
   const uint32_t ai = rec + CPL * sub, ah = rec + kRmaxOff;
-  if constexpr (CPL == 2) {
+  if constexpr (CPL == 4) {
+    asm volatile(
+        "ds_read_b32 %0, %6\n\t"
+        "ds_read_b32 %1, %6 offset:32\n\t"
+        "ds_read_b64 %2, %7\n\t"
+        "ds_read_b32 %3, %6 offset:96\n\t"
+        "ds_read_b32 %4, %6 offset:128\n\t"
+        "ds_read_b64 %5, %7 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k.idx), "=&v"(k.rad), "=&v"(k.hdr), "=&v"(v.idx), "=&v"(v.rad), "=&v"(v.hdr)
+        : "v"(ai), "v"(ah)
+        : "memory");
+  } else if constexpr (CPL == 2) {
     asm volatile(
         "ds_read_u16 %0, %6\n\t"
         "ds_read_u16 %1, %6 offset:32\n\t"
@@ -442,12 +454,14 @@ __device__ __forceinline__ void pv_chunks(const RecWords& w, uint32_t rec, const
 }
 
 template <int CPL, int GP>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   constexpr int LPT = 32 / CPL;          // lanes per token
   constexpr int TPS = 64 / LPT;          // tokens per pass
   constexpr int PASSES = kTileTokens / TPS;
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kTileBytes];
   __shared__ float4 cbs[2][kMaxWords];
+  __shared__ float4 qs[GP][kChunks];            // q (scaled) by head and chunk
+  __shared__ float kc[4][kTileTokens][GP];      // logit terms of fp16-kept key chunks
   __shared__ float wm[4][GP], wl[4][GP];
   static_assert(sizeof(ring) >= 4 * GP * kHeadDim * sizeof(float), "o' staging in the ring");
   float (*wo)[GP][kHeadDim] = reinterpret_cast<float (*)[GP][kHeadDim]>(&ring[0][0][0]);
@@ -476,6 +490,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (ok) w = reinterpret_cast<const uint2*>(a.q + (int64_t(b) * a.n_q_heads + gq) * kHeadDim)[j];
       qv[g][c] = make_float4(lo16(w.x) * a.alpha, hi16(w.x) * a.alpha, lo16(w.y) * a.alpha,
                              hi16(w.y) * a.alpha);
+      if (slot == 0) qs[g][j] = qv[g][c];
     }
   }
   // wait for q here, once: a wait of the compiler's inside the tile loop
@@ -537,36 +552,68 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       wait_vmcnt<(kRing - 1) * kDmaPerTile>();
       const int pos0 = (T0 + wave + 4 * k) * kTileTokens;
       const uint32_t tile_lds = ring0 + r * kTileBytes;
+      const bool partial = pos0 + kTileTokens > L;     // the sequence ends inside the tile
+      // ---- the tile's fp16-kept key chunks (at most three per record; their
+      // index and radius bytes are zero, so the coded path adds nothing for
+      // them): lane (token tt, slot e) adds <q_j, x_e> for the e-th kept
+      // chunk j of token tt, summed over e and left in kc[wave][tt][g]
+      {
+        const int tt = lane >> 2, e = lane & 3;
+        const uint32_t krec = tile_lds + tt * kTokenBytes;
+        uint32_t flags;
+        asm volatile("ds_read_b32 %0, %1 offset:68\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(flags)
+                     : "v"(krec)
+                     : "memory");
+        float cg[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) cg[g] = 0.f;
+        if (pos0 + tt < L && e < __popc(flags)) {
+          uint32_t f = flags;
+          if (e >= 1) f &= f - 1u;
+          if (e >= 2) f &= f - 1u;
+          const int j = __builtin_ctz(f);
+          const float4 x = read_kept(krec, e);
+#pragma unroll
+          for (int g = 0; g < GP; ++g) {
+            const float4 qq = qs[g][j];
+            cg[g] = fmaf(qq.x, x.x, fmaf(qq.y, x.y, fmaf(qq.z, x.z, qq.w * x.w)));
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          cg[g] += dpp_move<kQuadXor1>(cg[g]);
+          cg[g] += dpp_move<kQuadXor2>(cg[g]);
+          if (e == 0) kc[wave][tt][g] = cg[g];
+        }
+      }
       for (int ps = 0; ps < PASSES; ++ps) {
         const int t = ps * TPS + slot;
         const bool valid = pos0 + t < L;
         const uint32_t rec = tile_lds + t * kTokenBytes;
         RecWords wk, wv;
         read_record_pair<CPL>(rec, sub, wk, wv);
-        if (!valid) {
+        if (partial && !valid) {
           // positions past the sequence: zero words, so that nothing of
           // their bytes reaches the sums
           wk.idx = wk.rad = wv.idx = wv.rad = 0u;
           wk.hdr = wv.hdr = make_uint2(0u, 0u);
         }
-        // ---- logits
+        // ---- logits: the coded chunks, then the kept chunks' terms
         float part[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) part[g] = 0.f;
-        if (__builtin_amdgcn_ballot_w64((wk.hdr.y & my_mask) != 0u) != 0)
-          qk_chunks<CPL, GP, true>(wk, rec, cbs[0], sub, qv, part);
-        else
-          qk_chunks<CPL, GP, false>(wk, rec, cbs[0], sub, qv, part);
+        qk_chunks<CPL, GP, false>(wk, rec, cbs[0], sub, qv, part);
         float lg[GP];
-        bool up = false;
+        uint64_t up = 0;
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-          lg[g] = group_sum<LPT>(part[g]);
+          lg[g] = group_sum<LPT>(part[g]) + kc[wave][t][g];
           lg[g] = (valid && g0 + g < G) ? lg[g] : -INFINITY;
-          up |= lg[g] > thr[g];
+          up |= __builtin_amdgcn_ballot_w64(lg[g] > thr[g]);
         }
         // ---- lazy online softmax, one stream per token slot
-        if (__builtin_amdgcn_ballot_w64(up) != 0) {
+        if (up != 0) {
 #pragma unroll
           for (int g = 0; g < GP; ++g) {
             const float mn = fmaxf(m[g], lg[g]);
@@ -747,7 +794,7 @@ int launch_decode(const kvq_hqmq_dims& d, const kvq_hqmq_layer& layer,
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(plan.n_split, d.n_kv_heads * plan.n_pass, batch);
   if (heads_per_pass(a.group) == 4)
-    hipLaunchKernelGGL((decode_kernel<2, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<4, 4>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((decode_kernel<1, 8>), grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL(combine_kernel, dim3(d.n_q_heads, batch), dim3(128), 0, st, a);
