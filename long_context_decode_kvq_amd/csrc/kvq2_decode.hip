@@ -228,34 +228,65 @@ __device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int 
   }
   __syncthreads();
   if constexpr (GP > 0) {
-    {
-      // QK operand of the MFMA kernel in its per-lane layout: lane (gq, n)
-      // holds column n = 2GP p + GP t + g (t = 0: f16 hi part, 1: lo part of
-      // q'[g] scaled by 2^-e_g 2^(8 - 2s)) for the 32 k-slots of its lane group.
-      uint32_t* bq = a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords;
-      const int kk = tid >> 6;                 // 4 k-steps x 64 lanes
-      const int gq = lane >> 4, n = lane & 15;
-      const int j = n % (2 * GP), g = j % GP;
-      const bool hi_col = j < GP, ok = g < G;
-      const float down = ok ? ldexpf(1.0f, -qexp[g]) : 0.f;
+    // QK operand of the MFMA kernel in its per-lane layout: lane (gq, n)
+    // holds column n = 2GP blk + GP t + g (t = 0: f16 hi part, 1: lo part of
+    // q'[g] scaled by 2^-e_g 2^(8 - 2s)) for the 32 k-slots of its lane group.
+    // With one (scale, zero) pair per vector every column block holds all
+    // channels.  With ng quantization groups, block blk of column set c
+    // holds only the channels of group (c nblk + blk) mod ng (zero
+    // elsewhere), so that each block's dot is one group's; a second set
+    // is needed when the tile has fewer blocks than groups.
+    constexpr int NBLK = 16 / (2 * GP);
+    const int ng = a.ng;
+    const int sets = (GP <= 4 && ng > NBLK) ? ng / NBLK : 1;
+    const int gch = kHeadDim / ng;            // channels per group
+    // sums of q'[g] over each 32-channel quarter (ng <= 4 groups are unions)
+    __shared__ float qq4[GP > 0 ? GP : 1][4];
+    if (tid < G * 4) {
+      const int g = tid >> 2, k = tid & 3;
+      float sum = 0.f;
+      for (int c = 0; c < 32; ++c) sum += qs[g][32 * k + c];
+      qq4[g][k] = sum;
+    }
+    __syncthreads();
+    uint32_t* bq = a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords;
+    const int kk = tid >> 6;                 // 4 k-steps x 64 lanes
+    const int gq = lane >> 4, n = lane & 15;
+    const int blk = n / (2 * GP), j = n % (2 * GP), g = j % GP;
+    const bool hi_col = j < GP, ok = g < G;
+    const float down = ok ? ldexpf(1.0f, -qexp[g]) : 0.f;
+    for (int c = 0; c < sets; ++c) {
+      const int grp = (c * NBLK + blk) % ng;
       for (int q = 0; q < 4; ++q) {
         uint32_t word = 0;
         for (int e = 0; e < 2; ++e) {
           int ch, sc;
           kslot_channel(gq, kk, 2 * q + e, ch, sc);
-          const float v = ok ? qs[g][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
+          const bool in = ng == 1 || ch / gch == grp;
+          const float v = (ok && in) ? qs[g][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
           const _Float16 vh = static_cast<_Float16>(v);
           const _Float16 vl = static_cast<_Float16>(v - static_cast<float>(vh));
           const uint32_t bits = __builtin_bit_cast(uint16_t, hi_col ? vh : vl);
           word |= bits << (16 * e);
         }
-        bq[lane * 16 + kk * 4 + q] = word;
+        bq[c * kBqSetWords + lane * 16 + kk * 4 + q] = word;
       }
-      if (kk == 0) {
-        const float qscale = ok ? ldexpf(1.0f, 16 + qexp[g]) : 1.0f;
-        reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane] = qscale;
-        reinterpret_cast<float*>(bq)[64 * 16 + 2 * lane + 1] = ok ? qsum[g] / qscale : 0.f;
+    }
+    if (kk == 0) {
+      const float qscale = ok ? ldexpf(1.0f, 16 + qexp[g]) : 1.0f;
+      float* lc = reinterpret_cast<float*>(bq) + 2 * kBqSetWords + 4 * lane;
+      lc[0] = qscale;
+      for (int c = 0; c < 2; ++c) {
+        float qbar = ok ? qsum[g] : 0.f;
+        if (ng > 1 && ok && c < sets) {
+          const int grp = (c * NBLK + blk) % ng;
+          qbar = 0.f;
+          for (int k = 0; k < 4; ++k)
+            if ((32 * k) / gch == grp) qbar += qq4[g][k];
+        }
+        lc[1 + c] = qbar / qscale;
       }
+      lc[3] = 0.f;
     }
   }
 }
@@ -395,8 +426,10 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
   a.partials = reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes +
                                         plan.prefix_bytes);
   const int G = a.group;
-  // the matrix-core kernel reads one (s, z) pair per vector: groups of 128
-  a.gp = (which == kDecodeValu || G > 8 || a.ng != 1) ? 0 : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
+  // the matrix-core kernel takes narrower quantization groups for up to four
+  // rows per (b, h)
+  a.gp = (which == kDecodeValu || G > 8 || (a.ng != 1 && G > 4)) ? 0
+                                                                : (G <= 2 ? 2 : G <= 4 ? 4 : 8);
   a.n_split_int2 = plan.n_split_int2;
   a.n_split = plan.n_split;
   a.piece_cost = plan.piece_cost;

@@ -117,17 +117,20 @@ const DecodeTuning& decode_tuning() {
 DecodeKernel selected_decode_kernel(const kvq_dims& d) {
   // KVQ_DECODE_KERNEL=valu selects the plain VALU kernel (kept as the
   // measured comparison point for the MFMA kernel); default is MFMA.  The
-  // MFMA kernel reads one (s, z) pair per vector, so quantization groups
-  // narrower than 128 channels always take the VALU kernel.
+  // MFMA kernel takes quantization groups narrower than 128 channels for up
+  // to four query heads per KV head; wider groups of heads then take the
+  // VALU kernel.
   const char* s = std::getenv("KVQ_DECODE_KERNEL");
   if (s != nullptr && std::strcmp(s, "valu") == 0) return kDecodeValu;
-  if (d.quant_group != 0 && d.quant_group != kHeadDim) return kDecodeValu;
+  if (d.quant_group != 0 && d.quant_group != kHeadDim && d.n_q_heads / d.n_kv_heads > 4)
+    return kDecodeValu;
   return kDecodeMfma;
 }
 
 int multi_query_pass(const kvq_dims& d, int32_t n_query, DecodeKernel which) {
   const int G = d.n_q_heads / d.n_kv_heads;
-  const int rows = (which == kDecodeMfma && G <= 8) ? 8 : kMaxGroup;
+  const bool narrow = d.quant_group != 0 && d.quant_group != kHeadDim;
+  const int rows = (which == kDecodeMfma && G <= 8) ? (narrow ? 4 : 8) : kMaxGroup;
   return std::max(1, std::min<int>(n_query, rows / G));
 }
 

@@ -26,7 +26,12 @@ constexpr int kPartialStride = 132;    // floats per (split, query head) partial
                                        // m, l, 2 pad, o'[128]
 constexpr int kQStride = 132;          // floats per rotated query: q'[128], sum(q'),
                                        // f16 scaling exponent, 2 pad
-constexpr int kBqWords = 64 * 16 + 64 * 2;   // u32 words per (b, h) of the QK operand block
+// u32 words per (b, h) of the QK operand block: up to two column sets of
+// [64 lanes][16 dwords] (a second set when a tile's column blocks cannot
+// hold every quantization group), then [64 lanes][4] lane constants
+// (qscale, then sum(q') over the lane's group in each set, divided by qscale).
+constexpr int kBqSetWords = 64 * 16;
+constexpr int kBqWords = 2 * kBqSetWords + 64 * 4;
 
 // 16-token chunks per tile of the MFMA decode for head-group width gp (2, 4
 // or 8): the QK tile's 16 columns hold (chunk, f16 hi/lo, head), so a tile
@@ -41,7 +46,7 @@ struct DecodePlan {
   int n_split;        // VALU decode: n_split_int2 + 1 (the last one takes the bf16 segments)
   size_t ticket_bytes;
   size_t qrot_bytes;    // rotated queries [B][Hq][kQStride] fp32
-  size_t bq_bytes;      // QK MFMA operand per (b, h): [64 lanes][16 dwords] + [64][2] fp32
+  size_t bq_bytes;      // QK MFMA operand per (b, h): kBqWords u32
   int piece_cost;       // MFMA decode: virtual tiles charged per (b, h) piece start
   int n_tok_slices;     // MFMA decode: 64-token slices of the token-by-token list
   int64_t tok_slot0;    // MFMA decode: first partial slot of those slices

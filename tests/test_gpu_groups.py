@@ -5,8 +5,9 @@ full or a block-diagonal Hadamard in the rotation, through the C ABI.
 The cache bytes after ragged bulk appends and token-by-token steps must equal
 the oracle's (pool chunks of 1024 + 128 * (128 / group) bytes), and decode,
 decode-step and multi-query outputs must match the oracle within 2e-3 max
-normwise relative error.  These layouts run on the VALU decode kernel, also
-when the matrix-core kernel is the one selected."""
+normwise relative error.  Up to four query rows per KV head run on the
+matrix-core kernel (one QK column block per group, one PV operand per
+group), more on the VALU kernel; both kernels are tested."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +22,12 @@ pytestmark = pytest.mark.gpu
 LAYOUTS = [(32, 32), (64, 64), (32, 128)]      # (quant_group, hadamard_block)
 
 
+@pytest.fixture(params=["mfma", "valu"])
+def kernel(request, monkeypatch):
+    monkeypatch.setenv("KVQ_DECODE_KERNEL", request.param)
+    return request.param
+
+
 def _ids(v):
     return f"g{v[0]}_hb{v[1]}"
 
@@ -29,16 +36,17 @@ CASES = [
     # Hq, Hkv, P, n_sink, W, lens
     (8, 2, 16, 4, 32, [700, 130, 17, 0]),      # G = 4, an empty and a short sequence
     (8, 8, 64, 0, 16, [1100, 45]),             # G = 1, no sink, page 64
+    (4, 2, 16, 4, 32, [650, 3, 130]),          # G = 2
     (32, 2, 32, 20, 64, [900]),                # G = 16
 ]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=_ids)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"h{c[0]}x{c[1]}_P{c[2]}")
-def test_group_cache_bytes_and_decode(case, layout):
+def test_group_cache_bytes_and_decode(case, layout, kernel):
     Hq, Hkv, P, ns, W, lens = case
     g, hb = layout
-    say(f"[groups] {case} group={g} hadamard_block={hb}")
+    say(f"[groups] {case} group={g} hadamard_block={hb} kernel={kernel}")
     sc = Scenario(Hq, Hkv, P, ns, W, lens, seed=3 * g + Hq, fill=0x33, quant_group=g,
                   hadamard_block=hb)
     assert sc.dc.pool.shape[-1] == O.chunk_bytes(g)
@@ -52,7 +60,7 @@ def test_group_cache_bytes_and_decode(case, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS[:2], ids=_ids)
-def test_group_decode_steps(layout):
+def test_group_decode_steps(layout, kernel):
     """Token-by-token decode steps (append then attention in one call) over
     ring evictions into INT2 chunks of the narrower layout."""
     g, hb = layout
@@ -65,7 +73,7 @@ def test_group_decode_steps(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS[:2], ids=_ids)
-def test_group_multi_query(layout):
+def test_group_multi_query(layout, kernel):
     g, hb = layout
     M = 4
     sc = Scenario(8, 2, 16, 4, 16, [400, 90, 3], seed=29 + g, quant_group=g, hadamard_block=hb)
