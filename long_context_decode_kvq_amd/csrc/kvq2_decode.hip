@@ -232,13 +232,16 @@ __device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int 
     // holds column n = 2GP blk + GP t + g (t = 0: f16 hi part, 1: lo part of
     // q'[g] scaled by 2^-e_g 2^(8 - 2s)) for the 32 k-slots of its lane group.
     // With one (scale, zero) pair per vector every column block holds all
-    // channels.  With ng quantization groups, block blk of column set c
-    // holds only the channels of group (c nblk + blk) mod ng (zero
-    // elsewhere), so that each block's dot is one group's; a second set
-    // is needed when the tile has fewer blocks than groups.
+    // channels.  With ng quantization groups, block blk holds only the
+    // channels of the groups k with k mod nb = blk mod nb, nb = min(ng,
+    // nblk) (zero elsewhere), so that each block's dot is one group's; when
+    // the tile has fewer blocks than groups, the kernel runs one product per
+    // set c of nblk groups with the code operand restricted to that set's
+    // groups, and block blk of set c is group c nblk + blk.
     constexpr int NBLK = 16 / (2 * GP);
     const int ng = a.ng;
     const int sets = (GP <= 4 && ng > NBLK) ? ng / NBLK : 1;
+    const int nb = ng < NBLK ? ng : NBLK;
     const int gch = kHeadDim / ng;            // channels per group
     // sums of q'[g] over each 32-channel quarter (ng <= 4 groups are unions)
     __shared__ float qq4[GP > 0 ? GP : 1][4];
@@ -255,26 +258,23 @@ __device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int 
     const int blk = n / (2 * GP), j = n % (2 * GP), g = j % GP;
     const bool hi_col = j < GP, ok = g < G;
     const float down = ok ? ldexpf(1.0f, -qexp[g]) : 0.f;
-    for (int c = 0; c < sets; ++c) {
-      const int grp = (c * NBLK + blk) % ng;
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = 0;
-        for (int e = 0; e < 2; ++e) {
-          int ch, sc;
-          kslot_channel(gq, kk, 2 * q + e, ch, sc);
-          const bool in = ng == 1 || ch / gch == grp;
-          const float v = (ok && in) ? qs[g][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
-          const _Float16 vh = static_cast<_Float16>(v);
-          const _Float16 vl = static_cast<_Float16>(v - static_cast<float>(vh));
-          const uint32_t bits = __builtin_bit_cast(uint16_t, hi_col ? vh : vl);
-          word |= bits << (16 * e);
-        }
-        bq[c * kBqSetWords + lane * 16 + kk * 4 + q] = word;
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+      for (int e = 0; e < 2; ++e) {
+        int ch, sc;
+        kslot_channel(gq, kk, 2 * q + e, ch, sc);
+        const bool in = ng == 1 || (ch / gch) % nb == blk % nb;
+        const float v = (ok && in) ? qs[g][ch] * down * ldexpf(1.0f, 8 - 2 * sc) : 0.f;
+        const _Float16 vh = static_cast<_Float16>(v);
+        const _Float16 vl = static_cast<_Float16>(v - static_cast<float>(vh));
+        const uint32_t bits = __builtin_bit_cast(uint16_t, hi_col ? vh : vl);
+        word |= bits << (16 * e);
       }
+      bq[lane * 16 + kk * 4 + q] = word;
     }
     if (kk == 0) {
       const float qscale = ok ? ldexpf(1.0f, 16 + qexp[g]) : 1.0f;
-      float* lc = reinterpret_cast<float*>(bq) + 2 * kBqSetWords + 4 * lane;
+      float* lc = reinterpret_cast<float*>(bq) + kBqOperandWords + 4 * lane;
       lc[0] = qscale;
       for (int c = 0; c < 2; ++c) {
         float qbar = ok ? qsum[g] : 0.f;

@@ -242,21 +242,18 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   const int g_col = j % GP;          // query head of this column
   const bool g_ok = g_col < G;
 
-  // QK operand (q' hi/lo in f16, per-lane layout; one column set per
-  // SETS) and this column's logit scale and group sums of q', all prepared
-  // by the rotation pre-pass.
+  // QK operand (q' hi/lo in f16, per-lane layout) and this column's logit
+  // scale and group sums of q' (one per column set), all prepared by the
+  // rotation pre-pass.
   constexpr int SETS = Geo<GP, NG>::SETS;
-  half8_t Bq[SETS][4];
+  half8_t Bq[4];
   float qscale, qbar_s, qbar2;
   {
     const uint32_t* base = a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords;
+    const uint4* src = reinterpret_cast<const uint4*>(base + lane * 16);
 #pragma unroll
-    for (int c = 0; c < SETS; ++c) {
-      const uint4* src = reinterpret_cast<const uint4*>(base + c * kBqSetWords + lane * 16);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) Bq[c][kk] = __builtin_bit_cast(half8_t, src[kk]);
-    }
-    const float4 lq = reinterpret_cast<const float4*>(base + 2 * kBqSetWords)[lane];
+    for (int kk = 0; kk < 4; ++kk) Bq[kk] = __builtin_bit_cast(half8_t, src[kk]);
+    const float4 lq = reinterpret_cast<const float4*>(base + kBqOperandWords)[lane];
     qscale = lq.x;
     qbar_s = lq.y;
     qbar2 = lq.z;
@@ -264,9 +261,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     // waits for the loads here, once, instead of inside the tile loop, where
     // its vmcnt wait would also drain the in-flight tile DMA.
 #pragma unroll
-    for (int c = 0; c < SETS; ++c)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(Bq[c][kk]));
+    for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(Bq[kk]));
     asm volatile("" : "+v"(qscale), "+v"(qbar_s), "+v"(qbar2));
   }
 
@@ -385,10 +380,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         k_operands(kcp.x, a0, a1);
         k_operands(kcp.y, a2, a3);
         float4_t c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[0][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[0][1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bq[0][2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[0][3], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bq[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[3], c, 0, 0, 0);
         cq[p] = c;
       }
       // Every lane move below runs with all 64 lanes active and its result
@@ -542,20 +537,23 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       after_reads();
       float E[NPT][4];
+      // with two sets, lane gq's codes (channels of group gq NG / 4) enter
+      // only the product of their group's set
 #pragma unroll
       for (int p = 0; p < NPT; ++p) {
-        half8_t a0, a1, a2, a3;
-        k_operands(kc[p].x, a0, a1);
-        k_operands(kc[p].y, a2, a3);
 #pragma unroll
         for (int r = 0; r < 4; ++r) E[p][r] = 0.f;
 #pragma unroll
         for (int c = 0; c < SETS; ++c) {
+          const uint32_t keep = SETS == 1 ? ~0u : 0u - uint32_t((gq * NG / 4) / NBLK == c);
+          half8_t a0, a1, a2, a3;
+          k_operands(kc[p].x & keep, a0, a1);
+          k_operands(kc[p].y & keep, a2, a3);
           float4_t cc = {0.f, 0.f, 0.f, 0.f};
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[c][0], cc, 0, 0, 0);
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[c][1], cc, 0, 0, 0);
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bq[c][2], cc, 0, 0, 0);
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[c][3], cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[0], cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[1], cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bq[2], cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[3], cc, 0, 0, 0);
           const float qb = c == 0 ? qbar_s : qbar2;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -657,8 +655,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
                                                             __builtin_bit_cast(half8_t, bv),
                                                             cpv[J], 0, 0, 0);
           } else {
-            const u32x4_t bl = {bv[0] & col_lo, bv[1] & col_lo, bv[2] & col_lo, bv[3] & col_lo};
-            const u32x4_t bh = {bv[0] & col_hi, bv[1] & col_hi, bv[2] & col_hi, bv[3] & col_hi};
+            // the code mask of this J, restricted to the lane's output column
+            // half (lane-constant, so no extra operation per dword)
+            const uint32_t ml = mask & col_lo, mh = mask & col_hi;
+            const u32x4_t bl = {d & ml, ds & ml, f & ml, fs & ml};
+            const u32x4_t bh = {d & mh, ds & mh, f & mh, fs & mh};
             cpv[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op(2 * (J >> 2)),
                                                             __builtin_bit_cast(half8_t, bl),
                                                             cpv[J], 0, 0, 0);
@@ -724,10 +725,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       k_operands(kc[p].x, a0, a1);
       k_operands(kc[p].y, a2, a3);
       float4_t c = {0.f, 0.f, 0.f, 0.f};
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[0][0], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[0][1], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bq[0][2], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[0][3], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bq[0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bq[1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bq[2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bq[3], c, 0, 0, 0);
       cq[p] = c;
     }
     float4_t c4 = cq[0];

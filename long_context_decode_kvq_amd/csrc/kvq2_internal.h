@@ -26,12 +26,12 @@ constexpr int kPartialStride = 132;    // floats per (split, query head) partial
                                        // m, l, 2 pad, o'[128]
 constexpr int kQStride = 132;          // floats per rotated query: q'[128], sum(q'),
                                        // f16 scaling exponent, 2 pad
-// u32 words per (b, h) of the QK operand block: up to two column sets of
-// [64 lanes][16 dwords] (a second set when a tile's column blocks cannot
-// hold every quantization group), then [64 lanes][4] lane constants
-// (qscale, then sum(q') over the lane's group in each set, divided by qscale).
-constexpr int kBqSetWords = 64 * 16;
-constexpr int kBqWords = 2 * kBqSetWords + 64 * 4;
+// u32 words per (b, h) of the QK operand block: [64 lanes][16 dwords] of
+// operand, then [64 lanes][4] lane constants (qscale, then the sum of q'
+// over the lane's quantization group in each of up to two column sets,
+// divided by qscale).
+constexpr int kBqOperandWords = 64 * 16;
+constexpr int kBqWords = kBqOperandWords + 64 * 4;
 
 // 16-token chunks per tile of the MFMA decode for head-group width gp (2, 4
 // or 8): the QK tile's 16 columns hold (chunk, f16 hi/lo, head), so a tile
