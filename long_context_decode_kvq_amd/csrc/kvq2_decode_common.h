@@ -475,31 +475,27 @@ __device__ void store_partial(int G, const float (*wm)[GP], const float (*wl)[GP
     }
   }
 }
-
 // Split-K combine of one (b, h), by a work-group of 256 threads in a kernel
 // of its own: the partials in slots [base_slot, base_slot + n_parts) and
 // [tok_slot, tok_slot + n_tok), with M = max m_s, f_s = 2^(m_s - M):
 // o' = sum f_s o'_s / sum f_s l_s, then o = R_V o' to `out`.  The slots are
-// taken in slices of kSlice, all loads of a slice in flight together (the
-// running M, l and o' are rescaled between slices); R_V is loaded first.
+// taken in slices of kSlice (the running M, l and o' are rescaled between
+// slices).  Every load of a slice is issued before any is used, and R_V
+// after the first slice's: the wait for a slice then leaves R_V in flight,
+// so the call's critical path is one round trip to the partials.  The (m, l)
+// of a slice are staged in LDS per head, read back as vectors.
 template <int GP>
 __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slot, int n_parts,
                              int64_t tok_slot, int n_tok) {
   constexpr int kSlice = 16;
   constexpr int KO = (GP * kHeadDim + 255) / 256;   // outputs per thread
-  __shared__ float s_ml[kSlice][GP][2];
+  __shared__ __attribute__((aligned(16))) float s_m[GP][kSlice];
+  __shared__ __attribute__((aligned(16))) float s_l[GP][kSlice];
   __shared__ float ocomb[GP][kHeadDim];
   __shared__ float red[2][GP][kHeadDim];
   const int G = a.group;
   const int tid = threadIdx.x;
   const int ri = tid & (kHeadDim - 1), half = tid >> 7;
-  float4 r[16];
-  {
-    const float4* row = reinterpret_cast<const float4*>(
-        a.R_V + int64_t(h) * kHeadDim * kHeadDim + ri * kHeadDim + 64 * half);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) r[j] = row[j];
-  }
   auto slot_ptr = [&](int i) -> const float* {
     const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
     return a.partials + s * G * kPartialStride;
@@ -516,26 +512,52 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
     acc[k] = 0.f;
   }
   const int n_all = n_parts + n_tok;
-  for (int s0 = 0; s0 < n_all; s0 += kSlice) {
-    const int ns = min(kSlice, n_all - s0);
-    if (tid < ns * G) {
-      const float* p = slot_ptr(s0 + tid / G) + (tid % G) * kPartialStride;
-      s_ml[tid / G][tid % G][0] = p[0];
-      s_ml[tid / G][tid % G][1] = p[1];
-    }
-    float ov[kSlice][KO];
+  float ov[kSlice][KO];
+  float2 ml = {-INFINITY, 0.f};
+  // issue the loads of slice s0 (ns > 0 slots): thread (i, g), i < ns, takes
+  // the (m, l) of slot i, head g
+  auto load_slice = [&](int s0, int ns) {
 #pragma unroll
     for (int i = 0; i < kSlice; ++i) {
       const float* p = slot_ptr(s0 + min(i, ns - 1));   // past the slice: re-read, unused
 #pragma unroll
       for (int k = 0; k < KO; ++k) ov[i][k] = p[gk[k] * kPartialStride + 4 + ck[k]];
     }
+    if (tid < ns * G)
+      ml = *reinterpret_cast<const float2*>(slot_ptr(s0 + tid / G) + (tid % G) * kPartialStride);
+  };
+  if (n_all > 0) load_slice(0, min(kSlice, n_all));
+  // keep R_V's loads behind the slice's in issue order
+  asm volatile("" ::: "memory");
+  float4 r[16];
+  {
+    const float4* row = reinterpret_cast<const float4*>(
+        a.R_V + int64_t(h) * kHeadDim * kHeadDim + ri * kHeadDim + 64 * half);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = row[j];
+  }
+  for (int s0 = 0; s0 < n_all; s0 += kSlice) {
+    const int ns = min(kSlice, n_all - s0);
+    if (s0 > 0) load_slice(s0, ns);
+    if (tid < ns * G) {
+      s_m[tid % G][tid / G] = ml.x;
+      s_l[tid % G][tid / G] = ml.y;
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KO; ++k) {
       const int g = gk[k];
+      float mv[kSlice], lv[kSlice];
+#pragma unroll
+      for (int i = 0; i < kSlice; i += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&s_m[g][i]);
+        const float4 y = *reinterpret_cast<const float4*>(&s_l[g][i]);
+        mv[i] = x.x; mv[i + 1] = x.y; mv[i + 2] = x.z; mv[i + 3] = x.w;
+        lv[i] = y.x; lv[i + 1] = y.y; lv[i + 2] = y.z; lv[i + 3] = y.w;
+      }
       float mx = -INFINITY;
-      for (int i = 0; i < ns; ++i) mx = fmaxf(mx, s_ml[i][g][0]);
+#pragma unroll
+      for (int i = 0; i < kSlice; ++i) mx = i < ns ? fmaxf(mx, mv[i]) : mx;
       const float nM = fmaxf(M[k], mx);
       if (nM != -INFINITY) {
         const float sc = M[k] == -INFINITY ? 0.f : exp2f(M[k] - nM);
@@ -543,17 +565,14 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
         den[k] *= sc;
 #pragma unroll
         for (int i = 0; i < kSlice; ++i) {
-          if (i < ns) {
-            const float mi = s_ml[i][g][0];
-            const float f = mi == -INFINITY ? 0.f : exp2f(mi - nM);
-            acc[k] = fmaf(f, ov[i][k], acc[k]);
-            den[k] = fmaf(f, s_ml[i][g][1], den[k]);
-          }
+          const float f = (i >= ns || mv[i] == -INFINITY) ? 0.f : exp2f(mv[i] - nM);
+          acc[k] = fmaf(f, ov[i][k], acc[k]);
+          den[k] = fmaf(f, lv[i], den[k]);
         }
         M[k] = nM;
       }
     }
-    __syncthreads();   // s_ml is refilled by the next slice
+    __syncthreads();   // s_m, s_l are refilled by the next slice
   }
 #pragma unroll
   for (int k = 0; k < KO; ++k) {
@@ -593,7 +612,8 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
 // o = R_V o' to `out`.  Thread (part, c) takes channel c of the slots of its
 // part of each round (kRound slots per part, all loads in flight together;
 // the (m, l) of a round are staged in LDS once), and the NQ parts merge in
-// LDS; R_V row c is loaded first, 128 / NQ columns per thread.  With NQ = 8
+// LDS; R_V row c, 128 / NQ columns per thread, is loaded right after the
+// first round, so that the wait for the round leaves it in flight.  With NQ = 8
 // a round covers 128 slots: the split count of a batch-1 decode (about 70)
 // takes one round of dependent loads instead of three.
 template <int GP, int NQ>
@@ -608,6 +628,25 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
   const int G = a.group;
   const int tid = threadIdx.x;
   const int c = tid & (kHeadDim - 1), part = tid >> 7;
+  auto slot_ptr = [&](int i) -> const float* {
+    const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    return a.partials + (s * G + g) * kPartialStride;
+  };
+  const int n_all = n_parts + n_tok;
+  float ov[kRound];
+  float mlv = 0.f;
+  // issue the loads of round s0 (ns > 0 slots)
+  auto load_round = [&](int s0, int ns) {
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+      const int i = part * kRound + k;
+      ov[k] = slot_ptr(s0 + min(i, ns - 1))[4 + c];   // past the round: re-read, unused
+    }
+    if (tid < 2 * ns) mlv = slot_ptr(s0 + (tid >> 1))[tid & 1];
+  };
+  if (n_all > 0) load_round(0, min(NQ * kRound, n_all));
+  // keep R_V's loads behind the first round's in issue order
+  asm volatile("" ::: "memory");
   float4 r[kCols / 4];
   {
     const float4* row = reinterpret_cast<const float4*>(
@@ -615,24 +654,11 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
 #pragma unroll
     for (int j = 0; j < kCols / 4; ++j) r[j] = row[j];
   }
-  auto slot_ptr = [&](int i) -> const float* {
-    const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
-    return a.partials + (s * G + g) * kPartialStride;
-  };
-  const int n_all = n_parts + n_tok;
   float M = -INFINITY, den = 0.f, acc = 0.f;
   for (int s0 = 0; s0 < n_all; s0 += NQ * kRound) {
     const int ns = min(NQ * kRound, n_all - s0);
-    if (tid < 2 * ns) {
-      const float* p = slot_ptr(s0 + (tid >> 1));
-      s_ml[tid >> 1][tid & 1] = p[tid & 1];
-    }
-    float ov[kRound];
-#pragma unroll
-    for (int k = 0; k < kRound; ++k) {
-      const int i = part * kRound + k;
-      ov[k] = slot_ptr(s0 + min(i, ns - 1))[4 + c];   // past the round: re-read, unused
-    }
+    if (s0 > 0) load_round(s0, ns);
+    if (tid < 2 * ns) s_ml[tid >> 1][tid & 1] = mlv;
     __syncthreads();
     float mx = -INFINITY;
 #pragma unroll
