@@ -535,6 +535,9 @@ def main():
                          "(quaternion product codebook, Med3x fp16 chunks) on the same shape")
     ap.add_argument("--hqmq-secondary", type=int, default=10,
                     help="secondary quaternions S of the HQMQ codebook (24 S words)")
+    ap.add_argument("--prefix-aware", action="store_true",
+                    help="decode a workload with a shared prefix through "
+                         "kvq_decode_prefix_attention (the sharers as one group)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the read-ceiling probes")
     ap.add_argument("--no-graph", action="store_true",
@@ -594,8 +597,21 @@ def main():
                                         dc.recent, dc.block_table) for p in pools[1:]]
 
     max_len = int(lens_before.max()) + n_steps * M
-    ws = torch.zeros(kvq2.decode_multi_workspace_bytes(kd, w.batch, max_len, M),
-                     dtype=torch.uint8, device=device)
+    # --prefix-aware: the sequences sharing the prefix pages form one group
+    _, _, sharers = W.page_assignment(w, lens_before + n_steps * M)
+    prefix = args.prefix_aware and bool(w.shared_prefix) and M == 1 and ng == 1
+    if args.prefix_aware and not prefix:
+        raise SystemExit("--prefix-aware needs a workload with a shared prefix, one query per "
+                         "sequence and 128-channel quantization groups")
+    groups = group_tensors = None
+    if prefix:
+        group_tensors = [torch.tensor(x, dtype=torch.int32, device=device)
+                         for x in ([0, len(sharers)], sharers, [w.shared_prefix])]
+        groups = kvq2.prefix_groups(len(sharers), *group_tensors)
+        ws_bytes = kvq2.decode_prefix_workspace_bytes(kd, w.batch, max_len, groups)
+    else:
+        ws_bytes = kvq2.decode_multi_workspace_bytes(kd, w.batch, max_len, M)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device)
     out = torch.empty((w.batch, M, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=device)
     cu1 = torch.arange(w.batch + 1, dtype=torch.int32, device=device) * M
     starts = [torch.from_numpy((lens_before + k * M).astype(np.int32)).to(device)
@@ -615,14 +631,16 @@ def main():
     stream = torch.cuda.current_stream()
 
     def decode_call(h, seq, q, st):
-        if M == 1:
+        if prefix:
+            kvq2.decode_prefix_attention(kd, lay, h, w.batch, seq, max_len, q, out, groups, ws, st)
+        elif M == 1:
             kvq2.decode_attention(kd, lay, h, w.batch, seq, max_len, q, out, ws, st)
         else:
             kvq2.decode_multi_attention(kd, lay, h, w.batch, seq, max_len, M, q, out, ws, st)
 
     def step(k, st):
         h = handles[k % copies]
-        if M > 1:
+        if M > 1 or prefix:
             kvq2.quantize_append(kd, lay, h, w.batch, starts[k], cu1, w.batch * M, M, k_new[k],
                                  v_new[k], st)
             decode_call(h, seqs[k], qs[k], st)
@@ -713,9 +731,9 @@ def main():
     dec_bytes = decode_bytes(w, lens_before + (last + 1) * M, M, ng)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     # A shared prefix is read by every sharer (its pages are then mostly
-    # served from the Infinity Cache): achieved counts the bytes every
-    # sequence reads, unique counts each physical page once.
-    _, _, sharers = W.page_assignment(w, lens_before + n_steps * M)
+    # served from the Infinity Cache) unless the decode is prefix-aware
+    # (then once per row set of four sharers): achieved counts the bytes
+    # every sequence attends to, unique counts each physical page once.
     dec_unique = dec_bytes - shared_prefix_repeat_bytes(w, sharers, ng)
     log(f"[bench] pre-warm {n_pre} decode calls in {prewarm_wall:.2f}s; step "
         f"{ms_per_step * 1e3:.1f} us; decode {dec_avg_ms * 1e3:.1f} us (p10 {pct[10]:.1f}, "
@@ -764,7 +782,8 @@ def main():
             "page_size": w.page_size, "n_sink": w.n_sink, "n_recent": w.n_recent,
             "layers": 1, "decode_kernel": kernel, "pool_copies": copies,
             "quant_group": qg or HEAD_DIM,
-            "step_call": ("kvq_quantize_append + kvq_decode_multi_attention" if M > 1 else
+            "step_call": ("kvq_quantize_append + kvq_decode_prefix_attention" if prefix else
+                          "kvq_quantize_append + kvq_decode_multi_attention" if M > 1 else
                           "kvq_quantize_append + kvq_decode_attention" if args.two_calls
                           else "kvq_decode_step"),
             "launch": ("host loop" if graph is None
@@ -799,7 +818,11 @@ def main():
             "decode_unique_bytes": int(dec_unique),
             "decode_unique_gbs": round(dec_unique / (dec_avg_ms * 1e-3) / 1e9, 1),
             "decode_effective_gbs": round(achieved, 1),
-            "note": "every sharer reads the shared prefix pages; unique counts each page once",
+            "prefix_aware": prefix,
+            "note": ("the sharers form one group of kvq_decode_prefix_attention: the prefix "
+                     "tiles are read once per row set of four sharers" if prefix else
+                     "every sharer reads the shared prefix pages") +
+                    "; effective counts what every sequence attends to, unique each page once",
         },
         "cpu_baseline": cpu,
     }

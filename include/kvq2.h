@@ -262,6 +262,64 @@ int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * Shared-prefix groups of a batch (prefix caching; OSCAR summary sec. 2.2-B
+ * and sec. 3: the fused kernel works with paged attention and prefix
+ * caching).  Group j lists the member sequences
+ * members[member_start[j] .. member_start[j + 1]) whose positions
+ * [0, prefix_len[j]) lie on the same physical pages (equal block-table
+ * entries, pages written once and read-only afterwards).  All arrays are
+ * device int32:
+ *   member_start [n_groups + 1], non-decreasing, member_start[0] = 0 and
+ *                member_start[n_groups] = n_members
+ *   members      [n_members] sequence indices in [0, batch); a sequence
+ *                listed more than once counts as a member of its first
+ *                listing only
+ *   prefix_len   [n_groups] tokens, >= 0
+ * n_groups (0 .. 256) and n_members (0 .. 2^24) are host values.
+ */
+typedef struct kvq_prefix_groups {
+  int32_t n_groups;
+  int32_t n_members;
+  const int32_t* member_start;
+  const int32_t* members;
+  const int32_t* prefix_len;
+} kvq_prefix_groups;
+
+/*
+ * kvq_decode_attention with shared prefixes read once per group of four
+ * member sequences instead of once per member.  Same arguments, validation
+ * and results as kvq_decode_attention (up to the rounding of a different
+ * split order), plus the groups.  The INT2 tiles of a member that lie
+ * wholly inside its group's prefix are read by the group: each tile is
+ * brought into LDS once and attended by up to four members' query rows (one
+ * wave each); the rest of the member's cache is decoded as usual and the two
+ * parts meet in the split-K combine.  A member whose whole INT2 tiles do not
+ * cover the group's prefix (seq_len - n_recent too short) is decoded on its
+ * own, as is every sequence when the matrix-core decode does not take the
+ * shape (more than 8 query heads per KV head, or quantization groups
+ * narrower than 128 channels).
+ *   groups     host pointer; groups->n_groups = 0 is a plain decode
+ *   workspace  kvq_decode_prefix_workspace_bytes(dims, batch, max_seq_len,
+ *              groups) bytes, zero-filled once, reusable as for
+ *              kvq_decode_attention (for groups of the same or smaller
+ *              n_groups and n_members)
+ * Returns KVQ_ERR_ARG for a null groups, n_groups outside 0..256,
+ * n_members outside 0..2^24, or null arrays when n_groups > 0, and
+ * KVQ_ERR_UNSUPPORTED when the batch's and the groups' tiles together
+ * exceed the decode's 32-bit tile counters.
+ */
+size_t kvq_decode_prefix_workspace_bytes(const kvq_dims* dims, int32_t batch,
+                                         int32_t max_seq_len,
+                                         const kvq_prefix_groups* groups);
+int kvq_decode_prefix_attention(const kvq_dims* dims, const kvq_layer* layer,
+                                const kvq_cache* cache, int32_t batch,
+                                const int32_t* seq_len, int32_t max_seq_len,
+                                const uint16_t* q, float* out,
+                                const kvq_prefix_groups* groups,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Human-readable name of a kvq_status value (static storage). */
 const char* kvq_status_string(int status);
 

@@ -4,6 +4,7 @@
 // q-rotation / range-plan pre-pass (fused with the decode-step append for
 // kvq_decode_step) and then the selected decode kernel.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <mutex>
 
@@ -19,7 +20,106 @@ struct PlanLds {
   int scan[256];
   int carry;
   int rs[kChainGroups + 1];
+  // shared-prefix groups
+  int gs[kMaxPrefixGroups + 1];    // member starts (clamped)
+  int gskip[kMaxPrefixGroups];     // whole prefix tiles
+  int gvalid[kMaxPrefixGroups];    // some member is valid
+  int grep[kMaxPrefixGroups];      // first valid member index, then its sequence
+  int grs[kMaxPrefixGroups + 1];   // virtual tiles of earlier groups' items
+  int gib[kMaxPrefixGroups + 1];   // first item
+  int gw[kMaxPrefixGroups];        // virtual tiles per item
 };
+
+// Shared-prefix groups, by the plan's work-group: the valid members (a
+// sequence's first listing, whose whole INT2 tiles cover its group's prefix
+// tiles), the tiles they skip, and each group's row-set items (grp_info
+// rows, with LDS copies for the cut).  Values that other threads wrote are
+// read back with agent-scope loads.
+template <int GP>
+__device__ void plan_groups(const DecodeArgs& a, PlanLds& P) {
+  constexpr int npt = chunks_per_tile(GP);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int ngr = a.n_groups, B = a.batch, Hkv = a.n_kv_heads;
+  const int cf = (a.n_sink + kChunkTokens - 1) / kChunkTokens;
+  for (int g = tid; g <= ngr; g += nt) {
+    P.gs[g] = a.member_start[g];
+    if (g < ngr) {
+      // tiles of the group's prefix: whole tiles from the first whole chunk
+      const int pc = max(a.prefix_len[g], 0) / kChunkTokens;
+      P.gskip[g] = pc > cf ? (pc - cf) / npt : 0;
+      P.gvalid[g] = 0;
+      P.grep[g] = INT_MAX;
+    }
+  }
+  for (int b = tid; b < B; b += nt) {
+    a.seq_member[b] = INT_MAX;
+    a.seq_skip[b] = 0;
+    a.seq_group[b] = -1;
+  }
+  __syncthreads();
+  if (tid == 0) {   // member starts non-decreasing within [0, n_members]
+    int prev = 0;
+    for (int g = 0; g <= ngr; ++g) {
+      prev = g == 0 ? 0 : min(max(P.gs[g], prev), a.n_members);
+      P.gs[g] = prev;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  const int nm = P.gs[ngr];
+  for (int m = tid; m < nm; m += nt) {   // first listing of every sequence
+    const int b = a.members[m];
+    if (b >= 0 && b < B) atomicMin(&a.seq_member[b], m);
+  }
+  __threadfence();
+  __syncthreads();
+  for (int m = tid; m < nm; m += nt) {
+    const int b = a.members[m];
+    if (b < 0 || b >= B || load_agent(&a.seq_member[b]) != m) continue;
+    int lo = 0, hi = ngr;   // group of m: the largest g with gs[g] <= m
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.gs[mid] <= m) lo = mid; else hi = mid;
+    }
+    const int skip = P.gskip[lo];
+    const Int2Range rg = int2_range(a, a.seq_len[b], npt);
+    if (skip > 0 && (rg.cl - rg.cf) / npt >= skip) {
+      a.seq_skip[b] = skip;
+      a.seq_group[b] = lo;
+      atomicMin(&P.grep[lo], m);
+      P.gvalid[lo] = 1;
+    }
+  }
+  __syncthreads();
+  for (int g = tid; g < ngr; g += nt) P.grep[g] = P.gvalid[g] ? a.members[P.grep[g]] : 0;
+  __syncthreads();
+  if (tid == 0) {
+    int rs = 0, ib = 0;
+    for (int g = 0; g < ngr; ++g) {
+      const int rows = (P.gs[g + 1] - P.gs[g] + 3) / 4;
+      const int skip = P.gvalid[g] ? P.gskip[g] : 0;
+      const int w = max(1, a.rs_cost * skip) + a.piece_cost;
+      P.grs[g] = rs;
+      P.gib[g] = ib;
+      P.gw[g] = w;
+      int32_t* gi = a.grp_info + g * kGrpInfo;
+      gi[kGiRsPrefix] = rs;
+      gi[kGiWidth] = w;
+      gi[kGiSkip] = skip;
+      gi[kGiRep] = P.grep[g];
+      gi[kGiRowSets] = rows;
+      gi[kGiItemBase] = ib;
+      gi[kGiMemberStart] = P.gs[g];
+      gi[kGiMemberEnd] = P.gs[g + 1];
+      rs += Hkv * rows * w;
+      ib += Hkv * rows;
+    }
+    P.grs[ngr] = rs;
+    P.gib[ngr] = ib;
+  }
+  __threadfence();
+  __syncthreads();
+}
 template <int KG>
 struct PrologueLds {
   float qs[KG][kHeadDim];           // q, then q'
@@ -38,6 +138,7 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   // over blocks of 256 sequences).
   int* scan = P.scan;
   int& carry = P.carry;
+  if (a.n_groups > 0) plan_groups<GP>(a, P);
   if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
   __syncthreads();
   for (int base = 0; base < a.batch; base += 256) {
@@ -45,7 +146,8 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
     int w = 0;
     if (bb < a.batch) {
       const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
-      w = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
+      const int skip = a.n_groups > 0 ? load_agent(&a.seq_skip[bb]) : 0;
+      w = max(1, (rg.cl - rg.cf) / npt - skip) + a.piece_cost;
     }
     scan[tid] = w;
     __syncthreads();
@@ -66,7 +168,9 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   int* rs = P.rs;
   const int nwg = a.chain_groups;
   const int Hkv = a.n_kv_heads;
-  const int64_t total = int64_t(Hkv) * carry;
+  // the (b, h) pieces, then the row-set items of shared-prefix groups
+  const int64_t pairs_total = int64_t(Hkv) * carry;
+  const int64_t total = pairs_total + (a.n_groups > 0 ? P.grs[a.n_groups] : 0);
   const int rsz = a.round_size, rounds = rsz > 0 ? nwg / rsz : 0;
   const bool weighted = rsz > 0 && rsz % 8 == 0 && rounds >= 2 && rounds <= 4 &&
                         rounds * rsz == nwg && total >= 4 * int64_t(nwg);
@@ -127,10 +231,25 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   for (int pr = tid; pr < a.batch * Hkv; pr += blockDim.x) {
     const int bb = pr / Hkv, hh = pr % Hkv;
     const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
-    const int wbb = max(1, (rg.cl - rg.cf) / npt) + a.piece_cost;
+    const int skip = a.n_groups > 0 ? load_agent(&a.seq_skip[bb]) : 0;
+    const int wbb = max(1, (rg.cl - rg.cf) / npt - skip) + a.piece_cost;
     // the prefix of bb, recomputed from the scan output in global memory
     const int sp = Hkv * a.tile_prefix[bb] + hh * wbb;
     a.pair_range[pr] = range_of(sp) | (range_of(sp + wbb - 1) << 16);
+  }
+  // first and last range of every row-set item
+  if (a.n_groups > 0) {
+    const int ngr = a.n_groups;
+    for (int q = tid; q < P.gib[ngr]; q += blockDim.x) {
+      int lo = 0, hi = ngr;   // group of item q: the largest g with gib[g] <= q
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (P.gib[mid] <= q) lo = mid; else hi = mid;
+      }
+      const int64_t sq = pairs_total + P.grs[lo] + int64_t(q - P.gib[lo]) * P.gw[lo];
+      a.item_range[q] = range_of(static_cast<int>(sq)) |
+                        (range_of(static_cast<int>(sq + P.gw[lo] - 1)) << 16);
+    }
   }
 }
 
@@ -376,7 +495,8 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
                             const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
                             const uint16_t* q, float* out, void* workspace,
                             const DecodePlan& plan, DecodeKernel which, int32_t n_query,
-                            int32_t query_base, int32_t query_count) {
+                            int32_t query_base, int32_t query_count,
+                            const kvq_prefix_groups* groups) {
   DecodeArgs a{};
   a.R_K = layer.R_K;
   a.R_V = layer.R_V;
@@ -423,8 +543,25 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
     a.pair_range = reinterpret_cast<int32_t*>(pre + r256((size_t(batch) + 1) * sizeof(int32_t)) +
                                               r256((size_t(kChainGroups) + 1) * sizeof(int32_t)));
   }
-  a.partials = reinterpret_cast<float*>(ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes +
-                                        plan.prefix_bytes);
+  char* grp = ws + plan.ticket_bytes + plan.qrot_bytes + plan.bq_bytes + plan.prefix_bytes;
+  a.partials = reinterpret_cast<float*>(grp + plan.group_bytes);
+  if (plan.n_groups > 0 && groups != nullptr) {
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t bb = r256(size_t(batch) * sizeof(int32_t));
+    a.n_groups = plan.n_groups;
+    a.n_members = plan.n_members;
+    a.rs_cost = plan.rs_cost;
+    a.member_start = groups->member_start;
+    a.members = groups->members;
+    a.prefix_len = groups->prefix_len;
+    a.seq_skip = reinterpret_cast<int32_t*>(grp);
+    a.seq_member = reinterpret_cast<int32_t*>(grp + bb);
+    a.seq_group = reinterpret_cast<int32_t*>(grp + 2 * bb);
+    a.grp_info = reinterpret_cast<int32_t*>(grp + 3 * bb);
+    a.item_range = reinterpret_cast<int32_t*>(
+        grp + 3 * bb + r256(size_t(plan.n_groups) * kGrpInfo * sizeof(int32_t)));
+    a.rs_slot0 = plan.rs_slot0;
+  }
   const int G = a.group;
   // the matrix-core kernel takes narrower quantization groups for up to four
   // rows per (b, h)
@@ -444,9 +581,9 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                   const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
                   int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
                   const DecodePlan& plan, DecodeKernel which, void* stream, int32_t n_query,
-                  int32_t query_base, int32_t query_count) {
+                  int32_t query_base, int32_t query_count, const kvq_prefix_groups* groups) {
   DecodeArgs a = make_decode_args(d, sm_scale, layer, cache, batch, seq_len, q, out, workspace,
-                                  plan, which, n_query, query_base, query_count);
+                                  plan, which, n_query, query_base, query_count, groups);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
   const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch);
@@ -468,7 +605,7 @@ int launch_decode_step(const kvq_dims& d, float sm_scale, const kvq_layer& layer
                        const uint16_t* q, float* out, void* workspace, const DecodePlan& plan,
                        void* stream) {
   DecodeArgs a = make_decode_args(d, sm_scale, layer, cache, batch, seq_len, q, out, workspace,
-                                  plan, kDecodeMfma, 1, 0, 1);
+                                  plan, kDecodeMfma, 1, 0, 1, nullptr);
   const AppendArgs aa = make_append_args(d, layer, cache, batch, start_pos, cu_new, total_new,
                                          k_new, v_new);
   if (a.gp == 0 || aa.tokens_per_block != kWaves) return -1;   // not a fused-step shape

@@ -82,7 +82,35 @@ struct DecodeArgs {
   // tok_slot0 + (b Hkv + h) n_tok_slices + z, and the combine takes them in.
   int n_tok_slices;
   int64_t tok_slot0;
+  // MFMA decode with shared-prefix groups (n_groups > 0): the caller's
+  // groups, and the pre-pass's resolution of them.  A valid member b of
+  // group j skips its first seq_skip[b] INT2 tiles, which the group's
+  // row-set items read for up to four members at once; their partials are
+  // in slots rs_slot0 + 4 (range + item) + member % 4.
+  int n_groups;
+  int n_members;
+  int rs_cost;                 // virtual tiles per row-set tile
+  const int32_t* member_start; // [n_groups + 1]
+  const int32_t* members;      // [n_members]
+  const int32_t* prefix_len;   // [n_groups]
+  int32_t* seq_skip;           // [B] tiles read by the member's group (0: none)
+  int32_t* seq_member;         // [B] first member index listing b
+  int32_t* seq_group;          // [B] group of a valid member, else -1
+  int32_t* grp_info;           // [n_groups][kGrpInfo]
+  int32_t* item_range;         // per row-set item: first | last range << 16
+  int64_t rs_slot0;
 };
+
+// Row of grp_info per shared-prefix group (kGrpInfo ints, written by the
+// pre-pass).
+constexpr int kGiRsPrefix = 0;     // virtual tiles of the row-set items of earlier groups
+constexpr int kGiWidth = 1;        // virtual tiles per item of this group
+constexpr int kGiSkip = 2;         // prefix tiles (0 when no member is valid)
+constexpr int kGiRep = 3;          // representative sequence (a valid member, else 0)
+constexpr int kGiRowSets = 4;      // row sets (of four members) per KV head
+constexpr int kGiItemBase = 5;     // index of the group's first item
+constexpr int kGiMemberStart = 6;  // member range, clamped
+constexpr int kGiMemberEnd = 7;
 
 // INT2 work of a sequence of length L is split in two parts:
 //  * whole tiles of `npt` fully valid 16-token chunks [cf, cl), streamed in
@@ -475,6 +503,40 @@ __device__ void store_partial(int G, const float (*wm)[GP], const float (*wl)[GP
     }
   }
 }
+// The four waves' partials of a row-set piece, each for its own member's
+// query rows: wave w's G rows go to the slot after wave w - 1's.
+template <int GP>
+__device__ void store_wave_partials(int G, const float (*wm)[GP], const float (*wl)[GP],
+                                    const float (*wo)[GP][kHeadDim], float* part) {
+  for (int i = threadIdx.x; i < 4 * G * kHeadDim; i += blockDim.x) {
+    const int w = i / (G * kHeadDim), r = i % (G * kHeadDim);
+    const int g = r / kHeadDim, c = r % kHeadDim;
+    float* pw = part + (w * G + g) * kPartialStride;
+    pw[4 + c] = wo[w][g][c];
+    if (c == 0) {
+      pw[0] = wm[w][g];
+      pw[1] = wl[w][g];
+    }
+  }
+}
+
+// The row-set partials of (b, h) in a shared-prefix decode: returns their
+// count and sets `first` to the first one's slot (the others follow four
+// slots apart); 0 when b reads its whole cache itself.
+__device__ __forceinline__ int rowset_slots(const DecodeArgs& a, int b, int h, int64_t& first) {
+  first = 0;
+  if (a.n_groups <= 0) return 0;
+  const int gidx = a.seq_group[b];
+  if (gidx < 0) return 0;
+  const int32_t* gi = a.grp_info + int64_t(gidx) * kGrpInfo;
+  const int m = a.seq_member[b] - gi[kGiMemberStart];
+  const int64_t q = gi[kGiItemBase] + int64_t(h) * gi[kGiRowSets] + m / 4;
+  const int ir = a.item_range[q];
+  const int i0 = ir & 0xFFFF, i1 = ir >> 16;
+  first = a.rs_slot0 + (int64_t(i0) + q) * 4 + m % 4;
+  return i1 - i0 + 1;
+}
+
 // Split-K combine of one (b, h), by a work-group of 256 threads in a kernel
 // of its own: the partials in slots [base_slot, base_slot + n_parts) and
 // [tok_slot, tok_slot + n_tok), with M = max m_s, f_s = 2^(m_s - M):
@@ -484,9 +546,9 @@ __device__ void store_partial(int G, const float (*wm)[GP], const float (*wl)[GP
 // after the first slice's: the wait for a slice then leaves R_V in flight,
 // so the call's critical path is one round trip to the partials.  The (m, l)
 // of a slice are staged in LDS per head, read back as vectors.
-template <int GP>
+template <int GP, bool RSL = false>
 __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slot, int n_parts,
-                             int64_t tok_slot, int n_tok) {
+                             int64_t tok_slot, int n_tok, int64_t rs_slot = 0, int n_rs = 0) {
   constexpr int kSlice = 16;
   constexpr int KO = (GP * kHeadDim + 255) / 256;   // outputs per thread
   __shared__ __attribute__((aligned(16))) float s_m[GP][kSlice];
@@ -497,7 +559,8 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   const int tid = threadIdx.x;
   const int ri = tid & (kHeadDim - 1), half = tid >> 7;
   auto slot_ptr = [&](int i) -> const float* {
-    const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    if constexpr (RSL) s = i < n_parts + n_tok ? s : rs_slot + 4 * int64_t(i - n_parts - n_tok);
     return a.partials + s * G * kPartialStride;
   };
   int gk[KO], ck[KO];
@@ -511,7 +574,7 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
     den[k] = 0.f;
     acc[k] = 0.f;
   }
-  const int n_all = n_parts + n_tok;
+  const int n_all = n_parts + n_tok + (RSL ? n_rs : 0);
   float ov[kSlice][KO];
   float2 ml = {-INFINITY, 0.f};
   // issue the loads of slice s0 (ns > 0 slots): thread (i, g), i < ns, takes
@@ -616,9 +679,10 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
 // first round, so that the wait for the round leaves it in flight.  With NQ = 8
 // a round covers 128 slots: the split count of a batch-1 decode (about 70)
 // takes one round of dependent loads instead of three.
-template <int GP, int NQ>
+template <int GP, int NQ, bool RSL = false>
 __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t base_slot,
-                             int n_parts, int64_t tok_slot, int n_tok) {
+                             int n_parts, int64_t tok_slot, int n_tok, int64_t rs_slot = 0,
+                             int n_rs = 0) {
   constexpr int kRound = 16;              // slots per part per round
   constexpr int kCols = kHeadDim / NQ;    // R_V columns per thread
   __shared__ float s_ml[NQ * kRound][2];
@@ -629,10 +693,11 @@ __device__ void combine_head(const DecodeArgs& a, int b, int h, int g, int64_t b
   const int tid = threadIdx.x;
   const int c = tid & (kHeadDim - 1), part = tid >> 7;
   auto slot_ptr = [&](int i) -> const float* {
-    const int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
+    if constexpr (RSL) s = i < n_parts + n_tok ? s : rs_slot + 4 * int64_t(i - n_parts - n_tok);
     return a.partials + (s * G + g) * kPartialStride;
   };
-  const int n_all = n_parts + n_tok;
+  const int n_all = n_parts + n_tok + (RSL ? n_rs : 0);
   float ov[kRound];
   float mlv = 0.f;
   // issue the loads of round s0 (ns > 0 slots)

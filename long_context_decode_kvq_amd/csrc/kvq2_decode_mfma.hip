@@ -1,7 +1,9 @@
 // Launch side of the matrix-core decode (kernels in kvq2_decode_mfma_kernels.h):
 // the per-device launch geometry, the range cut's weights and the launches.
 // The kernels of quantization groups narrower than the head are built in
-// kvq2_decode_mfma_groups.hip (a separate code object).
+// kvq2_decode_mfma_groups.hip, those of eight query heads per KV head in
+// kvq2_decode_mfma_g8.hip and those of decodes with shared-prefix groups in
+// kvq2_decode_mfma_prefix.hip (separate code objects).
 #include <algorithm>
 #include <mutex>
 
@@ -13,6 +15,11 @@ int launch_decode_valu(const DecodeArgs& a, int batch, void* stream);
 // kvq2_decode_mfma_groups.hip: the kernels of narrower quantization groups
 int decode_mfma_groups_per_cu(int gp, int ng);
 int launch_decode_mfma_groups(const DecodeArgs& a, unsigned grid, void* stream);
+// kvq2_decode_mfma_g8.hip: the kernels of eight query heads per KV head
+int decode_mfma_g8_per_cu();
+void launch_decode_mfma_g8(const DecodeArgs& a, unsigned grid, bool per_head, void* stream);
+// kvq2_decode_mfma_prefix.hip: the kernels of decodes with shared-prefix groups
+void launch_decode_mfma_prefix(const DecodeArgs& a, unsigned grid, bool per_head, void* stream);
 
 // Group sizes up to 8 run on the matrix cores; 9..16 query heads per KV head
 // (two MFMA row blocks of hi/lo would not fit 16 rows) use the VALU kernel.
@@ -56,7 +63,7 @@ const DeviceGeometry& device_geometry() {
     g.per_cu[1][0] = kernel_per_cu<4, 1>();
     g.per_cu[1][1] = decode_mfma_groups_per_cu(4, 2);
     g.per_cu[1][2] = decode_mfma_groups_per_cu(4, 4);
-    g.per_cu[2][0] = g.per_cu[2][1] = g.per_cu[2][2] = kernel_per_cu<8, 1>();
+    g.per_cu[2][0] = g.per_cu[2][1] = g.per_cu[2][2] = decode_mfma_g8_per_cu();
     cached[dev] = g;
   });
   return cached[dev];
@@ -131,7 +138,9 @@ int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* st
   const bool per_head = 2 * a.batch * a.n_kv_heads < std::max(1, device_cus());
   const dim3 cgrid(a.n_kv_heads, a.batch, per_head ? a.group : 1);
   const dim3 cblock(per_head ? 128 * kHeadCombineParts : 256);
-  if (G <= 2) {
+  if (a.n_groups > 0) {
+    launch_decode_mfma_prefix(a, grid.x, per_head, stream);
+  } else if (G <= 2) {
     if (a.ng == 1) hipLaunchKernelGGL((decode_mfma_kernel<2, 1>), grid, dim3(256), 0, st, a);
     else launch_decode_mfma_groups(a, grid.x, stream);
     if (per_head) hipLaunchKernelGGL(combine_head_kernel<2>, cgrid, cblock, 0, st, a);
@@ -142,9 +151,7 @@ int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* st
     if (per_head) hipLaunchKernelGGL(combine_head_kernel<4>, cgrid, cblock, 0, st, a);
     else hipLaunchKernelGGL(combine_kernel<4>, cgrid, cblock, 0, st, a);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<8, 1>), grid, dim3(256), 0, st, a);
-    if (per_head) hipLaunchKernelGGL(combine_head_kernel<8>, cgrid, cblock, 0, st, a);
-    else hipLaunchKernelGGL(combine_kernel<8>, cgrid, cblock, 0, st, a);
+    launch_decode_mfma_g8(a, grid.x, per_head, stream);
   }
   return static_cast<int>(hipGetLastError());
 }

@@ -30,6 +30,7 @@
 #pragma once
 
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "kvq2_decode_common.h"
@@ -177,30 +178,52 @@ __device__ __forceinline__ float (*wave_o())[GP][kHeadDim] {
 // load's destination must not share a register with an address that a later
 // load of the block still reads.
 // M0 holds the LDS destination; lane i writes size bytes at M0 + size * i.
-// The loads carry the non-temporal hint: every chunk is read once, and on
+// The loads carry the non-temporal hint (NT) when a chunk is read once: on
 // the MI355X the scattered 1152-byte chunk pattern streams at ~6.55 TB/s
 // with it against ~5.85 TB/s without (global->LDS probe, 2.1 GB of chunks).
+// Chunks that several waves read at about the same time (a shared prefix's
+// row sets) are loaded without it, so that the L2 serves all but the first.
 
 // 16 bytes per lane from sbase + voff.
+template <bool NT = true>
 __device__ __forceinline__ void dma_x4(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1 nt"
-      :
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory", "m0");
 }
 
 // 4 bytes per lane from a per-lane address.
+template <bool NT = true>
 __device__ __forceinline__ void dma_x1(const uint8_t* vaddr, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, off nt"
-      :
-      : "v"(vaddr), "s"(lds)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, off nt"
+        :
+        : "v"(vaddr), "s"(lds)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, off"
+        :
+        : "v"(vaddr), "s"(lds)
+        : "memory", "m0");
 }
 
 template <int N>
@@ -210,12 +233,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One piece of (b, h): the INT2 tiles [t_lo, t_hi) of its range of W_b
 // virtual tiles (the first piece_cost of them stand for no tile; the rest
-// are clipped to the tiles the sequence has).  Leaves its partial in slot
-// part_slot for the combine kernel.
-template <int GP, int NG>
+// are clipped to the tiles the sequence has, past its first `skip` tiles,
+// which a shared-prefix group reads).  Leaves its partial in slot part_slot
+// for the combine kernel.
+//
+// Row-set mode (RS): a piece of a shared-prefix group's item.  The tiles
+// are the group's first `skip` tiles of sequence b (any member: they share
+// those pages), reached through virtual offsets of rs_cost per tile; every
+// wave takes every tile, for the query rows of its own member sequence bq_b,
+// and leaves its own partial in slot part_slot + wave.  The four waves
+// stream the same tiles at about the same time through their own rings,
+// with cache-allocating loads: the first brings a tile into the L2 and the
+// others read it there, so memory serves it once for up to four members,
+// while the waves stay as independent as in a plain piece.
+template <int GP, int NG, bool RS = false>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, const int h,
                                             const int t_lo, const int t_hi,
-                                            const int64_t part_slot) {
+                                            const int64_t part_slot, const int skip = 0,
+                                            const int bq_b = 0) {
   constexpr int NPT = Geo<GP, NG>::NPT;    // 16-token chunks per tile
   constexpr int RING = Geo<GP, NG>::RING;
   constexpr int TILE = Geo<GP, NG>::TILE;
@@ -249,7 +284,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   half8_t Bq[4];
   float qscale, qbar_s, qbar2;
   {
-    const uint32_t* base = a.bq + (int64_t(b) * a.n_kv_heads + h) * kBqWords;
+    const uint32_t* base = a.bq + (int64_t(RS ? bq_b : b) * a.n_kv_heads + h) * kBqWords;
     const uint4* src = reinterpret_cast<const uint4*>(base + lane * 16);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) Bq[kk] = __builtin_bit_cast(half8_t, src[kk]);
@@ -265,9 +300,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     asm volatile("" : "+v"(qscale), "+v"(qbar_s), "+v"(qbar2));
   }
 
-  const int tiles_all = (rg.cl - rg.cf) / NPT;
-  const int t_begin = min(max(t_lo - a.piece_cost, 0), tiles_all);
-  const int t_end = min(max(t_hi - a.piece_cost, 0), tiles_all);
+  int t_begin, t_end;
+  if constexpr (RS) {
+    // tile t covers virtual offsets (piece_cost + rs_cost (t - 1), piece_cost + rs_cost t]
+    auto tile_at = [&](int v) {
+      return min(max((v - a.piece_cost + a.rs_cost - 1) / a.rs_cost, 0), skip);
+    };
+    t_begin = t_lo <= a.piece_cost ? 0 : tile_at(t_lo);
+    t_end = t_hi <= a.piece_cost ? 0 : tile_at(t_hi);
+  } else {
+    const int tiles_own = (rg.cl - rg.cf) / NPT - skip;
+    t_begin = skip + min(max(t_lo - a.piece_cost, 0), tiles_own);
+    t_end = skip + min(max(t_hi - a.piece_cost, 0), tiles_own);
+  }
   const int n_tiles = t_end - t_begin;
   const int c_begin = rg.cf + NPT * t_begin;   // first chunk of this split
   const float log2_sigma = float(a.log2_sigma_v);
@@ -324,7 +369,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     }
     const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot));
 #pragma unroll
-    for (int p = 0; p < NPT; ++p) dma_x4(pool + off[p], 16u * lane, lds + 1024u * p);
+    for (int p = 0; p < NPT; ++p) dma_x4<!RS>(pool + off[p], 16u * lane, lds + 1024u * p);
     // params of chunks 2i (lanes 0-31) and 2i + 1 (lanes 32-63), in parts of
     // 128 bytes: part u of the pair at 1024 NPT + 256 (NG i + u)
 #pragma unroll
@@ -333,8 +378,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       const int64_t o = (lane >> 5) ? off[p1] : off[p0];
 #pragma unroll
       for (int u = 0; u < NG; ++u)
-        dma_x1(pool + o + kKParamsOff + 128 * u + 4 * (lane & 31),
-               lds + 1024u * NPT + 256u * (NG * i + u));
+        dma_x1<!RS>(pool + o + kKParamsOff + 128 * u + 4 * (lane & 31),
+                    lds + 1024u * NPT + 256u * (NG * i + u));
     }
   };
   constexpr int kDmaPerTile = NPT + Geo<GP, NG>::PARAM_DMA;
@@ -846,20 +891,23 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   // past the end read chunk 0 and are never computed), so the number of
   // loads in flight at each wait is the same on every path; page lookups
   // run one step ahead of the DMA.
-  const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;     // tiles wave, wave+4, ...
+  // tiles wave, wave + 4, ... (row-set mode: every tile)
+  constexpr int kStep = RS ? 1 : 4;
+  const int first = RS ? 0 : wave;
+  const int my_tiles = RS ? n_tiles : (n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0);
   if (my_tiles > 0) {
     Pages pn;
 #pragma unroll
     for (int k = 0; k < RING; ++k) {
-      fetch_pages(wave + 4 * k, pn);
-      issue_tile(wave + 4 * k, pn, ring_slot_k<GP, NG>(k, wave));
+      fetch_pages(first + kStep * k, pn);
+      issue_tile(first + kStep * k, pn, ring_slot_k<GP, NG>(k, wave));
     }
-    fetch_pages(wave + 4 * RING, pn);
+    fetch_pages(first + kStep * RING, pn);
     for (int k0 = 0; k0 < my_tiles; k0 += RING) {
 #pragma unroll
       for (int k = 0; k < RING; ++k) {
         if (k0 + k < my_tiles) {
-          const int ahead = wave + 4 * (k0 + k + RING);
+          const int ahead = first + kStep * (k0 + k + RING);
           uint8_t* slot = ring_slot_k<GP, NG>(k, wave);
           // Rotating wave priority: the arbiter otherwise serves the oldest
           // resident waves first, and the work-groups of one CU, which all
@@ -871,7 +919,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           else __builtin_amdgcn_s_setprio(3);
           compute_tile(slot, [&] {
             issue_tile(ahead, pn, slot);
-            fetch_pages(ahead + 4, pn);
+            fetch_pages(ahead + kStep, pn);
           });
         }
       }
@@ -936,7 +984,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   }
 
   __syncthreads();
-  store_partial<GP>(G, wm, wl, wo, a.partials + part_slot * G * kPartialStride);
+  if constexpr (RS) store_wave_partials<GP>(G, wm, wl, wo, a.partials + part_slot * G * kPartialStride);
+  else store_partial<GP>(G, wm, wl, wo, a.partials + part_slot * G * kPartialStride);
 }
 
 // Decode over equal tile ranges: the virtual tiles of all (b, h), in order,
@@ -1006,7 +1055,27 @@ __device__ void token_slice_item(const DecodeArgs& a, int idx) {
   for (int i = tid; i < G * kPartialStride; i += blockDim.x) out[i] = stage[i];
 }
 
+// A row-set piece of a shared-prefix group: group gidx, KV head h, row set
+// r (members 4r .. 4r + 3 of the group, one per wave; a wave without a valid
+// member takes the representative's rows and its partial is not read).
 template <int GP, int NG>
+__device__ __forceinline__ void rowset_piece(const DecodeArgs& a, int gidx, int h, int r,
+                                             int64_t q, int i, int t_lo, int t_hi) {
+  const int32_t* gi = a.grp_info + int64_t(gidx) * kGrpInfo;
+  const int skip = gi[kGiSkip], rep = gi[kGiRep];
+  const int m = gi[kGiMemberStart] + 4 * r + (threadIdx.x >> 6);
+  int bw = rep;
+  if (m < gi[kGiMemberEnd]) {
+    const int bb = a.members[m];
+    if (bb >= 0 && bb < a.batch && a.seq_group[bb] == gidx && a.seq_member[bb] == m) bw = bb;
+  }
+  decode_item<GP, NG, true>(a, rep, h, t_lo, t_hi, a.rs_slot0 + (int64_t(i) + q) * 4, skip,
+                            __builtin_amdgcn_readfirstlane(bw));
+}
+
+// PRE: the decode has shared-prefix groups (one (scale, zero) pair per
+// vector); their row-set items follow the (b, h) pieces.
+template <int GP, int NG, bool PRE = false>
 __global__ __launch_bounds__(256, GP <= 4 ? (NG == 1 ? 4 : 3) : 2) void decode_mfma_kernel(
     DecodeArgs a) {
   if (static_cast<int>(blockIdx.x) >= a.chain_groups) {
@@ -1018,26 +1087,71 @@ __global__ __launch_bounds__(256, GP <= 4 ? (NG == 1 ? 4 : 3) : 2) void decode_m
   const int32_t* pre = a.tile_prefix;
   const int g0 = a.range_start[i], g1 = a.range_start[i + 1];
   if (g0 >= g1) return;
-  // sequence holding tile g0: the largest b with Hkv * pre[b] <= g0
-  int lo = 0, hi = B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (Hkv * pre[mid] <= g0) lo = mid; else hi = mid;
+  // virtual tiles of the (b, h) pieces; a shared-prefix decode's row-set
+  // items follow them
+  const int pairs_total = PRE ? Hkv * pre[B] : INT_MAX;
+  bool first = true;
+  if (g0 < pairs_total) {
+    // sequence holding tile g0: the largest b with Hkv * pre[b] <= g0
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (Hkv * pre[mid] <= g0) lo = mid; else hi = mid;
+    }
+    int b = lo;
+    int wb = pre[b + 1] - pre[b];
+    int h = (g0 - Hkv * pre[b]) / wb;
+    for (;;) {
+      const int sp = Hkv * pre[b] + h * wb;   // first tile of (b, h)
+      if (sp >= g1) break;
+      if (!first) __syncthreads();   // the previous piece is done with every LDS buffer
+      first = false;
+      const int p = b * Hkv + h;
+      const int skip = PRE ? a.seq_skip[b] : 0;
+      decode_item<GP, NG>(a, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(h),
+                          max(g0, sp) - sp, min(g1, sp + wb) - sp, int64_t(i) + p,
+                          __builtin_amdgcn_readfirstlane(skip));
+      if (++h == Hkv) {
+        h = 0;
+        if (++b == B) break;
+        wb = pre[b + 1] - pre[b];
+      }
+    }
   }
-  int b = lo;
-  int wb = pre[b + 1] - pre[b];
-  int h = (g0 - Hkv * pre[b]) / wb;
-  for (int first = 1;; first = 0) {
-    const int sp = Hkv * pre[b] + h * wb;   // first tile of (b, h)
-    if (sp >= g1) break;
-    if (!first) __syncthreads();   // the previous piece is done with every LDS buffer
-    const int p = b * Hkv + h;
-    decode_item<GP, NG>(a, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(h),
-                    max(g0, sp) - sp, min(g1, sp + wb) - sp, int64_t(i) + p);
-    if (++h == Hkv) {
-      h = 0;
-      if (++b == B) break;
-      wb = pre[b + 1] - pre[b];
+  if (PRE && g1 > pairs_total) {
+    // row-set items: group by group, (h, r) in order within a group
+    const int v0 = max(g0, pairs_total) - pairs_total, v1 = g1 - pairs_total;
+    const int32_t* gi = a.grp_info;
+    // the largest group whose items start at or before v0 (groups without
+    // items share their successor's start and are passed over)
+    int lo = 0, hi = a.n_groups;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (gi[int64_t(mid) * kGrpInfo + kGiRsPrefix] <= v0) lo = mid; else hi = mid;
+    }
+    int gidx = lo;
+    int w = gi[int64_t(gidx) * kGrpInfo + kGiWidth];
+    int rows = gi[int64_t(gidx) * kGrpInfo + kGiRowSets];
+    int start = gi[int64_t(gidx) * kGrpInfo + kGiRsPrefix];
+    int idx = rows > 0 ? (v0 - start) / w : 0;
+    for (;;) {
+      if (idx >= Hkv * rows) {   // next group with items
+        if (++gidx >= a.n_groups) break;
+        w = gi[int64_t(gidx) * kGrpInfo + kGiWidth];
+        rows = gi[int64_t(gidx) * kGrpInfo + kGiRowSets];
+        start = gi[int64_t(gidx) * kGrpInfo + kGiRsPrefix];
+        idx = 0;
+        continue;
+      }
+      const int sq = start + idx * w;   // first virtual tile of the item
+      if (sq >= v1) break;
+      if (!first) __syncthreads();
+      first = false;
+      const int64_t q = gi[int64_t(gidx) * kGrpInfo + kGiItemBase] + idx;
+      if constexpr (PRE)
+        rowset_piece<GP, NG>(a, __builtin_amdgcn_readfirstlane(gidx), idx / rows, idx % rows, q,
+                             i, max(v0, sq) - sq, min(v1, sq + w) - sq);
+      ++idx;
     }
   }
 }
@@ -1051,27 +1165,31 @@ __global__ __launch_bounds__(256, GP <= 4 ? (NG == 1 ? 4 : 3) : 2) void decode_m
 // head) when there are few (sequence, KV head) pairs, so that a small
 // batch's combine spreads over more CUs and takes its many splits in one
 // round (combine_head_kernel).
-template <int GP>
+template <int GP, bool PRE = false>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int p = b * a.n_kv_heads + h;
   const int pr = a.pair_range[p];
   const int i0 = pr & 0xFFFF, i1 = pr >> 16;
   const int64_t tok = a.tok_slot0 + int64_t(p) * a.n_tok_slices;
-  combine_pair<GP>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices);
+  int64_t rs = 0;
+  const int n_rs = PRE ? rowset_slots(a, b, h, rs) : 0;
+  combine_pair<GP, PRE>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices, rs, n_rs);
 }
 
 constexpr int kHeadCombineParts = 8;   // 128-thread parts of a combine_head_kernel work-group
 
-template <int GP>
+template <int GP, bool PRE = false>
 __global__ __launch_bounds__(128 * kHeadCombineParts) void combine_head_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int p = b * a.n_kv_heads + h;
   const int pr = a.pair_range[p];
   const int i0 = pr & 0xFFFF, i1 = pr >> 16;
   const int64_t tok = a.tok_slot0 + int64_t(p) * a.n_tok_slices;
-  combine_head<GP, kHeadCombineParts>(a, b, h, blockIdx.z, int64_t(i0) + p, i1 - i0 + 1, tok,
-                                      a.n_tok_slices);
+  int64_t rs = 0;
+  const int n_rs = PRE ? rowset_slots(a, b, h, rs) : 0;
+  combine_head<GP, kHeadCombineParts, PRE>(a, b, h, blockIdx.z, int64_t(i0) + p, i1 - i0 + 1,
+                                           tok, a.n_tok_slices, rs, n_rs);
 }
 
 }  // namespace

@@ -109,6 +109,9 @@ __device__ __forceinline__ void store_agent(int* p, int v) {
 __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int load_agent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Arrival ticket: releases this wave's earlier stores, acquires those of the
 // waves that took the ticket before.
 __device__ __forceinline__ int fetch_add_acq_rel_agent(int* p, int v) {

@@ -86,7 +86,9 @@ namespace {
 DecodeTuning read_tuning() {
   DecodeTuning t = {{kPieceCostChunks, kPieceCostChunksG8},
                     {{1230, 1100, 940, 830}, {1120, 1024, 930, 1024}},
-                    {{1024, 1024}, {1024, 1024}}};
+                    {{1024, 1024}, {1024, 1024}},
+                    kRowSetCost};
+  t.rowset_cost = std::min(std::max(env_int("KVQ_ROWSET_COST", kRowSetCost), 1), 16);
   const int pc = env_int("KVQ_PIECE_COST", -1);
   if (pc >= 0) t.piece_cost[0] = t.piece_cost[1] = std::min(pc, 4096);
   for (int k = 0; k < 2; ++k) {
@@ -127,6 +129,12 @@ DecodeKernel selected_decode_kernel(const kvq_dims& d) {
   return kDecodeMfma;
 }
 
+bool prefix_groups_supported(const kvq_dims& d) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const bool narrow = d.quant_group != 0 && d.quant_group != kHeadDim;
+  return selected_decode_kernel(d) == kDecodeMfma && G <= 8 && !narrow;
+}
+
 int multi_query_pass(const kvq_dims& d, int32_t n_query, DecodeKernel which) {
   const int G = d.n_q_heads / d.n_kv_heads;
   const bool narrow = d.quant_group != 0 && d.quant_group != kHeadDim;
@@ -135,7 +143,7 @@ int multi_query_pass(const kvq_dims& d, int32_t n_query, DecodeKernel which) {
 }
 
 DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len,
-                            int32_t n_query) {
+                            int32_t n_query, const kvq_prefix_groups* groups) {
   DecodePlan p{};
   const int64_t int2_end = std::max<int64_t>(d.n_sink, int64_t(max_seq_len) - d.n_recent);
   const int64_t first_chunk = d.n_sink / kChunkTokens;
@@ -180,11 +188,28 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
     p.tok_slot0 = int64_t(kChainGroups) + heads;
     p.piece_cost = decode_tuning().piece_cost[gp == 8 ? 1 : 0] / npt;
   }
-  const size_t slots = own_token_item
-                           ? size_t(heads) * p.n_split
-                           : size_t(kChainGroups) + size_t(heads) * (1 + p.n_tok_slices);
+  size_t slots = own_token_item
+                     ? size_t(heads) * p.n_split
+                     : size_t(kChainGroups) + size_t(heads) * (1 + p.n_tok_slices);
+  // Shared-prefix groups: row-set items (Hkv per row set of four members;
+  // sum of ceil(n_j / 4) <= (n_members + 3 n_groups) / 4), four partial slots
+  // per (range, item) overlap, and the per-sequence and per-group tables.
+  if (groups != nullptr && groups->n_groups > 0 && !own_token_item && n_query == 1 &&
+      prefix_groups_supported(d)) {
+    p.n_groups = groups->n_groups;
+    p.n_members = groups->n_members;
+    p.n_items_max = static_cast<int>(int64_t(d.n_kv_heads) *
+                                     ((int64_t(groups->n_members) + 3 * groups->n_groups) / 4));
+    p.rs_cost = decode_tuning().rowset_cost;
+    p.group_bytes = 3 * r256(size_t(batch) * sizeof(int32_t)) +
+                    r256(size_t(groups->n_groups) * kGrpInfo * sizeof(int32_t)) +
+                    r256(size_t(p.n_items_max) * sizeof(int32_t));
+    p.rs_slot0 = int64_t(slots);
+    slots += 4 * (size_t(kChainGroups) + size_t(p.n_items_max));
+  }
   p.partial_bytes = slots * G * kPartialStride * sizeof(float);
-  p.total_bytes = p.ticket_bytes + p.qrot_bytes + p.bq_bytes + p.prefix_bytes + p.partial_bytes;
+  p.total_bytes = p.ticket_bytes + p.qrot_bytes + p.bq_bytes + p.prefix_bytes + p.group_bytes +
+                  p.partial_bytes;
   return p;
 }
 
@@ -301,6 +326,48 @@ int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer, const kvq
   return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
                                   max_seq_len, q, out, workspace, plan, selected_decode_kernel(*dims),
                                   stream));
+}
+
+// Shared-prefix groups: the host values and that the arrays are given.
+static int check_groups(const kvq_prefix_groups* groups) {
+  if (groups == nullptr || groups->n_groups < 0 || groups->n_groups > kMaxPrefixGroups ||
+      groups->n_members < 0 || groups->n_members > kMaxPrefixMembers)
+    return KVQ_ERR_ARG;
+  if (groups->n_groups > 0 && (groups->member_start == nullptr || groups->members == nullptr ||
+                               groups->prefix_len == nullptr))
+    return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+size_t kvq_decode_prefix_workspace_bytes(const kvq_dims* dims, int32_t batch,
+                                         int32_t max_seq_len, const kvq_prefix_groups* groups) {
+  if (check_dims(dims) != KVQ_OK || batch < 1 || max_seq_len < 0 || check_groups(groups) != KVQ_OK)
+    return 0;
+  return make_decode_plan(*dims, batch, max_seq_len, 1, groups).total_bytes;
+}
+
+int kvq_decode_prefix_attention(const kvq_dims* dims, const kvq_layer* layer,
+                                const kvq_cache* cache, int32_t batch, const int32_t* seq_len,
+                                int32_t max_seq_len, const uint16_t* q, float* out,
+                                const kvq_prefix_groups* groups, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  int rc = check_decode_args(dims, layer, cache, batch, seq_len, max_seq_len, q, out, &plan, 1);
+  if (rc != KVQ_OK) return rc;
+  if ((rc = check_groups(groups)) != KVQ_OK) return rc;
+  plan = make_decode_plan(*dims, batch, max_seq_len, 1, groups);
+  // the row-set items' virtual tiles are counted in 32 bits too
+  if (plan.n_groups > 0 &&
+      int64_t(batch) * dims->n_kv_heads * (int64_t(max_seq_len) / kChunkTokens + kPieceCostChunksG8 + 2) +
+              int64_t(plan.n_items_max) *
+                  (int64_t(plan.rs_cost) * (int64_t(max_seq_len) / kChunkTokens) + kPieceCostChunksG8 + 2) >=
+          (int64_t(1) << 31))
+    return KVQ_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan.total_bytes)
+    return KVQ_ERR_WORKSPACE;
+  return hip_status(launch_decode(*dims, resolved_scale(dims), *layer, *cache, batch, seq_len,
+                                  max_seq_len, q, out, workspace, plan, selected_decode_kernel(*dims),
+                                  stream, 1, 0, 1, plan.n_groups > 0 ? groups : nullptr));
 }
 
 size_t kvq_decode_multi_workspace_bytes(const kvq_dims* dims, int32_t batch,

@@ -51,9 +51,22 @@ struct DecodePlan {
   int n_tok_slices;     // MFMA decode: 64-token slices of the token-by-token list
   int64_t tok_slot0;    // MFMA decode: first partial slot of those slices
   size_t prefix_bytes;   // MFMA decode: per-sequence tile prefix [B + 1] int32
+  // MFMA decode with shared-prefix groups (0 groups otherwise)
+  int n_groups;
+  int n_members;
+  int n_items_max;      // row-set items: Hkv x sum over groups of ceil(members / 4), bounded
+  int rs_cost;          // virtual tiles per row-set tile
+  size_t group_bytes;   // per-sequence skip / member / group [3][B], group rows, item ranges
+  int64_t rs_slot0;     // first partial slot of the row-set pieces (4 per range and item)
   size_t partial_bytes;
   size_t total_bytes;
 };
+
+// Shared-prefix groups of the MFMA decode: grp_info row width and the
+// largest number of groups.
+constexpr int kGrpInfo = 8;
+constexpr int kMaxPrefixGroups = 256;
+constexpr int kMaxPrefixMembers = 1 << 24;
 
 // Upper bound of the MFMA decode's work-group count (resident work-groups of
 // the device, 256 CUs x 4); its partial slots number kChainGroups + B * Hkv,
@@ -67,12 +80,24 @@ constexpr int kChainGroups = 1024;
 // sustained decode (395 us against 398 at 200 and 406 at 300).
 constexpr int kPieceCostChunks = 80;
 constexpr int kPieceCostChunksG8 = 150;
+// Virtual tiles charged per tile of a shared-prefix row-set item: its
+// work-group's four waves all attend that tile (for four members), so it
+// takes about as long as the four tiles a plain work-group streams
+// meanwhile (64-sequence G = 8 batch with a 16K shared prefix: 331.8, 327.1,
+// 329.8 us per decode at 3, 4, 5).
+constexpr int kRowSetCost = 4;
 
 // Plan of a decode with n_query queries per sequence (1 for decode; M for
 // multi-query attention): its rows per (sequence, KV head) are
 // n_query * Hq / Hkv.
 DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_len,
-                            int32_t n_query = 1);
+                            int32_t n_query = 1, const kvq_prefix_groups* groups = nullptr);
+
+// Whether the decode of these dims takes shared-prefix groups (the
+// matrix-core kernel with one (scale, zero) pair per vector and at most 8
+// query heads per KV head); otherwise a prefix-aware call decodes every
+// sequence on its own.
+bool prefix_groups_supported(const kvq_dims& d);
 
 // Tuning constants of the MFMA decode, read once per process from the
 // environment (KVQ_PIECE_COST, KVQ_ROUND_WEIGHTS, KVQ_XCD_WEIGHTS) with the
@@ -83,6 +108,7 @@ struct DecodeTuning {
   int piece_cost[2];        // chunks charged per piece start: [G <= 4, G = 8]
   int round_weight[2][4];   // [G <= 4, G = 8][dispatch round], 1/1024 units
   int xcd_weight[2][2];     // [G <= 4, G = 8][even, odd XCD]
+  int rowset_cost;          // virtual tiles charged per tile of a shared-prefix row-set item
 };
 const DecodeTuning& decode_tuning();
 
@@ -115,7 +141,8 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
                   const kvq_cache& cache, int32_t batch, const int32_t* seq_len,
                   int32_t max_seq_len, const uint16_t* q, float* out, void* workspace,
                   const DecodePlan& plan, DecodeKernel which, void* stream,
-                  int32_t n_query = 1, int32_t query_base = 0, int32_t query_count = 1);
+                  int32_t n_query = 1, int32_t query_base = 0, int32_t query_count = 1,
+                  const kvq_prefix_groups* groups = nullptr);
 
 // Queries per launch of a multi-query attention of M queries per sequence:
 // the matrix-core decode takes at most 8 rows (queries x Hq / Hkv) per pass

@@ -43,6 +43,11 @@ class KvqCache(C.Structure):
                 ("recent", C.c_void_p), ("block_table", C.c_void_p), ("bt_stride", C.c_int32)]
 
 
+class KvqPrefixGroups(C.Structure):
+    _fields_ = [("n_groups", C.c_int32), ("n_members", C.c_int32), ("member_start", C.c_void_p),
+                ("members", C.c_void_p), ("prefix_len", C.c_void_p)]
+
+
 class KvqHqmqDims(C.Structure):
     _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("page_size", C.c_int32), ("n_secondary", C.c_int32), ("sm_scale", C.c_float)]
@@ -64,6 +69,7 @@ HQMQ_TOKEN_BYTES = 192            # K and V records of one (position, KV head)
 EXPORTS = ("kvq_calibrate", "kvq_quantize_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_multi_workspace_bytes",
            "kvq_decode_multi_attention", "kvq_decode_attention_noalloc", "kvq_decode_step",
+           "kvq_decode_prefix_workspace_bytes", "kvq_decode_prefix_attention",
            "kvq_status_string", "kvq_last_error")
 PROBE_EXPORTS = ("kvq_probe_stream_read", "kvq_probe_chunk_read")
 
@@ -100,6 +106,13 @@ def lib():
                                       C.POINTER(KvqCache), I32, P, P, I32, I32, P, P, P, I32,
                                       P, P, P, SZ, P]
         L.kvq_decode_step.restype = C.c_int
+        L.kvq_decode_prefix_workspace_bytes.argtypes = [C.POINTER(KvqDims), I32, I32,
+                                                        C.POINTER(KvqPrefixGroups)]
+        L.kvq_decode_prefix_workspace_bytes.restype = SZ
+        L.kvq_decode_prefix_attention.argtypes = [C.POINTER(KvqDims), C.POINTER(KvqLayer),
+                                                  C.POINTER(KvqCache), I32, P, I32, P, P,
+                                                  C.POINTER(KvqPrefixGroups), P, SZ, P]
+        L.kvq_decode_prefix_attention.restype = C.c_int
         L.kvq_status_string.argtypes = [C.c_int]
         L.kvq_status_string.restype = C.c_char_p
         L.kvq_last_error.argtypes = []
@@ -245,6 +258,32 @@ def decode_step(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, start_pos,
                                _ptr(seq_len), max_seq_len, _ptr(q), _ptr(out), _ptr(workspace),
                                nbytes, _stream_handle(stream))
     _check(rc, "kvq_decode_step")
+
+
+def prefix_groups(n_members: int, member_start=None, members=None, prefix_len=None
+                  ) -> KvqPrefixGroups:
+    """kvq_prefix_groups over device int32 tensors (member_start has
+    n_groups + 1 entries); keep the tensors alive while it is used."""
+    n_groups = 0 if member_start is None else int(member_start.numel()) - 1
+    return KvqPrefixGroups(n_groups, n_members, _ptr(member_start), _ptr(members),
+                           _ptr(prefix_len))
+
+
+def decode_prefix_workspace_bytes(d: KvqDims, batch: int, max_seq_len: int,
+                                  groups: KvqPrefixGroups) -> int:
+    return int(lib().kvq_decode_prefix_workspace_bytes(C.byref(d), batch, max_seq_len,
+                                                       C.byref(groups)))
+
+
+def decode_prefix_attention(d: KvqDims, lay: KvqLayer, cch: KvqCache, batch: int, seq_len,
+                            max_seq_len: int, q, out, groups: KvqPrefixGroups, workspace,
+                            stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kvq_decode_prefix_attention(C.byref(d), C.byref(lay), C.byref(cch), batch,
+                                           _ptr(seq_len), max_seq_len, _ptr(q), _ptr(out),
+                                           C.byref(groups), _ptr(workspace), nbytes,
+                                           _stream_handle(stream))
+    _check(rc, "kvq_decode_prefix_attention")
 
 
 # ------------------------------------------------------------------ HQMQ codec (kvq2_hqmq.h)

@@ -100,6 +100,32 @@ int main() {
   w2.n_recent = 2;
   CHECK(kvq_decode_multi_attention(&w2, &lay, &c, 2, i32, 100, 3, u16, f32, ws, 1 << 30, nullptr) == KVQ_ERR_ARG);
 
+  // ---- prefix-aware decode: groups validated, their workspace planned
+  {
+    kvq_prefix_groups g = {1, 2, i32, i32, i32};
+    const size_t needp = kvq_decode_prefix_workspace_bytes(&d, 2, 100, &g);
+    CHECK(needp > need);
+    const int before_prefix = kvq::g_launches;
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &g, ws, needp, nullptr) == KVQ_OK);
+    CHECK(kvq::g_launches == before_prefix + 1);
+    CHECK(kvq::g_last_ws_bytes == needp);
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &g, ws, needp - 1, nullptr) == KVQ_ERR_WORKSPACE);
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, nullptr, ws, needp, nullptr) == KVQ_ERR_ARG);
+    kvq_prefix_groups bad = {257, 2, i32, i32, i32};
+    CHECK(kvq_decode_prefix_workspace_bytes(&d, 2, 100, &bad) == 0);
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &bad, ws, needp, nullptr) == KVQ_ERR_ARG);
+    kvq_prefix_groups none = {0, 0, nullptr, nullptr, nullptr};
+    CHECK(kvq_decode_prefix_workspace_bytes(&d, 2, 100, &none) == need);
+    kvq_prefix_groups null_arrays = {1, 2, nullptr, i32, i32};
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &null_arrays, ws, needp, nullptr) == KVQ_ERR_ARG);
+    // member counts large enough to overflow the 32-bit virtual tile count
+    kvq_prefix_groups big = {256, 1 << 24, i32, i32, i32};
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &big, ws, 1 << 30, nullptr) == KVQ_ERR_UNSUPPORTED);
+    kvq_prefix_groups too_many = {256, (1 << 24) + 1, i32, i32, i32};
+    CHECK(kvq_decode_prefix_workspace_bytes(&d, 2, 100, &too_many) == 0);
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &too_many, ws, 1 << 30, nullptr) == KVQ_ERR_ARG);
+  }
+
   // ---- planning over a sweep of shapes (no overflow, monotone in batch)
   for (int G : {1, 2, 3, 4, 8, 16})
     for (int P : {16, 32, 64})

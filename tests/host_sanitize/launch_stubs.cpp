@@ -30,7 +30,8 @@ int launch_decode_step(const kvq_dims&, float, const kvq_layer&, const kvq_cache
 
 int launch_decode(const kvq_dims&, float, const kvq_layer&, const kvq_cache&, int32_t,
                   const int32_t*, int32_t, const uint16_t*, float*, void*,
-                  const DecodePlan& plan, DecodeKernel, void*, int32_t, int32_t, int32_t) {
+                  const DecodePlan& plan, DecodeKernel, void*, int32_t, int32_t, int32_t,
+                  const kvq_prefix_groups*) {
   ++g_launches;
   g_last_ws_bytes = plan.total_bytes;
   return 0;

@@ -284,3 +284,46 @@ def test_noalloc_decode_validates_before_launch():
     assert need > 64 << 20
     assert _noalloc(d, lay, cch, batch=2000) == ERR_WS
     assert b"64 MiB" in _lib().kvq_last_error()
+
+
+# ---------------------------------------------------------------- prefix-aware decode
+
+def _groups(n_groups=1, n_members=4, arrays=True):
+    p = FAKE + 0x600000 if arrays else None
+    return kvq2.KvqPrefixGroups(n_groups, n_members, p, p and p + 0x1000, p and p + 0x2000)
+
+
+def _prefix(d, lay, cch, g, batch=2, seq=FAKE, max_len=100, q=FAKE, out=FAKE, ws=FAKE,
+            wsb=1 << 30):
+    return _lib().kvq_decode_prefix_attention(C.byref(d), C.byref(lay), C.byref(cch), batch, seq,
+                                              max_len, q, out, None if g is None else C.byref(g),
+                                              ws, wsb, None)
+
+
+def test_prefix_decode_validates_before_launch():
+    d, lay, cch = _args()
+    assert _prefix(d, lay, cch, None) == ERR_ARG
+    assert _prefix(d, lay, cch, _groups(n_groups=-1)) == ERR_ARG
+    assert _prefix(d, lay, cch, _groups(n_groups=257)) == ERR_ARG
+    assert _prefix(d, lay, cch, _groups(n_members=-1)) == ERR_ARG
+    assert _prefix(d, lay, cch, _groups(arrays=False)) == ERR_ARG
+    assert _prefix(d, lay, cch, _groups(), q=FAKE + 2) == ERR_ARG      # the decode's own checks
+    assert _prefix(d, lay, cch, _groups(), seq=0) == ERR_ARG
+    need = _lib().kvq_decode_prefix_workspace_bytes(C.byref(d), 2, 100, C.byref(_groups()))
+    assert _prefix(d, lay, cch, _groups(), wsb=need - 1) == ERR_WS
+    assert _prefix(d, lay, cch, _groups(), ws=0) == ERR_WS
+
+
+def test_prefix_workspace_bytes():
+    d = kvq2.dims(64, 8, 16, 4, 128)
+    f = lambda g: _lib().kvq_decode_prefix_workspace_bytes(C.byref(d), 64, 65536, g)
+    plain = _lib().kvq_decode_workspace_bytes(C.byref(d), 64, 65536)
+    assert f(C.byref(_groups(n_groups=0, n_members=0, arrays=False))) == plain
+    one, two = f(C.byref(_groups(1, 32))), f(C.byref(_groups(2, 32)))
+    assert plain < one <= two
+    assert f(None) == 0 and f(C.byref(_groups(n_groups=300))) == 0
+    # quantization groups narrower than the head: the groups are not used
+    dn = kvq2.dims(64, 8, 16, 4, 128, quant_group=32)
+    g = C.byref(_groups(1, 32))
+    assert (_lib().kvq_decode_prefix_workspace_bytes(C.byref(dn), 64, 65536, g)
+            == _lib().kvq_decode_workspace_bytes(C.byref(dn), 64, 65536))
