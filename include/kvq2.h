@@ -276,7 +276,7 @@ int kvq_decode_step(const kvq_dims* dims, const kvq_layer* layer,
  *                listed more than once counts as a member of its first
  *                listing only
  *   prefix_len   [n_groups] tokens, >= 0
- * n_groups (0 .. 256) and n_members (0 .. 2^24) are host values.
+ * n_groups (0 .. 256) and n_members (0 .. 1024) are host values.
  */
 typedef struct kvq_prefix_groups {
   int32_t n_groups;
@@ -305,7 +305,7 @@ typedef struct kvq_prefix_groups {
  *              kvq_decode_attention (for groups of the same or smaller
  *              n_groups and n_members)
  * Returns KVQ_ERR_ARG for a null groups, n_groups outside 0..256,
- * n_members outside 0..2^24, or null arrays when n_groups > 0, and
+ * n_members outside 0..1024, or null arrays when n_groups > 0, and
  * KVQ_ERR_UNSUPPORTED when the batch's and the groups' tiles together
  * exceed the decode's 32-bit tile counters.
  */

@@ -20,7 +20,11 @@ struct PlanLds {
   int scan[256];
   int carry;
   int rs[kChainGroups + 1];
-  // shared-prefix groups
+};
+
+// LDS of the plan's shared-prefix groups (prefix-aware decodes only).
+constexpr int kPlanHash = 2 * kMaxPrefixMembers;   // open-addressing slots
+struct GroupLds {
   int gs[kMaxPrefixGroups + 1];    // member starts (clamped)
   int gskip[kMaxPrefixGroups];     // whole prefix tiles
   int gvalid[kMaxPrefixGroups];    // some member is valid
@@ -28,98 +32,148 @@ struct PlanLds {
   int grs[kMaxPrefixGroups + 1];   // virtual tiles of earlier groups' items
   int gib[kMaxPrefixGroups + 1];   // first item
   int gw[kMaxPrefixGroups];        // virtual tiles per item
+  int mseq[kMaxPrefixMembers];     // sequence of member m
+  int mtiles[kMaxPrefixMembers];   // its whole INT2 tiles (-1: not a sequence)
+  int mgroup[kMaxPrefixMembers];   // group of a valid member, else -1
+  int slot[kPlanHash];             // sequence -> member index of its first listing
 };
 
-// Shared-prefix groups, by the plan's work-group: the valid members (a
-// sequence's first listing, whose whole INT2 tiles cover its group's prefix
-// tiles), the tiles they skip, and each group's row-set items (grp_info
-// rows, with LDS copies for the cut).  Values that other threads wrote are
-// read back with agent-scope loads.
+__device__ __forceinline__ uint32_t plan_hash(int b) {
+  return (static_cast<uint32_t>(b) * 2654435761u) >> 21;   // 11 bits: kPlanHash slots
+}
+static_assert(kPlanHash == 2048, "plan_hash yields 11 bits");
+
+// Member index of the first listing of sequence b, or -1.
+__device__ __forceinline__ int first_listing(const GroupLds& L, int b) {
+  uint32_t h = plan_hash(b);
+  for (int k = 0; k < kPlanHash; ++k, h = (h + 1) & (kPlanHash - 1)) {
+    const int m = L.slot[h];
+    if (m < 0) return -1;
+    if (L.mseq[m] == b) return m;
+  }
+  return -1;
+}
+
+// Tiles that sequence b's pieces skip (read by its group's row sets).
+__device__ __forceinline__ int seq_skip_tiles(const GroupLds& L, int b) {
+  const int m = first_listing(L, b);
+  return m >= 0 && L.mgroup[m] >= 0 ? L.gskip[L.mgroup[m]] : 0;
+}
+
+// Shared-prefix groups, by the plan's work-group, in LDS: the valid members
+// (a sequence's first listing, found through an open-addressing table keyed
+// by sequence, whose whole INT2 tiles cover its group's prefix tiles), the
+// tiles they skip, each group's row-set items (grp_info rows, with LDS
+// copies for the cut) and the per-sequence tables of the later kernels.
 template <int GP>
-__device__ void plan_groups(const DecodeArgs& a, PlanLds& P) {
+__device__ void plan_groups(const DecodeArgs& a, GroupLds& L) {
   constexpr int npt = chunks_per_tile(GP);
   const int tid = threadIdx.x, nt = blockDim.x;
   const int ngr = a.n_groups, B = a.batch, Hkv = a.n_kv_heads;
   const int cf = (a.n_sink + kChunkTokens - 1) / kChunkTokens;
   for (int g = tid; g <= ngr; g += nt) {
-    P.gs[g] = a.member_start[g];
+    L.gs[g] = a.member_start[g];
     if (g < ngr) {
       // tiles of the group's prefix: whole tiles from the first whole chunk
       const int pc = max(a.prefix_len[g], 0) / kChunkTokens;
-      P.gskip[g] = pc > cf ? (pc - cf) / npt : 0;
-      P.gvalid[g] = 0;
-      P.grep[g] = INT_MAX;
+      L.gskip[g] = pc > cf ? (pc - cf) / npt : 0;
+      L.gvalid[g] = 0;
+      L.grep[g] = INT_MAX;
     }
   }
-  for (int b = tid; b < B; b += nt) {
-    a.seq_member[b] = INT_MAX;
-    a.seq_skip[b] = 0;
-    a.seq_group[b] = -1;
-  }
+  for (int m = tid; m < a.n_members; m += nt) L.mseq[m] = a.members[m];
+  for (int h = tid; h < kPlanHash; h += nt) L.slot[h] = -1;
   __syncthreads();
   if (tid == 0) {   // member starts non-decreasing within [0, n_members]
     int prev = 0;
     for (int g = 0; g <= ngr; ++g) {
-      prev = g == 0 ? 0 : min(max(P.gs[g], prev), a.n_members);
-      P.gs[g] = prev;
+      prev = g == 0 ? 0 : min(max(L.gs[g], prev), a.n_members);
+      L.gs[g] = prev;
     }
   }
-  __threadfence();
   __syncthreads();
-  const int nm = P.gs[ngr];
-  for (int m = tid; m < nm; m += nt) {   // first listing of every sequence
-    const int b = a.members[m];
-    if (b >= 0 && b < B) atomicMin(&a.seq_member[b], m);
+  const int nm = L.gs[ngr];
+  // first listing of every sequence: the table keeps the smallest member
+  // index per sequence (a slot, once claimed, only ever holds that sequence)
+  for (int m = tid; m < nm; m += nt) {
+    const int b = L.mseq[m];
+    int tiles = -1;
+    if (b >= 0 && b < B) {
+      const Int2Range rg = int2_range(a, a.seq_len[b], npt);
+      tiles = (rg.cl - rg.cf) / npt;
+      uint32_t h = plan_hash(b);
+      for (int k = 0; k < kPlanHash; ++k, h = (h + 1) & (kPlanHash - 1)) {
+        int cur = L.slot[h];
+        if (cur < 0) {
+          cur = atomicCAS(&L.slot[h], -1, m);
+          if (cur < 0) break;
+        }
+        if (L.mseq[cur] == b) {
+          atomicMin(&L.slot[h], m);
+          break;
+        }
+      }
+    }
+    L.mtiles[m] = tiles;
   }
-  __threadfence();
   __syncthreads();
   for (int m = tid; m < nm; m += nt) {
-    const int b = a.members[m];
-    if (b < 0 || b >= B || load_agent(&a.seq_member[b]) != m) continue;
-    int lo = 0, hi = ngr;   // group of m: the largest g with gs[g] <= m
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (P.gs[mid] <= m) lo = mid; else hi = mid;
+    const int b = L.mseq[m];
+    int grp = -1;
+    if (L.mtiles[m] >= 0 && first_listing(L, b) == m) {
+      int lo = 0, hi = ngr;   // group of m: the largest g with gs[g] <= m
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (L.gs[mid] <= m) lo = mid; else hi = mid;
+      }
+      const int skip = L.gskip[lo];
+      if (skip > 0 && L.mtiles[m] >= skip) {
+        grp = lo;
+        atomicMin(&L.grep[lo], m);
+        L.gvalid[lo] = 1;
+      }
     }
-    const int skip = P.gskip[lo];
-    const Int2Range rg = int2_range(a, a.seq_len[b], npt);
-    if (skip > 0 && (rg.cl - rg.cf) / npt >= skip) {
-      a.seq_skip[b] = skip;
-      a.seq_group[b] = lo;
-      atomicMin(&P.grep[lo], m);
-      P.gvalid[lo] = 1;
-    }
+    L.mgroup[m] = grp;
   }
   __syncthreads();
-  for (int g = tid; g < ngr; g += nt) P.grep[g] = P.gvalid[g] ? a.members[P.grep[g]] : 0;
+  for (int g = tid; g < ngr; g += nt) L.grep[g] = L.gvalid[g] ? L.mseq[L.grep[g]] : 0;
   __syncthreads();
   if (tid == 0) {
     int rs = 0, ib = 0;
     for (int g = 0; g < ngr; ++g) {
-      const int rows = (P.gs[g + 1] - P.gs[g] + 3) / 4;
-      const int skip = P.gvalid[g] ? P.gskip[g] : 0;
+      const int rows = (L.gs[g + 1] - L.gs[g] + 3) / 4;
+      const int skip = L.gvalid[g] ? L.gskip[g] : 0;
       const int w = max(1, a.rs_cost * skip) + a.piece_cost;
-      P.grs[g] = rs;
-      P.gib[g] = ib;
-      P.gw[g] = w;
+      L.grs[g] = rs;
+      L.gib[g] = ib;
+      L.gw[g] = w;
       int32_t* gi = a.grp_info + g * kGrpInfo;
       gi[kGiRsPrefix] = rs;
       gi[kGiWidth] = w;
       gi[kGiSkip] = skip;
-      gi[kGiRep] = P.grep[g];
+      gi[kGiRep] = L.grep[g];
       gi[kGiRowSets] = rows;
       gi[kGiItemBase] = ib;
-      gi[kGiMemberStart] = P.gs[g];
-      gi[kGiMemberEnd] = P.gs[g + 1];
+      gi[kGiMemberStart] = L.gs[g];
+      gi[kGiMemberEnd] = L.gs[g + 1];
       rs += Hkv * rows * w;
       ib += Hkv * rows;
     }
-    P.grs[ngr] = rs;
-    P.gib[ngr] = ib;
+    L.grs[ngr] = rs;
+    L.gib[ngr] = ib;
   }
-  __threadfence();
+  // per-sequence tables of the stream and combine kernels (read after this
+  // launch)
+  for (int b = tid; b < B; b += nt) {
+    const int m = first_listing(L, b);
+    const int grp = m >= 0 ? L.mgroup[m] : -1;
+    a.seq_member[b] = m;
+    a.seq_group[b] = grp;
+    a.seq_skip[b] = grp >= 0 ? L.gskip[grp] : 0;
+  }
   __syncthreads();
 }
+
 template <int KG>
 struct PrologueLds {
   float qs[KG][kHeadDim];           // q, then q'
@@ -128,9 +182,10 @@ struct PrologueLds {
   int qexp[KG];
 };
 
-// The equal-range plan of the MFMA decode, by one work-group of 256 threads.
-template <int GP>
-__device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
+// The equal-range plan of the MFMA decode, by one work-group of 256 threads
+// (PRE: with shared-prefix groups, whose LDS is *L).
+template <int GP, bool PRE = false>
+__device__ void plan_ranges(const DecodeArgs& a, PlanLds& P, GroupLds* L = nullptr) {
   constexpr int npt = chunks_per_tile(GP);
   const int tid = threadIdx.x;
   // W_b = max(1, whole INT2 tiles of sequence b) + piece_cost;
@@ -138,7 +193,7 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   // over blocks of 256 sequences).
   int* scan = P.scan;
   int& carry = P.carry;
-  if (a.n_groups > 0) plan_groups<GP>(a, P);
+  if constexpr (PRE) plan_groups<GP>(a, *L);
   if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
   __syncthreads();
   for (int base = 0; base < a.batch; base += 256) {
@@ -146,7 +201,8 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
     int w = 0;
     if (bb < a.batch) {
       const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
-      const int skip = a.n_groups > 0 ? load_agent(&a.seq_skip[bb]) : 0;
+      int skip = 0;
+      if constexpr (PRE) skip = seq_skip_tiles(*L, bb);
       w = max(1, (rg.cl - rg.cf) / npt - skip) + a.piece_cost;
     }
     scan[tid] = w;
@@ -170,7 +226,8 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   const int Hkv = a.n_kv_heads;
   // the (b, h) pieces, then the row-set items of shared-prefix groups
   const int64_t pairs_total = int64_t(Hkv) * carry;
-  const int64_t total = pairs_total + (a.n_groups > 0 ? P.grs[a.n_groups] : 0);
+  int64_t total = pairs_total;
+  if constexpr (PRE) total += L->grs[a.n_groups];
   const int rsz = a.round_size, rounds = rsz > 0 ? nwg / rsz : 0;
   const bool weighted = rsz > 0 && rsz % 8 == 0 && rounds >= 2 && rounds <= 4 &&
                         rounds * rsz == nwg && total >= 4 * int64_t(nwg);
@@ -231,24 +288,25 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
   for (int pr = tid; pr < a.batch * Hkv; pr += blockDim.x) {
     const int bb = pr / Hkv, hh = pr % Hkv;
     const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
-    const int skip = a.n_groups > 0 ? load_agent(&a.seq_skip[bb]) : 0;
+    int skip = 0;
+    if constexpr (PRE) skip = seq_skip_tiles(*L, bb);
     const int wbb = max(1, (rg.cl - rg.cf) / npt - skip) + a.piece_cost;
     // the prefix of bb, recomputed from the scan output in global memory
     const int sp = Hkv * a.tile_prefix[bb] + hh * wbb;
     a.pair_range[pr] = range_of(sp) | (range_of(sp + wbb - 1) << 16);
   }
   // first and last range of every row-set item
-  if (a.n_groups > 0) {
+  if constexpr (PRE) {
     const int ngr = a.n_groups;
-    for (int q = tid; q < P.gib[ngr]; q += blockDim.x) {
+    for (int q = tid; q < L->gib[ngr]; q += blockDim.x) {
       int lo = 0, hi = ngr;   // group of item q: the largest g with gib[g] <= q
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (P.gib[mid] <= q) lo = mid; else hi = mid;
+        if (L->gib[mid] <= q) lo = mid; else hi = mid;
       }
-      const int64_t sq = pairs_total + P.grs[lo] + int64_t(q - P.gib[lo]) * P.gw[lo];
+      const int64_t sq = pairs_total + L->grs[lo] + int64_t(q - L->gib[lo]) * L->gw[lo];
       a.item_range[q] = range_of(static_cast<int>(sq)) |
-                        (range_of(static_cast<int>(sq + P.gw[lo] - 1)) << 16);
+                        (range_of(static_cast<int>(sq + L->gw[lo] - 1)) << 16);
     }
   }
 }
@@ -264,14 +322,14 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P) {
 // GP: MFMA head-group width (2, 4 or 8); 0 for the VALU decode.
 // Work-group (hx, b) of the pre-pass grid (Hkv + 1, B) (Hkv, B for the
 // VALU decode), with its LDS.
-template <int GP>
+template <int GP, bool PRE = false>
 __device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int b,
                                                PrologueLds<(GP > 0 ? GP : kMaxGroup)>& Lq,
-                                               PlanLds& P) {
+                                               PlanLds& P, GroupLds* L = nullptr) {
   constexpr int KG = GP > 0 ? GP : kMaxGroup;   // query heads per KV head held
   if constexpr (GP > 0) {
     if (hx == a.n_kv_heads) {
-      if (b == 0) plan_ranges<GP>(a, P);
+      if (b == 0) plan_ranges<GP, PRE>(a, P, L);
       return;
     }
   }
@@ -415,6 +473,16 @@ __global__ __launch_bounds__(256, 5) void prologue_kernel(DecodeArgs a) {
   __shared__ PrologueLds<(GP > 0 ? GP : kMaxGroup)> Lq;
   __shared__ PlanLds P;
   prologue_block<GP>(a, blockIdx.x, blockIdx.y, Lq, P);
+}
+
+// The pre-pass of a decode with shared-prefix groups (MFMA decode): the
+// plan also resolves the groups (GroupLds).
+template <int GP>
+__global__ __launch_bounds__(256) void prologue_prefix_kernel(DecodeArgs a) {
+  __shared__ PrologueLds<GP> Lq;
+  __shared__ PlanLds P;
+  __shared__ GroupLds L;
+  prologue_block<GP, true>(a, blockIdx.x, blockIdx.y, Lq, P, &L);
 }
 
 // The pre-pass of a fused decode step: the work-groups of the decode-step
@@ -587,7 +655,11 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
   const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch);
-  if (a.gp == 2) hipLaunchKernelGGL(prologue_kernel<2>, pgrid, dim3(256), 0, st, a);
+  if (a.n_groups > 0) {
+    if (a.gp == 2) hipLaunchKernelGGL(prologue_prefix_kernel<2>, pgrid, dim3(256), 0, st, a);
+    else if (a.gp == 4) hipLaunchKernelGGL(prologue_prefix_kernel<4>, pgrid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(prologue_prefix_kernel<8>, pgrid, dim3(256), 0, st, a);
+  } else if (a.gp == 2) hipLaunchKernelGGL(prologue_kernel<2>, pgrid, dim3(256), 0, st, a);
   else if (a.gp == 4) hipLaunchKernelGGL(prologue_kernel<4>, pgrid, dim3(256), 0, st, a);
   else if (a.gp == 8) hipLaunchKernelGGL(prologue_kernel<8>, pgrid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(prologue_kernel<0>, pgrid, dim3(256), 0, st, a);

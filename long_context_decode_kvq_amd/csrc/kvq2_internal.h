@@ -66,7 +66,7 @@ struct DecodePlan {
 // largest number of groups.
 constexpr int kGrpInfo = 8;
 constexpr int kMaxPrefixGroups = 256;
-constexpr int kMaxPrefixMembers = 1 << 24;
+constexpr int kMaxPrefixMembers = 1024;
 
 // Upper bound of the MFMA decode's work-group count (resident work-groups of
 // the device, 256 CUs x 4); its partial slots number kChainGroups + B * Hkv,

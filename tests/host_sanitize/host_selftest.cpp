@@ -119,9 +119,12 @@ int main() {
     kvq_prefix_groups null_arrays = {1, 2, nullptr, i32, i32};
     CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &null_arrays, ws, needp, nullptr) == KVQ_ERR_ARG);
     // member counts large enough to overflow the 32-bit virtual tile count
-    kvq_prefix_groups big = {256, 1 << 24, i32, i32, i32};
-    CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &big, ws, 1 << 30, nullptr) == KVQ_ERR_UNSUPPORTED);
-    kvq_prefix_groups too_many = {256, (1 << 24) + 1, i32, i32, i32};
+    // the row-set items' tiles overflow the 32-bit virtual tile count
+    kvq_prefix_groups big = {256, 1024, i32, i32, i32};
+    kvq_cache long_c = c;
+    long_c.bt_stride = 1 << 18;
+    CHECK(kvq_decode_prefix_attention(&d, &lay, &long_c, 2, i32, 1 << 22, u16, f32, &big, ws, size_t(1) << 40, nullptr) == KVQ_ERR_UNSUPPORTED);
+    kvq_prefix_groups too_many = {256, 1025, i32, i32, i32};
     CHECK(kvq_decode_prefix_workspace_bytes(&d, 2, 100, &too_many) == 0);
     CHECK(kvq_decode_prefix_attention(&d, &lay, &c, 2, i32, 100, u16, f32, &too_many, ws, 1 << 30, nullptr) == KVQ_ERR_ARG);
   }
