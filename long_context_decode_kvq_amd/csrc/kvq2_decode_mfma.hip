@@ -84,7 +84,10 @@ int resident_work_groups() {
 // each still gets kMinTilesPerCuGroup tiles, so that small batches fill the
 // GPU (measured at batch 1: 32768 tokens 46.8 -> 37.4 us per step with 256
 // work-groups instead of 64; more than one round of small ranges was slower).
-constexpr int kMinTilesPerGroup = 128;
+// 64 tiles per work-group: one sequence of 131072 tokens (32768 tiles over 8
+// KV heads) decodes in 40.5 us with 512 work-groups, 47.5 us with 256 (128
+// tiles each) and 52.7 us with 1024 (32 tiles each).
+constexpr int kMinTilesPerGroup = 64;
 constexpr int kMinTilesPerCuGroup = 32;
 
 template <int GP, int NG>
