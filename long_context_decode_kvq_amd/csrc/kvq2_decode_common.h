@@ -537,7 +537,7 @@ __device__ __forceinline__ int rowset_slots(const DecodeArgs& a, int b, int h, i
   return i1 - i0 + 1;
 }
 
-// Split-K combine of one (b, h), by a work-group of 256 threads in a kernel
+// Split-K combine of one (b, h), by a work-group of NT (256 or 512) threads in a kernel
 // of its own: the partials in slots [base_slot, base_slot + n_parts) and
 // [tok_slot, tok_slot + n_tok), with M = max m_s, f_s = 2^(m_s - M):
 // o' = sum f_s o'_s / sum f_s l_s, then o = R_V o' to `out`.  The slots are
@@ -546,18 +546,20 @@ __device__ __forceinline__ int rowset_slots(const DecodeArgs& a, int b, int h, i
 // after the first slice's: the wait for a slice then leaves R_V in flight,
 // so the call's critical path is one round trip to the partials.  The (m, l)
 // of a slice are staged in LDS per head, read back as vectors.
-template <int GP, bool RSL = false>
+template <int GP, bool RSL = false, int NT = 256>
 __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slot, int n_parts,
                              int64_t tok_slot, int n_tok, int64_t rs_slot = 0, int n_rs = 0) {
   constexpr int kSlice = 16;
-  constexpr int KO = (GP * kHeadDim + 255) / 256;   // outputs per thread
+  constexpr int KO = (GP * kHeadDim + NT - 1) / NT;   // outputs per thread
+  constexpr int NS = NT / kHeadDim;                   // parts of an R_V row
+  constexpr int RC = kHeadDim / NS;                   // R_V columns per thread
   __shared__ __attribute__((aligned(16))) float s_m[GP][kSlice];
   __shared__ __attribute__((aligned(16))) float s_l[GP][kSlice];
   __shared__ float ocomb[GP][kHeadDim];
-  __shared__ float red[2][GP][kHeadDim];
+  __shared__ float red[NS][GP][kHeadDim];
   const int G = a.group;
   const int tid = threadIdx.x;
-  const int ri = tid & (kHeadDim - 1), half = tid >> 7;
+  const int ri = tid & (kHeadDim - 1), part = tid / kHeadDim;
   auto slot_ptr = [&](int i) -> const float* {
     int64_t s = i < n_parts ? base_slot + i : tok_slot + (i - n_parts);
     if constexpr (RSL) s = i < n_parts + n_tok ? s : rs_slot + 4 * int64_t(i - n_parts - n_tok);
@@ -567,7 +569,7 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   float M[KO], den[KO], acc[KO];
 #pragma unroll
   for (int k = 0; k < KO; ++k) {
-    const int o = tid + 256 * k;
+    const int o = tid + NT * k;
     gk[k] = min(o / kHeadDim, G - 1);   // rows past G load head G - 1 and are not stored
     ck[k] = o % kHeadDim;
     M[k] = -INFINITY;
@@ -592,12 +594,12 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   if (n_all > 0) load_slice(0, min(kSlice, n_all));
   // keep R_V's loads behind the slice's in issue order
   asm volatile("" ::: "memory");
-  float4 r[16];
+  float4 r[RC / 4];
   {
     const float4* row = reinterpret_cast<const float4*>(
-        a.R_V + int64_t(h) * kHeadDim * kHeadDim + ri * kHeadDim + 64 * half);
+        a.R_V + int64_t(h) * kHeadDim * kHeadDim + ri * kHeadDim + RC * part);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) r[j] = row[j];
+    for (int j = 0; j < RC / 4; ++j) r[j] = row[j];
   }
   for (int s0 = 0; s0 < n_all; s0 += kSlice) {
     const int ns = min(kSlice, n_all - s0);
@@ -639,31 +641,35 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   }
 #pragma unroll
   for (int k = 0; k < KO; ++k) {
-    const int o = tid + 256 * k;
+    const int o = tid + NT * k;
     if (o < G * kHeadDim) ocomb[gk[k]][ck[k]] = den[k] > 0.f ? acc[k] / den[k] : 0.f;
   }
   __syncthreads();
-  // o = R_V o' (row-major R_V: o_i = sum_j R_V[i][j] o'_j); thread (half, i)
-  // holds half of row i and applies it to every head; the halves meet in LDS.
+  // o = R_V o' (row-major R_V: o_i = sum_j R_V[i][j] o'_j); thread (part, i)
+  // holds one of NS parts of row i and applies it to every head; the parts
+  // meet in LDS.
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
     if (g < G) {
-      const float* oc = &ocomb[g][64 * half];
+      const float* oc = &ocomb[g][RC * part];
       float o = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < RC / 4; ++j) {
         o = fmaf(r[j].x, oc[4 * j + 0], o);
         o = fmaf(r[j].y, oc[4 * j + 1], o);
         o = fmaf(r[j].z, oc[4 * j + 2], o);
         o = fmaf(r[j].w, oc[4 * j + 3], o);
       }
-      red[half][g][ri] = o;
+      red[part][g][ri] = o;
     }
   }
   __syncthreads();
-  for (int k = tid; k < G * kHeadDim; k += blockDim.x) {
+  for (int k = tid; k < G * kHeadDim; k += NT) {
     const int g = k / kHeadDim, c = k % kHeadDim;
-    a.out[row_offset(a, b, h, g) + c] = red[0][g][c] + red[1][g][c];
+    float o = red[0][g][c];
+#pragma unroll
+    for (int q = 1; q < NS; ++q) o += red[q][g][c];
+    a.out[row_offset(a, b, h, g) + c] = o;
   }
 }
 

@@ -140,7 +140,8 @@ int launch_decode_mfma(const DecodeArgs& a, int batch, int max_seq_len, void* st
   const dim3 grid(a.chain_groups + a.batch * a.n_kv_heads * a.n_tok_slices);
   const bool per_head = 2 * a.batch * a.n_kv_heads < std::max(1, device_cus());
   const dim3 cgrid(a.n_kv_heads, a.batch, per_head ? a.group : 1);
-  const dim3 cblock(per_head ? 128 * kHeadCombineParts : 256);
+  const dim3 cblock(per_head ? 128 * kHeadCombineParts
+                             : (a.gp == 2 ? combine_threads<2>() : combine_threads<4>()));
   if (a.n_groups > 0) {
     launch_decode_mfma_prefix(a, grid.x, per_head, stream);
   } else if (G <= 2) {

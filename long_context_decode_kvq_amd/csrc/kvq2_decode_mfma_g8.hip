@@ -22,7 +22,7 @@ void launch_decode_mfma_g8(const DecodeArgs& a, unsigned grid, bool per_head, vo
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL((decode_mfma_kernel<8, 1>), dim3(grid), dim3(256), 0, st, a);
   const dim3 cgrid(a.n_kv_heads, a.batch, per_head ? a.group : 1);
-  const dim3 cblock(per_head ? 128 * kHeadCombineParts : 256);
+  const dim3 cblock(per_head ? 128 * kHeadCombineParts : combine_threads<8>());
   if (per_head) hipLaunchKernelGGL(combine_head_kernel<8>, cgrid, cblock, 0, st, a);
   else hipLaunchKernelGGL(combine_kernel<8>, cgrid, cblock, 0, st, a);
 }
@@ -33,7 +33,7 @@ void launch_decode_mfma_g8_prefix(const DecodeArgs& a, unsigned grid, bool per_h
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL((decode_mfma_kernel<8, 1, true>), dim3(grid), dim3(256), 0, st, a);
   const dim3 cgrid(a.n_kv_heads, a.batch, per_head ? a.group : 1);
-  const dim3 cblock(per_head ? 128 * kHeadCombineParts : 256);
+  const dim3 cblock(per_head ? 128 * kHeadCombineParts : combine_threads<8>());
   if (per_head) hipLaunchKernelGGL((combine_head_kernel<8, true>), cgrid, cblock, 0, st, a);
   else hipLaunchKernelGGL((combine_kernel<8, true>), cgrid, cblock, 0, st, a);
 }

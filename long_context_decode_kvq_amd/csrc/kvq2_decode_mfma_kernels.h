@@ -1165,8 +1165,13 @@ __global__ __launch_bounds__(256, GP <= 4 ? (NG == 1 ? 4 : 3) : 2) void decode_m
 // head) when there are few (sequence, KV head) pairs, so that a small
 // batch's combine spreads over more CUs and takes its many splits in one
 // round (combine_head_kernel).
+// Threads of a combine_kernel work-group: 512 for eight heads (four outputs
+// per thread of 256 would hold 250 VGPRs), else 256.
+template <int GP>
+constexpr int combine_threads() { return GP == 8 ? 512 : 256; }
+
 template <int GP, bool PRE = false>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(combine_threads<GP>()) void combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int p = b * a.n_kv_heads + h;
   const int pr = a.pair_range[p];
@@ -1174,7 +1179,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int64_t tok = a.tok_slot0 + int64_t(p) * a.n_tok_slices;
   int64_t rs = 0;
   const int n_rs = PRE ? rowset_slots(a, b, h, rs) : 0;
-  combine_pair<GP, PRE>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, tok, a.n_tok_slices, rs, n_rs);
+  combine_pair<GP, PRE, combine_threads<GP>()>(a, b, h, int64_t(i0) + p, i1 - i0 + 1, tok,
+                                              a.n_tok_slices, rs, n_rs);
 }
 
 constexpr int kHeadCombineParts = 8;   // 128-thread parts of a combine_head_kernel work-group

@@ -16,7 +16,8 @@ void launch_decode_mfma_g8_prefix(const DecodeArgs& a, unsigned grid, bool per_h
 void launch_decode_mfma_prefix(const DecodeArgs& a, unsigned grid, bool per_head, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 cgrid(a.n_kv_heads, a.batch, per_head ? a.group : 1);
-  const dim3 cblock(per_head ? 128 * kHeadCombineParts : 256);
+  const dim3 cblock(per_head ? 128 * kHeadCombineParts
+                             : (a.gp == 2 ? combine_threads<2>() : combine_threads<4>()));
   if (a.gp == 2) {
     hipLaunchKernelGGL((decode_mfma_kernel<2, 1, true>), dim3(grid), dim3(256), 0, st, a);
     if (per_head) hipLaunchKernelGGL((combine_head_kernel<2, true>), cgrid, cblock, 0, st, a);
