@@ -555,7 +555,7 @@ __device__ void combine_pair(const DecodeArgs& a, int b, int h, int64_t base_slo
   constexpr int RC = kHeadDim / NS;                   // R_V columns per thread
   __shared__ __attribute__((aligned(16))) float s_m[GP][kSlice];
   __shared__ __attribute__((aligned(16))) float s_l[GP][kSlice];
-  __shared__ float ocomb[GP][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float ocomb[GP][kHeadDim];
   __shared__ float red[NS][GP][kHeadDim];
   const int G = a.group;
   const int tid = threadIdx.x;

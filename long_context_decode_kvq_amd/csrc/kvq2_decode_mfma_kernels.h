@@ -1166,12 +1166,16 @@ __global__ __launch_bounds__(256, GP <= 4 ? (NG == 1 ? 4 : 3) : 2) void decode_m
 // batch's combine spreads over more CUs and takes its many splits in one
 // round (combine_head_kernel).
 // Threads of a combine_kernel work-group: 512 for eight heads (four outputs
-// per thread of 256 would hold 250 VGPRs), else 256.
+// per thread of 256 would hold 250 VGPRs), else 256.  The eight-head
+// combine keeps two work-groups per CU (four waves per SIMD, at most 128
+// VGPRs), so that the 512 (sequence, KV head) pairs of a 64-sequence batch
+// run in one round.
 template <int GP>
 constexpr int combine_threads() { return GP == 8 ? 512 : 256; }
 
 template <int GP, bool PRE = false>
-__global__ __launch_bounds__(combine_threads<GP>()) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(combine_threads<GP>(), GP == 8 ? 4 : 1) void combine_kernel(
+    DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int p = b * a.n_kv_heads + h;
   const int pr = a.pair_range[p];
