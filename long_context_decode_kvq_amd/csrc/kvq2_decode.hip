@@ -15,11 +15,21 @@ namespace kvq {
 
 namespace {
 
-// LDS of the range plan and of the q-rotation pre-pass.
+// Threads of every pre-pass work-group (a constant: blockDim is an implicit
+// kernel argument, and each read of one that missed the scalar cache cost
+// the plan a memory latency).
+constexpr int kPrePassThreads = 256;
+
+// LDS of the range plan and of the q-rotation pre-pass.  The plan keeps
+// W_b and the tile prefix of the first kPlanSeq sequences in LDS for the
+// pair ranges (later sequences read them back from global memory).
+constexpr int kPlanSeq = 1024;
 struct PlanLds {
   int scan[256];
   int carry;
   int rs[kChainGroups + 1];
+  int w[kPlanSeq];         // W_b
+  int pre[kPlanSeq];       // tile prefix before sequence b
 };
 
 // LDS of the plan's shared-prefix groups (prefix-aware decodes only).
@@ -68,7 +78,7 @@ __device__ __forceinline__ int seq_skip_tiles(const GroupLds& L, int b) {
 template <int GP>
 __device__ void plan_groups(const DecodeArgs& a, GroupLds& L) {
   constexpr int npt = chunks_per_tile(GP);
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = kPrePassThreads;
   const int ngr = a.n_groups, B = a.batch, Hkv = a.n_kv_heads;
   const int cf = (a.n_sink + kChunkTokens - 1) / kChunkTokens;
   for (int g = tid; g <= ngr; g += nt) {
@@ -188,6 +198,19 @@ template <int GP, bool PRE = false>
 __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P, GroupLds* L = nullptr) {
   constexpr int npt = chunks_per_tile(GP);
   const int tid = threadIdx.x;
+  // Every argument the plan reads is loaded here, in one batch of scalar
+  // loads waited for once: fetched where each is first used, the argument
+  // block's cache lines missed one after another, a memory latency each.
+  {
+    int v[13] = {a.batch, a.n_sink, a.n_recent, a.piece_cost, a.chain_groups, a.n_kv_heads,
+                 a.round_size, a.round_weight[0], a.round_weight[1], a.round_weight[2],
+                 a.round_weight[3], a.xcd_weight[0], a.xcd_weight[7]};
+#pragma unroll
+    for (int k = 0; k < 13; ++k) asm volatile("" : : "s"(v[k]));
+    const void* ptr[4] = {a.seq_len, a.tile_prefix, a.range_start, a.pair_range};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("" : : "s"(ptr[k]));
+  }
   // W_b = max(1, whole INT2 tiles of sequence b) + piece_cost;
   // tile_prefix[b] = W_0 + ... + W_{b-1} (inclusive Hillis-Steele scan
   // over blocks of 256 sequences).
@@ -214,6 +237,10 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P, GroupLds* L = nullp
       __syncthreads();
     }
     if (bb < a.batch) a.tile_prefix[bb + 1] = carry + scan[tid];
+    if (bb < a.batch && bb < kPlanSeq) {
+      P.w[bb] = w;
+      P.pre[bb] = carry + scan[tid] - w;
+    }
     __syncthreads();
     if (tid == 255) carry += scan[255];
     __syncthreads();
@@ -234,79 +261,95 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P, GroupLds* L = nullp
   // Work-group j weighs round_weight[j / rsz] * xcd_weight[j % 8]; range i
   // starts at total * (weight of work-groups < i) / (weight of all).  A round
   // (rsz, a multiple of 8 when weighted) holds every XCD rsz / 8 times.
-  // The weights are held in registers and the loops have fixed trip counts:
-  // read from the argument block term by term, the dependent loads made this
-  // cut the longest part of the pre-pass.
+  // Each thread's cut is a closed form in 32-bit integers and fp64 (exact:
+  // every weight sum stays below 2^53) on weights held in registers: 64-bit
+  // integer products and divisions per range made this loop the longest part
+  // of the pre-pass, and so did reading the weights from the argument block.
   int xw[8], rw[4];
 #pragma unroll
   for (int x = 0; x < 8; ++x) xw[x] = a.xcd_weight[x];
 #pragma unroll
   for (int r = 0; r < 4; ++r) rw[r] = a.round_weight[r];
-  int64_t xsum = 0;
+  int xsum = 0;
 #pragma unroll
   for (int x = 0; x < 8; ++x) xsum += xw[x];
-  auto xcd_prefix = [&](int64_t k) {   // sum of xcd_weight[j % 8] over j < k (k >= 0)
-    int64_t c = (k >> 3) * xsum;
-    const int m = static_cast<int>(k & 7);
+  // weight of the first k work-groups of one round, over its xcd weights
+  auto xcd_prefix = [&](int k) {
+    int c = (k >> 3) * xsum;
+    const int m = k & 7;
 #pragma unroll
     for (int x = 0; x < 7; ++x) c += x < m ? xw[x] : 0;
     return c;
   };
-  int64_t ctot = 0;
+  const double round_w = xcd_prefix(rsz);   // xcd weight of one whole round
+  double ctot = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    if (r < rounds) ctot += int64_t(rw[r]) * xcd_prefix(rsz);
+    if (r < rounds) ctot += double(rw[r]) * round_w;
   const int64_t q = (total + nwg - 1) / nwg;
-  for (int i = tid; i <= nwg; i += blockDim.x) {
-    int64_t v;
+  // total * c / ctot: monotone in c, truncated, and range nwg ends exactly
+  // at total (total < 2^31: range starts are 32-bit)
+  const double scale = double(total) / (ctot > 0 ? ctot : 1.0);
+  const double dtotal = double(total);
+  for (int i = tid; i <= nwg; i += kPrePassThreads) {
+    int v;
     if (!weighted) {
-      v = min(total, int64_t(i) * q);
+      v = static_cast<int>(min(total, int64_t(i) * q));
     } else {
-      int64_t c = 0;
+      const int r0 = min(i / rsz, rounds);   // i's round (rounds at i == nwg)
+      double c = 0;   // whole rounds before r0
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (r < rounds) {
-          const int64_t lo = int64_t(r) * rsz;
-          const int64_t cnt = i <= lo ? 0 : min(int64_t(i), lo + rsz) - lo;
-          c += int64_t(rw[r]) * xcd_prefix(cnt);
-        }
-      }
-      v = total * c / ctot;
+      for (int r = 0; r < 4; ++r) c += r < r0 ? double(rw[r]) * round_w : 0.0;
+      const int rw0 = r0 == 0 ? rw[0] : r0 == 1 ? rw[1] : r0 == 2 ? rw[2] : r0 == 3 ? rw[3] : 0;
+      c += double(rw0) * double(xcd_prefix(i - r0 * rsz));
+      v = i == nwg ? static_cast<int>(total) : static_cast<int>(fmin(dtotal, trunc(c * scale)));
     }
-    rs[i] = static_cast<int>(v);
-    a.range_start[i] = static_cast<int>(v);
+    rs[i] = v;
+    a.range_start[i] = v;
   }
   __syncthreads();
-  auto range_of = [&](int x) {   // largest i < nwg with rs[i] <= x
-    int lo = 0, hi = nwg;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (rs[mid] <= x) lo = mid; else hi = mid;
+  // (largest i < nwg with rs[i] <= x0) | (the same for x1) << 16: both
+  // searches in one loop of power-of-two steps, so that their dependent LDS
+  // reads overlap (rs[0] = 0 <= x)
+  int top = 1;
+  while (2 * top < nwg) top *= 2;
+  auto range_pair = [&](int x0, int x1) {
+    int i0 = 0, i1 = 0;
+    for (int st = top; st > 0; st >>= 1) {
+      const int j0 = min(i0 + st, nwg - 1), j1 = min(i1 + st, nwg - 1);
+      const int r0 = rs[j0], r1 = rs[j1];
+      if (r0 <= x0) i0 = j0;
+      if (r1 <= x1) i1 = j1;
     }
-    return lo;
+    return i0 | (i1 << 16);
   };
-  for (int pr = tid; pr < a.batch * Hkv; pr += blockDim.x) {
+  for (int pr = tid; pr < a.batch * Hkv; pr += kPrePassThreads) {
     const int bb = pr / Hkv, hh = pr % Hkv;
-    const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
-    int skip = 0;
-    if constexpr (PRE) skip = seq_skip_tiles(*L, bb);
-    const int wbb = max(1, (rg.cl - rg.cf) / npt - skip) + a.piece_cost;
-    // the prefix of bb, recomputed from the scan output in global memory
-    const int sp = Hkv * a.tile_prefix[bb] + hh * wbb;
-    a.pair_range[pr] = range_of(sp) | (range_of(sp + wbb - 1) << 16);
+    int wbb, pre_b;
+    if (bb < kPlanSeq) {
+      wbb = P.w[bb];
+      pre_b = P.pre[bb];
+    } else {   // recomputed, and the prefix read back from the scan output
+      const Int2Range rg = int2_range(a, a.seq_len[bb], npt);
+      int skip = 0;
+      if constexpr (PRE) skip = seq_skip_tiles(*L, bb);
+      wbb = max(1, (rg.cl - rg.cf) / npt - skip) + a.piece_cost;
+      pre_b = a.tile_prefix[bb];
+    }
+    const int sp = Hkv * pre_b + hh * wbb;
+    a.pair_range[pr] = range_pair(sp, sp + wbb - 1);
   }
   // first and last range of every row-set item
   if constexpr (PRE) {
     const int ngr = a.n_groups;
-    for (int q = tid; q < L->gib[ngr]; q += blockDim.x) {
+    for (int q = tid; q < L->gib[ngr]; q += kPrePassThreads) {
       int lo = 0, hi = ngr;   // group of item q: the largest g with gib[g] <= q
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (L->gib[mid] <= q) lo = mid; else hi = mid;
       }
       const int64_t sq = pairs_total + L->grs[lo] + int64_t(q - L->gib[lo]) * L->gw[lo];
-      a.item_range[q] = range_of(static_cast<int>(sq)) |
-                        (range_of(static_cast<int>(sq + L->gw[lo] - 1)) << 16);
+      a.item_range[q] = range_pair(static_cast<int>(sq), static_cast<int>(sq + L->gw[lo] - 1));
     }
   }
 }
@@ -384,14 +427,14 @@ __device__ __forceinline__ void prologue_block(const DecodeArgs& a, int hx, int 
   }
   __syncthreads();
   float* dst = a.qrot + qrot_offset(a, b, h);
-  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
+  for (int i = tid; i < G * kHeadDim; i += kPrePassThreads) {
     const int g = i / kHeadDim, c = i % kHeadDim;
     const float v = (part[0][g][c] + part[1][g][c]) * a.alpha;
     qs[g][c] = v;
     dst[g * kQStride + c] = v;
   }
   __syncthreads();
-  for (int g = wave; g < G; g += blockDim.x / 64) {
+  for (int g = wave; g < G; g += kPrePassThreads / 64) {
     const float v0 = qs[g][lane], v1 = qs[g][lane + 64];
     const float sum = wave_sum(v0 + v1);
     const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
