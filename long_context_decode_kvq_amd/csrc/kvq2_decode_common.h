@@ -310,9 +310,10 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
       kind == 2 ? gbase + param_offset(0, ts, ng, (qq * ng) >> 2) : gpool);
   // Values: one dword per lane and token (bf16: channels 2 lane, 2 lane + 1
   // of the value row; INT2: the dword holding this lane's code byte), and
-  // for INT2 tokens the (s_V, z_V) pair of the lane's value group: with one
-  // group the same for every lane, through the scalar cache.
-  typedef const uint32_t __attribute__((address_space(4))) const_u32;
+  // for INT2 tokens the (s_V, z_V) pair of the lane's value group.  Every
+  // one is a vector load on one path: a scalar load under a branch on the
+  // group count made the compiler wait for all earlier vector loads before
+  // each token's, sixteen memory latencies per tile.
   uint32_t vword[16], vpar[16];
   int vkind[16];
   const int cg = lane >> 1, vgrp = (lane * ng) >> 6;
@@ -324,20 +325,14 @@ __device__ void token_tile(const DecodeArgs& a, int b, int h, const TokenList& t
     const int boff = kVCodesOff + 32 * (cg & 15) + 8 * (s >> 2) + 4 * (cg >> 4);   // + (s & 3)
     const int woff = vkind[tt] == 1 ? 2 * kHeadDim + 4 * lane : boff;
     vword[tt] = *reinterpret_cast<global_u32*>(bp + woff);
-    if (ng == 1) {
-      const uint8_t* pp = vkind[tt] == 2 ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(bp)) + kVParamsOff + 4 * s
-                                         : a.pool;
-      vpar[tt] = *reinterpret_cast<const_u32*>(reinterpret_cast<uintptr_t>(pp));
-    } else {
-      vpar[tt] = *reinterpret_cast<global_u32*>(
-          vkind[tt] == 2 ? bp + param_offset(1, s, ng, vgrp) : gpool);
-    }
+    vpar[tt] = *reinterpret_cast<global_u32*>(vkind[tt] == 2 ? bp + param_offset(1, s, ng, vgrp)
+                                                               : gpool);
   }
   // Empty asm statements take the loaded values here: the compiler would
   // otherwise sink each load into the branch that uses it, one wait per load.
   asm volatile("" : "+v"(kb[0]), "+v"(kb[1]), "+v"(kb[2]), "+v"(kb[3]), "+v"(kc), "+v"(kpar));
 #pragma unroll
-  for (int tt = 0; tt < 16; ++tt) asm volatile("" : "+v"(vword[tt]));
+  for (int tt = 0; tt < 16; ++tt) asm volatile("" : "+v"(vword[tt]), "+v"(vpar[tt]));
   // ---- logits
   float dot[GP];
 #pragma unroll
