@@ -13,10 +13,11 @@ device; the cache is built before timing (inputs resident in HBM).
 
 Prints one JSON line: value = algorithmic bytes per step / step time (GB/s),
 with the K timed steps run back to back between one pair of HIP events;
-ms_per_step; a roofline object for the decode launch (algorithmic bytes per
-launch / its average duration, from HIP events recorded on the launch stream
-around each of K decode launches over the cache after the last step); and
-the CPU oracle timed on a bounded sample.
+ms_per_step; a roofline object for the decode call (algorithmic bytes per
+call / its average duration: K calls over the cache after the last step run
+back to back as one HIP graph between two events on their stream; the
+spread comes from K more calls, each between its own event pair); and the
+CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -422,6 +423,8 @@ def run_hqmq(args):
         step(k, stream)
     torch.cuda.synchronize()
     graph = None
+    last = args.warmup + args.steps - 1
+    dgraph = None
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
@@ -429,6 +432,12 @@ def run_hqmq(args):
         with torch.cuda.graph(graph, stream=cap):
             for i in range(args.steps):
                 step(args.warmup + i, cap)
+        torch.cuda.synchronize()
+        # the decode call alone, K times back to back (see main())
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph, stream=cap):
+            for _ in range(args.steps):
+                decode_call(handles[last % copies], seqs[last], qs[last], cap)
         torch.cuda.synchronize()
     # untimed pre-warm (decode calls only read the cache)
     t_pre, n_pre = time.perf_counter(), 0
@@ -447,7 +456,12 @@ def run_hqmq(args):
         for i in range(args.steps):
             step(args.warmup + i, stream)
     e_end.record(stream)
-    last = args.warmup + args.steps - 1
+    d_begin = torch.cuda.Event(enable_timing=True)
+    d_end = torch.cuda.Event(enable_timing=True)
+    if dgraph is not None:
+        d_begin.record(stream)
+        dgraph.replay()
+        d_end.record(stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for a0, a1 in ev:
@@ -457,7 +471,9 @@ def run_hqmq(args):
     torch.cuda.synchronize()
     ms_per_step = e_begin.elapsed_time(e_end) / args.steps
     dec_ms = np.array([a0.elapsed_time(a1) for a0, a1 in ev])
-    dec_avg_ms = float(np.mean(dec_ms))
+    dec_event_avg_ms = float(np.mean(dec_ms))
+    dec_avg_ms = (d_begin.elapsed_time(d_end) / args.steps if dgraph is not None
+                  else dec_event_avg_ms)
     pct = {p: float(np.percentile(dec_ms, p)) * 1e3 for p in (10, 50, 90)}
     step_bytes = [hqmq_decode_bytes(w, lens_before + args.warmup + i + 1, S) +
                   hqmq_append_bytes(w, 1, S) for i in range(args.steps)]
@@ -491,6 +507,9 @@ def run_hqmq(args):
                        else f"one HIP graph of the {args.steps} steps, replayed once"),
             "us_per_step": round(ms_per_step * 1e3, 2),
             "decode_us": round(dec_avg_ms * 1e3, 2),
+            "decode_timing": ("one HIP graph of the K decode calls between two events"
+                              if dgraph is not None else "an event pair around each call"),
+            "decode_event_us_mean": round(dec_event_avg_ms * 1e3, 2),
             "decode_us_p10": round(pct[10], 2),
             "decode_us_p50": round(pct[50], 2),
             "decode_us_p90": round(pct[90], 2),
@@ -659,6 +678,8 @@ def main():
     # serving loop launches its decode step that way, and at batch 1 the
     # per-call host cost of launching from Python exceeds the GPU time.
     graph = None
+    last = args.warmup + args.steps - 1
+    dgraph = None
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
@@ -666,6 +687,14 @@ def main():
         with torch.cuda.graph(graph, stream=cap):
             for i in range(args.steps):
                 step(args.warmup + i, cap)
+        torch.cuda.synchronize()
+        # the decode call alone, K times back to back over the cache after
+        # the last step: one graph, timed by one event pair (an event pair
+        # around each call adds its own GPU time, ~10 us per call)
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph, stream=cap):
+            for _ in range(args.steps):
+                decode_call(handles[last % copies], seqs[last], qs[last], cap)
         torch.cuda.synchronize()
 
     # ---- untimed pre-warm: back-to-back decode calls over the cache (whose
@@ -706,11 +735,17 @@ def main():
         for i in range(args.steps):
             step(args.warmup + i, stream)
     e_end.record(stream)
-    # The decode launch on its own, for the roofline: K launches over the
-    # cache after the last step, each bracketed by HIP events on the stream it
-    # is launched on, queued behind the timed steps (no idle gap: the GPU
-    # stays in its sustained-load state).
-    last = args.warmup + args.steps - 1
+    # The decode call on its own, for the roofline, queued behind the timed
+    # steps (no idle gap: the GPU stays in its sustained-load state): K calls
+    # over the cache after the last step as one graph between two events on
+    # the stream they run on (the average), then K calls each bracketed by
+    # its own event pair (the spread; those times include the events' cost).
+    d_begin = torch.cuda.Event(enable_timing=True)
+    d_end = torch.cuda.Event(enable_timing=True)
+    if dgraph is not None:
+        d_begin.record(stream)
+        dgraph.replay()
+        d_end.record(stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for a0, a1 in ev:
@@ -720,7 +755,9 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = e_begin.elapsed_time(e_end) / args.steps
     dec_ms = np.array([a0.elapsed_time(a1) for a0, a1 in ev])
-    dec_avg_ms = float(np.mean(dec_ms))
+    dec_event_avg_ms = float(np.mean(dec_ms))
+    dec_avg_ms = (d_begin.elapsed_time(d_end) / args.steps if dgraph is not None
+                  else dec_event_avg_ms)
     pct = {p: float(np.percentile(dec_ms, p)) * 1e3 for p in (10, 50, 90)}
 
     step_bytes = []
@@ -736,8 +773,9 @@ def main():
     # every sequence attends to, unique counts each physical page once.
     dec_unique = dec_bytes - shared_prefix_repeat_bytes(w, sharers, ng)
     log(f"[bench] pre-warm {n_pre} decode calls in {prewarm_wall:.2f}s; step "
-        f"{ms_per_step * 1e3:.1f} us; decode {dec_avg_ms * 1e3:.1f} us (p10 {pct[10]:.1f}, "
-        f"p50 {pct[50]:.1f}, p90 {pct[90]:.1f}); decode {achieved:.0f} GB/s = "
+        f"{ms_per_step * 1e3:.1f} us; decode {dec_avg_ms * 1e3:.1f} us (each call between "
+        f"events: mean {dec_event_avg_ms * 1e3:.1f}, p10 {pct[10]:.1f}, p50 {pct[50]:.1f}, "
+        f"p90 {pct[90]:.1f}); decode {achieved:.0f} GB/s = "
         f"{100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s")
 
     ceiling = None
@@ -790,9 +828,13 @@ def main():
                        else f"one HIP graph of the {args.steps} steps, replayed once"),
             "us_per_step": round(ms_per_step * 1e3, 2),
             "decode_us": round(dec_avg_ms * 1e3, 2),
+            "decode_timing": ("one HIP graph of the K decode calls between two events"
+                              if dgraph is not None else "an event pair around each call"),
+            "decode_event_us_mean": round(dec_event_avg_ms * 1e3, 2),
             "decode_us_p10": round(pct[10], 2),
             "decode_us_p50": round(pct[50], 2),
             "decode_us_p90": round(pct[90], 2),
+            "decode_us_pct_note": "p10/p50/p90 of the calls bracketed each by its own event pair",
             "step_pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "decode_bytes": int(dec_bytes),
         },
