@@ -27,6 +27,8 @@ constexpr int kPlanSeq = 1024;
 struct PlanLds {
   int scan[256];
   int carry;
+  int fbw[12];             // the range weights of this call: XCD [8], round [4]
+  uint32_t fbraw[kFbWords];  // the self-calibration state as the previous call left it
   int rs[kChainGroups + 1];
   int w[kPlanSeq];         // W_b
   int pre[kPlanSeq];       // tile prefix before sequence b
@@ -192,6 +194,63 @@ struct PrologueLds {
   int qexp[KG];
 };
 
+// One step of the self-calibrating range weights (one thread): the mean
+// duration of the ranges of each XCD (and of each dispatch round) measured
+// by the previous call with this state, against the mean of all, scales
+// that XCD's (round's) weight by sqrt(mean / its mean); the weights are
+// then renormalised to a mean of 1024 and clamped to [724, 1448] (each
+// within a factor of two of every other, so that no weighted range is
+// empty), stored, and the sums cleared for this call.  Before the first
+// measurement, and while the ranges last under 50 us, the launch's weights
+// stand.  fb_in: the state as read at the
+// plan's start (LDS); fb: the state itself (written); out: XCD weights [8],
+// round weights [4] for this call.
+__device__ void feedback_update(const uint32_t* fb_in, uint32_t* fb, int rounds, const int* xw0,
+                                const int* rw0, int* out) {
+  int xw[8], rw[4];
+  const bool init = fb_in[kFbXw] != 0;
+  for (int x = 0; x < 8; ++x) xw[x] = init ? static_cast<int>(fb_in[kFbXw + x]) : xw0[x];
+  for (int r = 0; r < 4; ++r) rw[r] = init ? static_cast<int>(fb_in[kFbRw + r]) : rw0[r];
+  double sx[8] = {}, nx[8] = {}, sr[4] = {}, nr[4] = {}, s = 0, n = 0;
+  for (int r = 0; r < rounds; ++r) {
+    for (int x = 0; x < 8; ++x) {
+      const double v = fb_in[kFbSum + 8 * r + x], c = fb_in[kFbCnt + 8 * r + x];
+      sx[x] += v; nx[x] += c; sr[r] += v; nr[r] += c; s += v; n += c;
+    }
+  }
+  // Ranges shorter than kFbMinTicks (batch-1 decodes) are dominated by
+  // fixed latencies, not by their share of the tiles: their launch weights
+  // stand.
+  constexpr double kFbMinTicks = 5000.0;   // 50 us of the 100 MHz clock
+  bool every = n > 0 && s >= kFbMinTicks * n;
+  for (int x = 0; x < 8; ++x) every = every && nx[x] > 0;
+  for (int r = 0; r < rounds; ++r) every = every && nr[r] > 0;
+  if (n > 0 && s < kFbMinTicks * n) {
+    for (int x = 0; x < 8; ++x) xw[x] = xw0[x];
+    for (int r = 0; r < 4; ++r) rw[r] = rw0[r];
+  }
+  if (every) {
+    const double mean = s / n;
+    auto settle = [](int* w, int k, const double* f) {
+      double m = 0;
+      for (int j = 0; j < k; ++j) m += w[j] * f[j];
+      m /= k;
+      for (int j = 0; j < k; ++j)
+        w[j] = min(1448, max(724, static_cast<int>(w[j] * f[j] * 1024.0 / m + 0.5)));
+    };
+    double fx[8], fr[4];
+    for (int x = 0; x < 8; ++x) fx[x] = sqrt(mean / (sx[x] / nx[x]));
+    for (int r = 0; r < rounds; ++r) fr[r] = sqrt(mean / (sr[r] / nr[r]));
+    settle(xw, 8, fx);
+    settle(rw, rounds, fr);
+  }
+  for (int x = 0; x < 8; ++x) fb[kFbXw + x] = static_cast<uint32_t>(xw[x]);
+  for (int r = 0; r < 4; ++r) fb[kFbRw + r] = static_cast<uint32_t>(rw[r]);
+  for (int k = 0; k < 64; ++k) fb[kFbSum + k] = 0u;
+  for (int x = 0; x < 8; ++x) out[x] = xw[x];
+  for (int r = 0; r < 4; ++r) out[8 + r] = rw[r];
+}
+
 // The equal-range plan of the MFMA decode, by one work-group of 256 threads
 // (PRE: with shared-prefix groups, whose LDS is *L).
 template <int GP, bool PRE = false>
@@ -216,6 +275,9 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P, GroupLds* L = nullp
   // over blocks of 256 sequences).
   int* scan = P.scan;
   int& carry = P.carry;
+  // the self-calibration state, read now so that its latency overlaps the
+  // scan's (the scan's barriers publish it)
+  if (a.feedback != nullptr && tid < kFbWords) P.fbraw[tid] = a.feedback[tid];
   if constexpr (PRE) plan_groups<GP>(a, *L);
   if (tid == 0) { carry = 0; a.tile_prefix[0] = 0; }
   __syncthreads();
@@ -270,6 +332,14 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P, GroupLds* L = nullp
   for (int x = 0; x < 8; ++x) xw[x] = a.xcd_weight[x];
 #pragma unroll
   for (int r = 0; r < 4; ++r) rw[r] = a.round_weight[r];
+  if (a.feedback != nullptr && weighted) {
+    if (tid == 0) feedback_update(P.fbraw, a.feedback, rounds, xw, rw, P.fbw);
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 8; ++x) xw[x] = P.fbw[x];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rw[r] = P.fbw[8 + r];
+  }
   int xsum = 0;
 #pragma unroll
   for (int x = 0; x < 8; ++x) xsum += xw[x];
@@ -567,6 +637,10 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) 
 // comes from hipGetSymbolAddress, once per device (static_scratch).
 __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
+// The self-calibrating range-weight states of this GPU (kFb* layout), zero
+// when the library is loaded; addressed like scratch (decode_feedback).
+__device__ __align__(256) uint32_t feedback_state[kFbStates * kFbWords];
+
 }  // namespace
 
 int static_scratch(void** ptr) {
@@ -581,6 +655,23 @@ int static_scratch(void** ptr) {
   std::call_once(once[dev], [dev] {
     // runs with device `dev` current (the caller's current device)
     status[dev] = static_cast<int>(hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)));
+  });
+  if (status[dev] != 0) return status[dev];
+  *ptr = addr[dev];
+  return 0;
+}
+
+int decode_feedback(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices];
+  static int status[kMaxDevices];
+  static std::once_flag once[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::call_once(once[dev], [dev] {
+    status[dev] = static_cast<int>(hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(feedback_state)));
   });
   if (status[dev] != 0) return status[dev];
   *ptr = addr[dev];
@@ -686,6 +777,30 @@ DecodeArgs make_decode_args(const kvq_dims& d, float sm_scale, const kvq_layer& 
   return a;
 }
 
+// The self-calibrating weight state of a launch: one per (G <= 4 or G = 8,
+// 2 .. 4 dispatch rounds); none when the cut is not weighted, when ranges
+// hold fewer than kFbMinTiles tiles (fixed latencies, not the weights, set
+// their durations; measured at one sequence of 131072 tokens the state's
+// bookkeeping only lengthened the pre-pass by ~3 us) or with KVQ_ADAPT=0.
+constexpr int64_t kFbMinTiles = 128;
+int attach_feedback(DecodeArgs& a, int batch, int max_seq_len) {
+  a.feedback = nullptr;
+  if (!decode_tuning().adapt || a.round_size <= 0) return 0;
+  const int rounds = a.chain_groups / a.round_size;
+  if (rounds < 2 || rounds > 4 || rounds * a.round_size != a.chain_groups ||
+      a.round_size % 8 != 0)
+    return 0;
+  const int64_t int2_end = std::max<int64_t>(a.n_sink, int64_t(max_seq_len) - a.n_recent);
+  const int64_t tiles = int64_t(batch) * a.n_kv_heads *
+                        ((int2_end / kChunkTokens) / chunks_per_tile(a.gp));
+  if (tiles < kFbMinTiles * a.chain_groups) return 0;
+  void* base = nullptr;
+  const int err = decode_feedback(&base);
+  if (err != 0) return err;
+  a.feedback = static_cast<uint32_t*>(base) + ((a.group > 4 ? 3 : 0) + rounds - 2) * kFbWords;
+  return 0;
+}
+
 }  // namespace
 
 int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
@@ -696,7 +811,11 @@ int launch_decode(const kvq_dims& d, float sm_scale, const kvq_layer& layer,
   DecodeArgs a = make_decode_args(d, sm_scale, layer, cache, batch, seq_len, q, out, workspace,
                                   plan, which, n_query, query_base, query_count, groups);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.gp != 0) set_chain_geometry(a, batch, max_seq_len);
+  if (a.gp != 0) {
+    set_chain_geometry(a, batch, max_seq_len);
+    const int err = attach_feedback(a, batch, max_seq_len);
+    if (err != 0) return err;
+  }
   const dim3 pgrid(d.n_kv_heads + (a.gp != 0 ? 1 : 0), batch);
   if (a.n_groups > 0) {
     if (a.gp == 2) hipLaunchKernelGGL(prologue_prefix_kernel<2>, pgrid, dim3(256), 0, st, a);
@@ -726,6 +845,10 @@ int launch_decode_step(const kvq_dims& d, float sm_scale, const kvq_layer& layer
   if (a.gp == 0 || aa.tokens_per_block != kWaves) return -1;   // not a fused-step shape
   hipStream_t st = static_cast<hipStream_t>(stream);
   set_chain_geometry(a, batch, max_seq_len);
+  {
+    const int err = attach_feedback(a, batch, max_seq_len);
+    if (err != 0) return err;
+  }
   const int n_app_x = (total_new + kWaves - 1) / kWaves;
   const dim3 grid(n_app_x * d.n_kv_heads * 2 + (d.n_kv_heads + 1) * batch);
   if (a.gp == 2) hipLaunchKernelGGL(step_prologue_kernel<2>, grid, dim3(256), 0, st, aa, a, n_app_x);

@@ -16,6 +16,14 @@ namespace kvq {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kCombineSlice = 64;   // splits staged per combine pass
 
+// Words of one state of the self-calibrating range weights: the sums of
+// range durations (s_memrealtime ticks) per (dispatch round r, XCD x) at
+// kFbSum + 8 r + x, their counts at kFbCnt + 8 r + x, then the current XCD
+// and round weights (1/1024 units; 0 before the first update).  One state
+// per (G <= 4 or G = 8, 2 .. 4 rounds).
+constexpr int kFbSum = 0, kFbCnt = 32, kFbXw = 64, kFbRw = 72, kFbWords = 80;
+constexpr int kFbStates = 6;
+
 struct DecodeArgs {
   const float* R_K;
   const float* R_V;
@@ -71,6 +79,10 @@ struct DecodeArgs {
   // of one CU stream at different rates by dispatch order.
   int32_t* range_start;
   int32_t* pair_range;
+  // Self-calibrating range weights (kFb* layout below), or null: each range
+  // work-group adds its duration to the cell (round, XCD) of its index, and
+  // the next call's plan moves the weights toward equal durations.
+  uint32_t* feedback;
   int chain_groups;
   int round_size;
   int round_weight[4];

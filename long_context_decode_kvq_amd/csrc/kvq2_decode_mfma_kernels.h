@@ -1082,6 +1082,10 @@ __global__ __launch_bounds__(256, GP <= 4 ? (NG == 1 ? 4 : 3) : 2) void decode_m
     token_slice_item<GP, NG>(a, static_cast<int>(blockIdx.x) - a.chain_groups);
     return;
   }
+  // (low 32 bits of the 100 MHz clock: differences wrap correctly; held in
+  // a vector register, the scalar ones being the scarcer here)
+  uint32_t t_start = static_cast<uint32_t>(__builtin_amdgcn_s_memrealtime());
+  asm volatile("" : "+v"(t_start));
   const int i = blockIdx.x;
   const int Hkv = a.n_kv_heads, B = a.batch;
   const int32_t* pre = a.tile_prefix;
@@ -1153,6 +1157,14 @@ __global__ __launch_bounds__(256, GP <= 4 ? (NG == 1 ? 4 : 3) : 2) void decode_m
                              i, max(v0, sq) - sq, min(v1, sq + w) - sq);
       ++idx;
     }
+  }
+  // this range's duration, into the cell (dispatch round, XCD) of its index
+  // for the next call's weights (vector atomics; one lane)
+  if (a.feedback != nullptr && threadIdx.x == 0) {
+    const uint32_t dur = static_cast<uint32_t>(__builtin_amdgcn_s_memrealtime()) - t_start;
+    const int cell = 8 * min(i / a.round_size, 3) + (i & 7);
+    atomicAdd(a.feedback + kFbSum + cell, dur);
+    atomicAdd(a.feedback + kFbCnt + cell, 1u);
   }
 }
 

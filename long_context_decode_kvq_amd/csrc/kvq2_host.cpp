@@ -87,8 +87,10 @@ DecodeTuning read_tuning() {
   DecodeTuning t = {{kPieceCostChunks, kPieceCostChunksG8},
                     {{1230, 1100, 940, 830}, {1120, 1024, 930, 1024}},
                     {{1024, 1024}, {1024, 1024}},
-                    kRowSetCost};
+                    kRowSetCost,
+                    1};
   t.rowset_cost = std::min(std::max(env_int("KVQ_ROWSET_COST", kRowSetCost), 1), 16);
+  t.adapt = env_int("KVQ_ADAPT", 1) != 0 ? 1 : 0;
   const int pc = env_int("KVQ_PIECE_COST", -1);
   if (pc >= 0) t.piece_cost[0] = t.piece_cost[1] = std::min(pc, 4096);
   for (int k = 0; k < 2; ++k) {

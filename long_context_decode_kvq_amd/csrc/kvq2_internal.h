@@ -100,7 +100,8 @@ DecodePlan make_decode_plan(const kvq_dims& d, int32_t batch, int32_t max_seq_le
 bool prefix_groups_supported(const kvq_dims& d);
 
 // Tuning constants of the MFMA decode, read once per process from the
-// environment (KVQ_PIECE_COST, KVQ_ROUND_WEIGHTS, KVQ_XCD_WEIGHTS) with the
+// environment (KVQ_PIECE_COST, KVQ_ROUND_WEIGHTS, KVQ_XCD_WEIGHTS,
+// KVQ_ROWSET_COST, KVQ_ADAPT) with the
 // measured defaults.  Range weights are clamped so that the largest is at
 // most four times the smallest: with at least four virtual tiles per range
 // on average (the cut's precondition) no weighted range is then empty.
@@ -109,6 +110,7 @@ struct DecodeTuning {
   int round_weight[2][4];   // [G <= 4, G = 8][dispatch round], 1/1024 units
   int xcd_weight[2][2];     // [G <= 4, G = 8][even, odd XCD]
   int rowset_cost;          // virtual tiles charged per tile of a shared-prefix row-set item
+  int adapt;                // 1: range weights self-calibrate from measured durations
 };
 const DecodeTuning& decode_tuning();
 
@@ -155,6 +157,10 @@ constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 // Device address of the current device's scratch (resolved once per device
 // with hipGetSymbolAddress); returns a hipError_t value.
 int static_scratch(void** ptr);
+// Device address of the current device's self-calibrating range-weight
+// states (kFbStates x kFbWords words, zero at load; resolved once per
+// device); returns a hipError_t value.
+int decode_feedback(void** ptr);
 // Zero `bytes` (a multiple of 4) at device address p with a fill kernel
 // (no memset node, so the call can be captured in a HIP graph).
 int launch_zero_words(void* p, size_t bytes, void* stream);

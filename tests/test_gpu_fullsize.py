@@ -2,7 +2,8 @@
 
 Each workload's whole cache is built on the GPU by bulk quantize-append from
 its seeded tokens, with the rotations and clip thresholds of the oracle's
-calibration, and decoded once in the launch configuration bench.py times.
+calibration, and decoded (six times: the range weights self-calibrate over
+calls) in the launch configuration bench.py times.
 For a few sampled pairs the oracle builds the pair's cache by itself from the
 same seeded tokens (fp64 rotation, its own quantizer and packing), decodes the
 pair's query heads and the outputs are compared row by row (max normwise
@@ -88,6 +89,8 @@ def oracle_pair(w, cal, b, h, L, q_bits, dc=None):
     return oc.decode(R_K, R_V, [L], q_bits[None, h * G:(h + 1) * G])[0]
 
 
+N_REPEAT = 6        # decode calls per full-size case
+
 # (workload, sampled pairs); pairs cover the first and last sequence and KV head
 CASES = [
     ("conc_28x100k", [(0, 0), (27, 7)]),
@@ -111,17 +114,27 @@ def test_fullsize_sampled_pairs(name, pairs):
     out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device="cuda")
     seq = torch.from_numpy(lens.astype(np.int32)).cuda()
     q = W.decode_queries_device(w, 0)
-    kvq2.decode_attention(kd, lay, dc.handle, w.batch, seq, max_len, q, out, ws)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
-    assert np.isfinite(got).all()
+    # repeated calls: with the self-calibrating range weights the later calls
+    # cut the ranges differently (only the split-K boundaries move)
+    outs = []
+    for _ in range(N_REPEAT):
+        kvq2.decode_attention(kd, lay, dc.handle, w.batch, seq, max_len, q, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    got, last = outs[0], outs[-1]
+    assert np.isfinite(got).all() and np.isfinite(last).all()
+    for k in range(1, N_REPEAT):
+        assert rel_err(outs[k], got) <= TOL, (name, k)
+    say(f"  {N_REPEAT} calls: last vs first rel_err={rel_err(last, got):.3e}")
     q_bits = q.cpu().numpy().view(np.uint16)
     G = w.group
     for b, h in pairs:
         ref = oracle_pair(w, cal, b, h, int(lens[b]), q_bits[b], dc)
         e = rel_err(got[b, h * G:(h + 1) * G], ref)
-        say(f"  pair (b={b}, h={h}) len={int(lens[b])}: rel_err={e:.3e}")
+        e_last = rel_err(last[b, h * G:(h + 1) * G], ref)
+        say(f"  pair (b={b}, h={h}) len={int(lens[b])}: rel_err={e:.3e} (last call {e_last:.3e})")
         assert e <= TOL, (name, b, h, e)
+        assert e_last <= TOL, (name, b, h, e_last)
 
 
 STEP_CASES = [
