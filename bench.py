@@ -141,8 +141,8 @@ def build_cache(w, kvq2, W, lens_before, n_steps, device, quant_group=0):
 # (`bench.py --copy-probe`).  The counters are tied to a hash of the kernel
 # sources; after any source change the figure is stale and reported as null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_conc_28x100k_traffic.txt")
-KERNEL_SOURCES = ("kvq2_decode.hip", "kvq2_decode_mfma.hip", "kvq2_decode_common.h",
-                  "kvq2_device.h", "kvq2_internal.h")
+KERNEL_SOURCES = ("kvq2_decode.hip", "kvq2_decode_mfma.hip", "kvq2_decode_mfma_kernels.h",
+                  "kvq2_decode_common.h", "kvq2_device.h", "kvq2_internal.h")
 
 
 def kernel_source_hash():
