@@ -194,61 +194,70 @@ struct PrologueLds {
   int qexp[KG];
 };
 
-// One step of the self-calibrating range weights (one thread): the mean
-// duration of the ranges of each XCD (and of each dispatch round) measured
-// by the previous call with this state, against the mean of all, scales
-// that XCD's (round's) weight by sqrt(mean / its mean); the weights are
-// then renormalised to a mean of 1024 and clamped to [724, 1448] (each
-// within a factor of two of every other, so that no weighted range is
-// empty), stored, and the sums cleared for this call.  Before the first
-// measurement, and while the ranges last under 50 us, the launch's weights
-// stand.  fb_in: the state as read at the
-// plan's start (LDS); fb: the state itself (written); out: XCD weights [8],
-// round weights [4] for this call.
-__device__ void feedback_update(const uint32_t* fb_in, uint32_t* fb, int rounds, const int* xw0,
-                                const int* rw0, int* out) {
-  int xw[8], rw[4];
+// One step of the self-calibrating range weights, by the 64 lanes of one
+// wave (lane c < 32 holds cell (round c / 8, XCD c % 8)): the mean duration
+// of the ranges of each XCD (and of each dispatch round) measured by the
+// previous call with this state, against the mean of all, scales that XCD's
+// (round's) weight by sqrt(mean / its mean); the weights are then
+// renormalised to a mean of 1024 and clamped to [724, 1448] (each within a
+// factor of two of every other, so that no weighted range is empty) and
+// stored; the caller clears the sums.  Before the first measurement, and
+// while the ranges last under 50 us, the launch's weights stand.  fb_in:
+// the state as read at the plan's start (LDS); fb: the state itself; w
+// (LDS): XCD weights [8], round weights [4], the launch's on entry and this
+// call's on return.
+__device__ void feedback_update(const uint32_t* fb_in, uint32_t* fb, int rounds, int* w) {
+  const int c = threadIdx.x & 63, r = (c >> 3) & 3, x = c & 7;
   const bool init = fb_in[kFbXw] != 0;
-  for (int x = 0; x < 8; ++x) xw[x] = init ? static_cast<int>(fb_in[kFbXw + x]) : xw0[x];
-  for (int r = 0; r < 4; ++r) rw[r] = init ? static_cast<int>(fb_in[kFbRw + r]) : rw0[r];
-  double sx[8] = {}, nx[8] = {}, sr[4] = {}, nr[4] = {}, s = 0, n = 0;
-  for (int r = 0; r < rounds; ++r) {
-    for (int x = 0; x < 8; ++x) {
-      const double v = fb_in[kFbSum + 8 * r + x], c = fb_in[kFbCnt + 8 * r + x];
-      sx[x] += v; nx[x] += c; sr[r] += v; nr[r] += c; s += v; n += c;
-    }
-  }
+  // this lane's cell, and the current weights of its XCD and round
+  const bool cell = c < 32 && r < rounds;
+  const float v = cell ? static_cast<float>(fb_in[kFbSum + c]) : 0.f;
+  const float k = cell ? static_cast<float>(fb_in[kFbCnt + c]) : 0.f;
+  const int lx = w[x], lr = w[8 + r];   // the launch's
+  int wx = init ? static_cast<int>(fb_in[kFbXw + x]) : lx;
+  int wr = init ? static_cast<int>(fb_in[kFbRw + r]) : lr;
+  const float s = wave_sum(v), n = wave_sum(k);
+  // per XCD: the lanes c ^ 8, c ^ 16; per round: c ^ 1, c ^ 2, c ^ 4
+  float sx = v + __shfl_xor(v, 8), nx = k + __shfl_xor(k, 8);
+  sx += __shfl_xor(sx, 16);
+  nx += __shfl_xor(nx, 16);
+  float sr = v + __shfl_xor(v, 1), nr = k + __shfl_xor(k, 1);
+  sr += __shfl_xor(sr, 2);
+  nr += __shfl_xor(nr, 2);
+  sr += __shfl_xor(sr, 4);
+  nr += __shfl_xor(nr, 4);
   // Ranges shorter than kFbMinTicks (batch-1 decodes) are dominated by
-  // fixed latencies, not by their share of the tiles: their launch weights
-  // stand.
-  constexpr double kFbMinTicks = 5000.0;   // 50 us of the 100 MHz clock
-  bool every = n > 0 && s >= kFbMinTicks * n;
-  for (int x = 0; x < 8; ++x) every = every && nx[x] > 0;
-  for (int r = 0; r < rounds; ++r) every = every && nr[r] > 0;
-  if (n > 0 && s < kFbMinTicks * n) {
-    for (int x = 0; x < 8; ++x) xw[x] = xw0[x];
-    for (int r = 0; r < 4; ++r) rw[r] = rw0[r];
+  // fixed latencies, not by their share of the tiles: the launch weights.
+  constexpr float kFbMinTicks = 5000.f;   // 50 us of the 100 MHz clock
+  if (n > 0.f && s < kFbMinTicks * n) {
+    wx = lx;
+    wr = lr;
   }
+  // every XCD and every used round measured
+  const bool have = c < 32 && nx > 0.f && (r >= rounds || nr > 0.f);
+  const bool every = n > 0.f && s >= kFbMinTicks * n &&
+                     __builtin_amdgcn_ballot_w64(c < 32 && !have) == 0;
   if (every) {
-    const double mean = s / n;
-    auto settle = [](int* w, int k, const double* f) {
-      double m = 0;
-      for (int j = 0; j < k; ++j) m += w[j] * f[j];
-      m /= k;
-      for (int j = 0; j < k; ++j)
-        w[j] = min(1448, max(724, static_cast<int>(w[j] * f[j] * 1024.0 / m + 0.5)));
-    };
-    double fx[8], fr[4];
-    for (int x = 0; x < 8; ++x) fx[x] = sqrt(mean / (sx[x] / nx[x]));
-    for (int r = 0; r < rounds; ++r) fr[r] = sqrt(mean / (sr[r] / nr[r]));
-    settle(xw, 8, fx);
-    settle(rw, rounds, fr);
+    const float mean = s / n;
+    const float fx = sqrtf(mean * nx / sx);
+    const float fr = r < rounds ? sqrtf(mean * nr / sr) : 1.f;
+    // renormalise: the mean of the new XCD weights (lanes 0 .. 7) and of the
+    // used rounds' (lanes 0, 8, 16, 24 below rounds) is 1024
+    const float mx = wave_sum(c < 8 ? wx * fx : 0.f) / 8.f;
+    const float mr = wave_sum(c < 32 && x == 0 && r < rounds ? wr * fr : 0.f) /
+                     static_cast<float>(rounds);
+    wx = min(1448, max(724, static_cast<int>(wx * fx * 1024.f / mx + 0.5f)));
+    if (r < rounds) wr = min(1448, max(724, static_cast<int>(wr * fr * 1024.f / mr + 0.5f)));
   }
-  for (int x = 0; x < 8; ++x) fb[kFbXw + x] = static_cast<uint32_t>(xw[x]);
-  for (int r = 0; r < 4; ++r) fb[kFbRw + r] = static_cast<uint32_t>(rw[r]);
-  for (int k = 0; k < 64; ++k) fb[kFbSum + k] = 0u;
-  for (int x = 0; x < 8; ++x) out[x] = xw[x];
-  for (int r = 0; r < 4; ++r) out[8 + r] = rw[r];
+  __builtin_amdgcn_wave_barrier();   // (every lane has read w)
+  if (c < 8) {
+    fb[kFbXw + c] = static_cast<uint32_t>(wx);
+    w[c] = wx;
+  }
+  if (c < 32 && x == 0) {   // lane 8 r holds round r's weight
+    fb[kFbRw + r] = static_cast<uint32_t>(wr);
+    w[8 + r] = wr;
+  }
 }
 
 // The equal-range plan of the MFMA decode, by one work-group of 256 threads
@@ -333,7 +342,17 @@ __device__ void plan_ranges(const DecodeArgs& a, PlanLds& P, GroupLds* L = nullp
 #pragma unroll
   for (int r = 0; r < 4; ++r) rw[r] = a.round_weight[r];
   if (a.feedback != nullptr && weighted) {
-    if (tid == 0) feedback_update(P.fbraw, a.feedback, rounds, xw, rw, P.fbw);
+    if (tid == 0) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) P.fbw[x] = xw[x];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) P.fbw[8 + r] = rw[r];
+    }
+    __syncthreads();
+    if (tid < 64) {
+      feedback_update(P.fbraw, a.feedback, rounds, P.fbw);
+      a.feedback[kFbSum + tid] = 0u;   // sums and counts, for this call's ranges
+    }
     __syncthreads();
 #pragma unroll
     for (int x = 0; x < 8; ++x) xw[x] = P.fbw[x];
