@@ -182,6 +182,13 @@ size_t kvq_decode_workspace_bytes(const kvq_dims* dims, int32_t batch,
  *   max_seq_len  host, >= every seq_len (sizes the split-K grid)
  *   q            device bf16 [batch][Hq][128]
  *   out          device fp32 [batch][Hq][128]  (an empty sequence gives 0)
+ * Split-K boundaries, and so the last bits of `out`, can differ between
+ * calls on identical inputs: for long contexts the matrix-core decode cuts
+ * its ranges with weights it calibrates from the durations measured in
+ * earlier calls on the same GPU (library-owned device state, shared by every
+ * caller on that GPU; concurrent calls only perturb the weights within
+ * their bounds).  The environment variable KVQ_ADAPT=0 keeps the launch
+ * weights fixed.
  */
 int kvq_decode_attention(const kvq_dims* dims, const kvq_layer* layer,
                          const kvq_cache* cache, int32_t batch,
