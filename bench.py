@@ -180,6 +180,78 @@ def copy_probe(n_bytes=1 << 30, reps=5):
     log(f"[copy-probe] {reps} copies of {n_bytes} bytes")
 
 
+def cached_pages_probe(w, calls=50, reps=5, cached_target=1200 * 1024):
+    """The decode call with its pages in HBM against the same call with every
+    block-table entry pointing into the first ~1.2 MB of pages (which the
+    caches then serve): the second time is what the kernels take when HBM is
+    not the limit.  Each figure is the median over `reps` replays of one HIP
+    graph of `calls` back-to-back decode calls.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from long_context_decode_kvq_amd import kvq2
+    from long_context_decode_kvq_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    lens = w.seq_lens()
+    kd, dc, lay, keep = build_cache(w, kvq2, W, lens, 1, dev, 0)
+    max_len = int(lens.max()) + 1
+    ws = torch.zeros(kvq2.decode_workspace_bytes(kd, w.batch, max_len), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=dev)
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    q = W.decode_queries_device(w, 0, dev).contiguous()
+
+    def call(st):
+        kvq2.decode_attention(kd, lay, dc.handle, w.batch, seq, max_len, q, out, ws, st)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(calls):
+            call(cap)
+    torch.cuda.synchronize()
+
+    def timed():
+        t = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1000.0 / calls)
+        return float(np.median(t))
+
+    t0 = time.time()
+    while time.time() - t0 < 0.5:      # out of the idle power state
+        graph.replay()
+        torch.cuda.synchronize()
+    hbm = timed()
+    page_bytes = dc.pool.numel() // dc.num_pages
+    n_phys = max(1, cached_target // page_bytes)
+    bt = dc.block_table.clone()
+    # every sequence's logical page j -> sequence 0's physical page j mod n_phys
+    cols = torch.arange(bt.shape[1], device=dev) % n_phys
+    dc.block_table.copy_(bt[0, :n_phys][cols].unsqueeze(0).expand(bt.shape[0], -1))
+    graph.replay()
+    torch.cuda.synchronize()
+    cached = timed()
+    dc.block_table.copy_(bt)
+    torch.cuda.synchronize()
+    hbm_again = timed()
+    nbytes = decode_bytes(w, lens)
+    print(json.dumps({
+        "probe": "cached_pages", "workload": w.name, "decode_bytes": int(nbytes),
+        "decode_us_hbm": round(hbm, 2), "decode_us_cached_pages": round(cached, 2),
+        "decode_us_hbm_again": round(hbm_again, 2), "cached_page_bytes": int(n_phys * page_bytes),
+        "timing": f"median of {reps} replays of one HIP graph of {calls} decode calls"}),
+        flush=True)
+    del keep
+
+
 def _oracle_pair_run(w, b, h, seconds_budget, max_steps, barrier=None):
     """The CPU oracle on one (sequence b, KV head h) pair of workload w: build
     the pair's cache to L - 1 tokens (untimed), then decode steps (append one
@@ -567,6 +639,9 @@ def main():
                          "of one kvq_decode_step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--cached-pages-probe", action="store_true",
+                    help="only time the decode call of --workload with its pages in HBM and "
+                         "again with every block-table entry remapped into ~1.2 MB of pages")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the decode kernel source hash and exit")
     args = ap.parse_args()
@@ -584,7 +659,8 @@ def main():
     # the oracle's worker processes are forked before this process touches the GPU
     # (the oracle leg times the one-query decode step; multi-query lines go without it)
     pool = None
-    if (not args.no_cpu_baseline and not args.copy_probe and args.n_query == 1
+    if (not args.no_cpu_baseline and not args.copy_probe and not args.cached_pages_probe
+            and args.n_query == 1
             and args.quant_group in (0, 128)):
         pool = OraclePool()
 
@@ -593,6 +669,10 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.cached_pages_probe:
+        from long_context_decode_kvq_amd import workloads as W
+        cached_pages_probe(W.WORKLOADS[args.workload])
         return
 
     from long_context_decode_kvq_amd import kvq2
