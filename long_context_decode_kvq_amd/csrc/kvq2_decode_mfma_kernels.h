@@ -445,7 +445,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         const float d = select_bits(hi_sel, d0, d1m);
         const uint32_t kpr = r == 0 ? kp.x : r == 1 ? kp.y : r == 2 ? kp.z : kp.w;
         const uint32_t vpr = r == 0 ? vp.x : r == 1 ? vp.y : r == 2 ? vp.z : vp.w;
-        lg[r] = fmaf(f16lo(kpr), d, f16hi(kpr) * qbar_s);
+        lg[r] = fmaf(f16lo(kpr), d, fmaf(f16hi(kpr), qbar_s, 0.f));
         svb[r] = vpr;
         zv[r] = f16hi(vpr);
       }
@@ -480,21 +480,24 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         m_eff = g_ok ? ml - log2_sigma : INFINITY;
         thr = g_ok ? (ml + kTau) / qscale : INFINITY;
       }
-      float w[4];
+      float w[4], pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(lg[r], qscale, -m_eff));
         l_lane += p;
         z_lane = fmaf(p, zv[r], z_lane);
-        w[r] = p * f16lo(svb[r]);
+        pr[r] = p;
+        w[r] = fmaf(p, f16lo(svb[r]), 0.f);   // (see the four-head path)
       }
       const fp16x2_t h02 = __builtin_amdgcn_cvt_pkrtz(w[0], w[2]);
       const fp16x2_t h13 = __builtin_amdgcn_cvt_pkrtz(w[1], w[3]);
       const uint32_t hi02 = __builtin_bit_cast(uint32_t, h02), hi13 = __builtin_bit_cast(uint32_t, h13);
       const uint32_t lo02 = __builtin_bit_cast(
-          uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0] - float(h02[0]), w[2] - float(h02[1])));
+          uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(pr[0], f16lo(svb[0]), -float(h02[0])),
+                                               fmaf(pr[2], f16lo(svb[2]), -float(h02[1]))));
       const uint32_t lo13 = __builtin_bit_cast(
-          uint32_t, __builtin_amdgcn_cvt_pkrtz(w[1] - float(h13[0]), w[3] - float(h13[1])));
+          uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(pr[1], f16lo(svb[1]), -float(h13[0])),
+                                               fmaf(pr[3], f16lo(svb[3]), -float(h13[1]))));
       // row n < 8: hi parts of chunk 0 (own) and chunk 1 (lane n + 8);
       // row n + 8: lo parts of chunk 0 (lane n) and chunk 1 (own)
       const uint32_t hi02u = dpp_u<0x100 + GP>(hi02), hi13u = dpp_u<0x100 + GP>(hi13);
@@ -787,7 +790,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       const float d = c4[r] + dpp_f<0x100 + GP>(c4[r]);          // hi + lo columns
       const uint32_t kpr = r == 0 ? kp.x : r == 1 ? kp.y : r == 2 ? kp.z : kp.w;
       const uint32_t vpr = r == 0 ? vp.x : r == 1 ? vp.y : r == 2 ? vp.z : vp.w;
-      lg[r] = fmaf(f16lo(kpr), d, f16hi(kpr) * qbar_s);          // lg' = s_K d + z_K sum(q')/qscale
+      lg[r] = fmaf(f16lo(kpr), d, fmaf(f16hi(kpr), qbar_s, 0.f));          // lg' = s_K d + z_K sum(q')/qscale
       svb[r] = vpr;
       zv[r] = f16hi(vpr);
     }
@@ -824,24 +827,32 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       m_eff = g_ok ? ml - log2_sigma : INFINITY;
       thr = g_ok ? (ml + kTau) / qscale : INFINITY;
     }
-    float w[4];
+    // Products with an f16 operand are written as fmaf(x, f16, 0): each is
+    // then one mixed-precision FMA instead of a conversion and a multiply
+    // (the same value: one rounding of the exact product; the kernel is
+    // bound by VALU issue as much as by HBM, so every instruction per tile
+    // counts).
+    float w[4], pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(lg[r], qscale, -m_eff));
       l_lane += p;                       // lo lanes accumulate garbage, masked at the end
       z_lane = fmaf(p, zv[r], z_lane);
-      w[r] = p * f16lo(svb[r]);
+      pr[r] = p;
+      w[r] = fmaf(p, f16lo(svb[r]), 0.f);
     }
     // f16 hi/lo split of w (each part packed two per dword, rounded toward
-    // zero: lo = w - hi carries the remainder, so hi + lo is w to ~2^-20);
-    // lo parts move GP lanes up (row_shr) into the lo rows
+    // zero: lo = p s_V - hi, one FMA, carries the remainder, so hi + lo is w
+    // to ~2^-20); lo parts move GP lanes up (row_shr) into the lo rows
     const fp16x2_t h02 = __builtin_amdgcn_cvt_pkrtz(w[0], w[2]);
     const fp16x2_t h13 = __builtin_amdgcn_cvt_pkrtz(w[1], w[3]);
     const uint32_t hi02 = __builtin_bit_cast(uint32_t, h02), hi13 = __builtin_bit_cast(uint32_t, h13);
     const uint32_t lo02 = __builtin_bit_cast(
-        uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0] - float(h02[0]), w[2] - float(h02[1])));
+        uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(pr[0], f16lo(svb[0]), -float(h02[0])),
+                                             fmaf(pr[2], f16lo(svb[2]), -float(h02[1]))));
     const uint32_t lo13 = __builtin_bit_cast(
-        uint32_t, __builtin_amdgcn_cvt_pkrtz(w[1] - float(h13[0]), w[3] - float(h13[1])));
+        uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(pr[1], f16lo(svb[1]), -float(h13[0])),
+                                             fmaf(pr[3], f16lo(svb[3]), -float(h13[1]))));
     const uint32_t lo02s = dpp_u<0x110 + GP>(lo02), lo13s = dpp_u<0x110 + GP>(lo13);
     const uint32_t av0 = is_hi ? hi02 : lo02s;
     const uint32_t av1 = is_hi ? hi13 : lo13s;
