@@ -328,8 +328,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   // and w = p' s_V <= 2^8 fits f16; l, z and o' all carry the same factor.
   // thr = (m + tau) / qscale is the lazy-rescale threshold on lg'.
   // Columns of padding heads (g >= G) keep m_eff = thr = +inf: p' = 0.
+  // Lanes whose logits are not used (the lo columns, except in the
+  // eight-head layout) keep thr = +inf too, so that the rescale test is a
+  // plain compare on every lane.
+  const bool thr_lane = g_ok && (Geo<GP, NG>::SHARED || is_hi);
   float m_eff = g_ok ? -INFINITY : INFINITY;
-  float thr = g_ok ? -INFINITY : INFINITY;
+  float thr = thr_lane ? -INFINITY : INFINITY;
   float l_lane = 0.f, z_lane = 0.f;
   float zg_lane[NG];                 // sum of p z_V per quantization group (NG > 1)
 #pragma unroll
@@ -357,6 +361,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
   };
   // DMA one tile from HBM into an LDS slot: NPT 64-lane x 16 B loads of the
   // code bytes, then 64-lane dword loads of the params of two chunks each.
+  const uint32_t hi_half = 0u - uint32_t(lane >> 5);   // all ones on lanes 32-63
   auto issue_tile = [&](int tile, const Pages& P, uint8_t* slot) {
     int64_t off[NPT];
 #pragma unroll
@@ -375,10 +380,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
 #pragma unroll
     for (int i = 0; i < (NPT + 1) / 2; ++i) {
       const int p0 = 2 * i, p1 = NPT > 1 ? 2 * i + 1 : 0;
-      const int64_t o = (lane >> 5) ? off[p1] : off[p0];
+      // lanes 32-63 read chunk p1's params: one wave-uniform difference from
+      // chunk p0's, kept per lane by an AND with the lane's mask
+      const uint64_t d = uint64_t(off[p1] - off[p0]);
+      const int64_t dl = int64_t(d & (uint64_t(hi_half) | (uint64_t(hi_half) << 32)));
+      const uint8_t* pb = pool + off[p0] + kKParamsOff;
 #pragma unroll
       for (int u = 0; u < NG; ++u)
-        dma_x1<!RS>(pool + o + kKParamsOff + 128 * u + 4 * (lane & 31),
+        dma_x1<!RS>(pb + (dl + (128 * u + 4 * (lane & 31))),
                     lds + 1024u * NPT + 256u * (NG * i + u));
     }
   };
@@ -450,7 +459,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         zv[r] = f16hi(vpr);
       }
       const float tmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-      if (__builtin_amdgcn_ballot_w64(g_ok && tmax > thr) != 0) {
+      if (__builtin_amdgcn_ballot_w64(tmax > thr) != 0) {
         const float tm = g_ok ? tmax * qscale : -INFINITY;
         float corr[GP];
 #pragma unroll
@@ -478,7 +487,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
         l_lane *= cl;
         z_lane *= cl;
         m_eff = g_ok ? ml - log2_sigma : INFINITY;
-        thr = g_ok ? (ml + kTau) / qscale : INFINITY;
+        thr = thr_lane ? (ml + kTau) / qscale : INFINITY;
       }
       float w[4], pr[4];
 #pragma unroll
@@ -624,7 +633,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
           if (pblk == p) lg[r] = E[p][r];
       }
       float tmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-      if (__builtin_amdgcn_ballot_w64(is_hi && g_ok && tmax > thr) != 0) {
+      if (__builtin_amdgcn_ballot_w64(tmax > thr) != 0) {
         const float tm = (is_hi && g_ok) ? tmax * qscale : -INFINITY;
         float corr[GP];
 #pragma unroll
@@ -652,7 +661,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
 #pragma unroll
         for (int k = 0; k < NG; ++k) zg_lane[k] *= cl;
         m_eff = g_ok ? ml - log2_sigma : INFINITY;
-        thr = g_ok ? (ml + kTau) / qscale : INFINITY;
+        thr = thr_lane ? (ml + kTau) / qscale : INFINITY;
       }
       float w[NG][4];
 #pragma unroll
@@ -796,7 +805,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
     }
     // lazy running max
     float tmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    if (__builtin_amdgcn_ballot_w64(is_hi && g_ok && tmax > thr) != 0) {
+    if (__builtin_amdgcn_ballot_w64(tmax > thr) != 0) {
       const float tm = (is_hi && g_ok) ? tmax * qscale : -INFINITY;
       float corr[GP];
 #pragma unroll
@@ -825,7 +834,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const int b, co
       l_lane *= cl;
       z_lane *= cl;
       m_eff = g_ok ? ml - log2_sigma : INFINITY;
-      thr = g_ok ? (ml + kTau) / qscale : INFINITY;
+      thr = thr_lane ? (ml + kTau) / qscale : INFINITY;
     }
     // Products with an f16 operand are written as fmaf(x, f16, 0): each is
     // then one mixed-precision FMA instead of a conversion and a multiply
